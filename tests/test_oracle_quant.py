@@ -1,0 +1,228 @@
+"""Pins for the oracle's affine-quantized K/V attention.
+
+Source: "ffai/flash_quantized_sdpa.rs" (metaltile-std 0.1.0) -- layout doc,
+base kernel macro (dequant x = scale_g * code + bias_g, GQA q_idx/repeat,
+sink initialisation, final o / l), float-mask macro (additive bias).
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tree_masked_decode_amd import inputs
+
+
+def qcase(seed=0, B=2, nQ=4, nKV=2, dim=64, L=40, cap=None, q_l=1, bits=4, G=32,
+          sinks=False, mask=None):
+    return inputs.quant_case(dict(batch=B, n_q_heads=nQ, n_kv_heads=nKV, dim=dim,
+                                  kv_seq_len=L, kv_capacity=cap or L, q_l=q_l,
+                                  bits=bits, group_size=G, sinks=sinks,
+                                  mask=mask), seed=seed)
+
+
+def qrun(c, **kw):
+    args = dict(n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
+                bits=c["bits"], group_size=c["group_size"], scale=c["scale"],
+                sinks=c["sinks"], mask=c["mask"],
+                mask_head_stride=c["mask_head_stride"],
+                mask_stride=c["mask_stride"])
+    args.update(kw)
+    return oracle.quant_attention(c["q"], c["k_packed"], c["k_scales"],
+                                  c["k_biases"], c["v_packed"], c["v_scales"],
+                                  c["v_biases"], **args)
+
+
+def _word_fixture(golden_dir):
+    rows = []
+    for line in open(os.path.join(golden_dir, "quant_word_order.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        parts = line.split()
+        rows.append((int(parts[0]), int(parts[1], 16), [int(x) for x in parts[2:]]))
+    return rows
+
+
+def test_word_order_golden(golden_dir):
+    # One key (so the output IS the dequantised value row), scale 1, bias 0.
+    for bits, word, codes in _word_fixture(golden_dir):
+        dim = 32 // bits
+        c = qcase(B=1, nQ=1, nKV=1, dim=dim, L=1, bits=bits, G=dim)
+        c["v_packed"][:] = np.uint32(word)
+        c["v_scales"][:] = np.float16(1.0)
+        c["v_biases"][:] = np.float16(0.0)
+        got = qrun(c)
+        assert np.array_equal(got[0, 0], np.array(codes, dtype=np.float64))
+        # the generator packs in the same order
+        assert int(inputs.pack_codes(np.array([codes]), bits)[0, 0]) == word
+
+
+def test_affine_dequant_per_group():
+    # single key: out = s_g * code + b_g, group g = d // G
+    c = qcase(1, B=1, nQ=2, nKV=1, dim=64, L=1, bits=4, G=16)
+    got = qrun(c)
+    pf = 8
+    words = c["v_packed"][0, 0]
+    sc = c["v_scales"][0, 0].astype(np.float64)
+    bi = c["v_biases"][0, 0].astype(np.float64)
+    for d in range(64):
+        code = (int(words[d // pf]) >> ((d % pf) * 4)) & 15
+        expect = sc[d // 16] * code + bi[d // 16]
+        assert got[0, 0, d] == expect and got[1, 0, d] == expect
+
+
+def test_eight_bit_unit_affine_equals_fp_path():
+    # 8-bit codes with scale 1, bias 0 are exactly the integers; the fp-path
+    # oracle fed those integers (and the same Q) must agree.
+    B, nQ, nKV, dim, L = 1, 4, 2, 64, 33
+    c = qcase(2, B=B, nQ=nQ, nKV=nKV, dim=dim, L=L, bits=8, G=64)
+    rng = np.random.default_rng(5)
+    kc = rng.integers(0, 256, size=(nKV, L, dim), dtype=np.uint32)
+    vc = rng.integers(0, 256, size=(nKV, L, dim), dtype=np.uint32)
+    c["k_packed"] = inputs.pack_codes(kc, 8)
+    c["v_packed"] = inputs.pack_codes(vc, 8)
+    for n in ("k_scales", "v_scales"):
+        c[n][:] = np.float16(1.0)
+    for n in ("k_biases", "v_biases"):
+        c[n][:] = np.float16(0.0)
+    c["scale"] = 1.0 / 512.0
+    got = qrun(c)  # [nQ, 1, dim]
+    ref = oracle.attention(c["q"][:, 0:1, :].astype(np.float32),
+                           kc.astype(np.float32), vc.astype(np.float32), None,
+                           n_kv_heads=nKV, kv_seq_len=L, scale=c["scale"])
+    np.testing.assert_allclose(got[:, 0, :], ref[0], rtol=0, atol=1e-10)
+
+
+def _brute_quant(c):
+    """Dequantise everything with numpy, then softmax in matrix form."""
+    bits, G = c["bits"], c["group_size"]
+    pf = 32 // bits
+    def deq(packed, sc, bi):
+        S, N, W = packed.shape
+        shifts = (np.arange(pf, dtype=np.uint32) * bits)
+        codes = (packed[..., None] >> shifts) & np.uint32((1 << bits) - 1)
+        codes = codes.reshape(S, N, W * pf).astype(np.float64)
+        s = np.repeat(sc.astype(np.float64), G, axis=2)
+        b = np.repeat(bi.astype(np.float64), G, axis=2)
+        return s * codes + b
+    K = deq(c["k_packed"], c["k_scales"], c["k_biases"])
+    V = deq(c["v_packed"], c["v_scales"], c["v_biases"])
+    BnQ, q_l, dim = c["q"].shape
+    nQ = c["n_q_heads"]
+    rep = nQ // c["n_kv_heads"]
+    L = c["kv_seq_len"]
+    out = np.zeros((BnQ, q_l, dim))
+    for qi in range(BnQ):
+        kv = qi // rep
+        z = c["scale"] * (c["q"][qi].astype(np.float64) @ K[kv, :L].T)
+        if c["mask"] is not None:
+            z = z + c["mask"].reshape(BnQ, q_l, -1)[qi, :, :L].astype(np.float64)
+        cols = [z]
+        vals = [V[kv, :L]]
+        if c["sinks"] is not None:
+            cols.append(np.full((q_l, 1), float(c["sinks"][qi % nQ])))
+            vals.append(np.zeros((1, dim)))
+        z = np.concatenate(cols, axis=1)
+        Vx = np.concatenate(vals, axis=0)
+        w = np.exp(z - z.max(axis=1, keepdims=True))
+        out[qi] = (w @ Vx) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+@pytest.mark.parametrize("bits,G,sinks,alibi", [
+    (4, 32, False, False), (4, 64, True, True), (8, 32, True, False),
+    (8, 16, False, True)])
+def test_matches_brute_force(bits, G, sinks, alibi):
+    c = qcase(3, B=2, nQ=4, nKV=2, dim=64, L=57, bits=bits, G=G, sinks=sinks,
+              mask="alibi" if alibi else None)
+    np.testing.assert_allclose(qrun(c), _brute_quant(c), rtol=0, atol=1e-12)
+
+
+def test_sink_closed_form_single_key():
+    # Q = 0 and one key: logit 0, so out = V0 * 1 / (1 + e^sink).
+    c = qcase(4, B=1, nQ=2, nKV=1, dim=32, L=1, bits=4, G=32, sinks=True)
+    c["q"][:] = np.float16(0.0)
+    no_sink = qrun(c, sinks=None)
+    got = qrun(c)
+    for h in range(2):
+        f = 1.0 / (1.0 + np.exp(np.float64(c["sinks"][h])))
+        np.testing.assert_allclose(got[h, 0], no_sink[h, 0] * f, rtol=1e-14)
+
+
+def test_far_negative_sink_is_no_sink():
+    c = qcase(5, sinks=True)
+    c["sinks"][:] = np.float32(-1e4)
+    assert np.array_equal(qrun(c), qrun(c, sinks=None))
+
+
+def test_sink_scales_output_by_mass_ratio():
+    # O_sink = O_nosink * A / (A + e^s), A = sum of the key weights, all
+    # relative to the same max; checked through two sinks on the same row.
+    c = qcase(6, B=1, nQ=1, nKV=1, dim=32, L=10, bits=4, G=32, sinks=True)
+    base = qrun(c, sinks=None)[0, 0]
+    s1 = np.array([0.3], dtype=np.float32)
+    s2 = np.array([1.7], dtype=np.float32)
+    o1 = qrun(c, sinks=s1)[0, 0]
+    o2 = qrun(c, sinks=s2)[0, 0]
+    # base/o = 1 + e^s / A  ->  (base/o1 - 1) e^(s2 - s1) = base/o2 - 1
+    idx = np.argmax(np.abs(base))
+    r1 = base[idx] / o1[idx] - 1.0
+    r2 = base[idx] / o2[idx] - 1.0
+    np.testing.assert_allclose(
+        r1 * np.exp(np.float64(s2[0]) - np.float64(s1[0])), r2, rtol=1e-10)
+
+
+def test_additive_mask_shift_invariance_without_sinks():
+    # Bias values on a 1/8 grid are exact in f16 before and after the shift.
+    c = qcase(7, B=1, nQ=2, nKV=1, dim=32, L=30, bits=4, G=32)
+    grid = np.random.default_rng(1).integers(-40, 1, size=(2, 1, 30))
+    c["mask"] = (grid / 8.0).astype(np.float16)
+    c["mask_head_stride"] = 30
+    c["mask_stride"] = 30
+    shifted = dict(c)
+    shifted["mask"] = ((grid - 16) / 8.0).astype(np.float16)
+    np.testing.assert_allclose(qrun(shifted), qrun(c), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(qrun(c), _brute_quant(c), rtol=0, atol=1e-12)
+    # with a sink the shift is NOT neutral (the sink logit is not biased)
+    c["sinks"] = shifted["sinks"] = np.zeros(2, dtype=np.float32)
+    assert not np.allclose(qrun(shifted), qrun(c), atol=1e-6)
+
+
+def test_gqa_mapping_repeat():
+    # q_idx uses stream q_idx // (nQ/nKV) within its batch ([FQS] kv_idx).
+    c = qcase(8, B=2, nQ=4, nKV=2, dim=32, L=20, bits=4, G=32)
+    m = dict(c)
+    for n in ("k_packed", "k_scales", "k_biases", "v_packed", "v_scales", "v_biases"):
+        m[n] = np.repeat(c[n], 2, axis=0)  # MHA with each stream repeated
+    m["n_kv_heads"] = 4
+    assert np.array_equal(qrun(m), qrun(c))
+
+
+def test_masked_cells_excluded_and_implicit_causal_rows():
+    c = qcase(9, B=1, nQ=2, nKV=1, dim=32, L=24, q_l=3, bits=4, G=32)
+    implicit = qrun(c)
+    # the implicit rule as an explicit f16 mask (0 / -65504) gives the same rows
+    i = np.arange(3)[:, None]
+    t = np.arange(24)[None, :]
+    m = np.where(t <= 24 - 3 + i, 0.0, -65504.0).astype(np.float16)
+    c2 = dict(c)
+    c2["mask"] = np.broadcast_to(m, (2, 3, 24)).copy()
+    c2["mask_head_stride"] = 3 * 24
+    c2["mask_stride"] = 24
+    assert np.array_equal(qrun(c2), implicit)
+    # broadcast tree mask (head stride 0) is the same thing
+    c3 = dict(c)
+    c3["mask"] = m.copy()
+    c3["mask_head_stride"] = 0
+    c3["mask_stride"] = 24
+    assert np.array_equal(qrun(c3), implicit)
+
+
+def test_quant_rows_selection_matches_full():
+    c = qcase(10, B=2, nQ=4, nKV=2, dim=64, L=30, q_l=2, bits=8, G=64, sinks=True)
+    full = qrun(c)
+    rows = [(0, 0), (5, 1), (7, 0)]
+    sel = qrun(c, rows=rows)
+    for r, (qi, i) in enumerate(rows):
+        assert np.array_equal(sel[r], full[qi, i])
