@@ -1,0 +1,232 @@
+/*
+ * tree_attn.h -- C ABI of libtreeattn.so: tree-masked decode attention for
+ * AMD MI355X (gfx950).
+ *
+ * One pass of the tree-verify step of speculative decoding: every draft-tree
+ * node (query) attends the KV cache under an explicit per-node mask, with
+ * GQA, an online softmax over split KV ranges, and a log-sum-exp merge of
+ * the split results.  A second entry point does the same over an
+ * affine-quantized (4/8-bit) KV cache with optional attention sinks.
+ *
+ * Sources, cited by page title and section:
+ *   [TA]  "tree_attention.metal" (mlx-native 0.9.1): header comment,
+ *         TreeAttentionParams, tree_attention_impl.
+ *   [OPS] "ops/tree_attention.rs" (mlx-native 0.9.2): module doc, mask
+ *         constants, TreeAttentionParams, validate_buffers, validate_params,
+ *         tree_attention() doc, tmp_buffer_bytes.
+ *   [FQS] "ffai/flash_quantized_sdpa.rs" (metaltile-std 0.1.0): module doc
+ *         (Layout, Mask variants, dispatch invariants), base and float-mask
+ *         kernel macros.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked DEVICE are device memory owned by the caller (for
+ *   example torch tensors); HOST pointers are host memory.  The library
+ *   allocates nothing, keeps no pointer after returning, and never
+ *   synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   null stream) and is complete when that stream reaches it.
+ * - Every `*_bytes` argument is the size of the caller's buffer.  It is
+ *   compared with the size the call needs, computed in 64-bit arithmetic
+ *   with overflow checks ([OPS] validate_buffers uses checked multiplies for
+ *   the same reason).
+ * - All arguments are validated on the host before anything is enqueued.
+ *   On any error the function returns a negative TA_* code, enqueues
+ *   nothing, and tree_attn_last_error() describes the problem.
+ * - Device pointers must be 16-byte aligned (torch allocations are).
+ * - Calls on one stream are ordered; calls sharing an output or partial
+ *   buffer on different streams race and are the caller's to order.
+ * - Thread-safe: the only library state is the per-thread error string.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of the library; everything else in it is hidden. */
+#define TA_API __attribute__((visibility("default")))
+
+/* Return codes. */
+#define TA_OK 0
+#define TA_EINVAL (-1)       /* an argument is invalid (shape, pointer, topology) */
+#define TA_ESIZE (-2)        /* a buffer is smaller than the call needs */
+#define TA_EOVERFLOW (-3)    /* a size computation overflows 64 bits */
+#define TA_EUNSUPPORTED (-4) /* valid but not implemented (head_dim, dtype, ...) */
+#define TA_EHIP (-5)         /* the HIP runtime reported an error on launch */
+
+/* Element types. */
+#define TA_F32 0
+#define TA_F16 1
+
+/* Mask sentinels ([OPS] mask constants).  A mask cell <= TA_MASKED excludes
+ * the key; any larger value is ADDED to the scaled logit (0 = attended). */
+#define TA_MASKED (-65504.0f)
+#define TA_ATTENDED 0.0f
+
+/*
+ * Bytes of the split-KV partial-result scratch for `nwg` splits:
+ *   n_heads * q_l * nwg * (head_dim + 2) * 4, saturating at SIZE_MAX.
+ * This is the size formula of [OPS] tmp_buffer_bytes with the split count
+ * as an argument.  For the quantized path pass n_heads = batch * n_q_heads.
+ * Layout (this library's own): float O[nwg][nrows][head_dim] holding the
+ * unnormalised output of each split, then float SM[nwg][nrows][2] holding
+ * (S, M): the split's softmax denominator and its running maximum in base-2
+ * units (log2(e) * max logit; -inf for a split that saw no key).
+ * nrows = n_heads * q_l and row r is the output row (r = i * n_heads + h on
+ * the fp path, r = q_idx * q_l + i on the quantized path).
+ */
+TA_API size_t tree_attn_partials_bytes(uint32_t n_heads, uint32_t head_dim,
+                                uint32_t q_l, uint32_t nwg);
+
+/*
+ * A split count for tree_attn_forward that fills `num_cus` compute units
+ * (0 means 256, MI355X), given the problem shape.  Pure function of its
+ * arguments (no device query).  Always >= 1.  Callers pass the result as
+ * `nwg` to the forward call, size the partials with it and pass it to
+ * tree_attn_reduce.
+ */
+TA_API uint32_t tree_attn_pick_nwg(uint32_t n_heads, uint32_t n_kv_heads,
+                            uint32_t head_dim, uint32_t kv_seq_len,
+                            uint32_t q_l, int kv_dtype, uint32_t num_cus);
+
+/* The same for tree_attn_quant_forward. */
+TA_API uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
+                                  uint32_t n_kv_heads, uint32_t dim,
+                                  uint32_t kv_seq_len, uint32_t q_l,
+                                  uint32_t num_cus);
+
+/*
+ * Tree-attention forward pass ([TA] tree_attention_impl; [OPS]
+ * tree_attention()).  For every node i < q_l and query head h < n_heads,
+ * with kv head hk = h / (n_heads / n_kv_heads) ([TA] GQA mapping):
+ *   logit_j = scale * dot(q[h, i, :], k[hk, j, :]) + mask[i, j]  for j < kv_seq_len
+ *   out[i, h, :] = sum_j softmax(logit)_j * v[hk, j, :]
+ * where keys with mask[i, j] <= TA_MASKED are left out, and a row that
+ * keeps no key yields zeros ([TA] writes 0 when the sum S is 0).
+ *
+ *   q     DEVICE f32  [n_heads, q_l, head_dim]               (q_bytes)
+ *   k, v  DEVICE kv_dtype (TA_F32 or TA_F16)
+ *                     [n_kv_heads, kv_capacity, head_dim]    (kv_bytes each)
+ *         Rows j >= kv_seq_len are never read.
+ *   mask  DEVICE f32  [q_l, mask_stride], row-major, mask_stride >= kv_seq_len
+ *         (mask_bytes >= q_l * mask_stride * 4); cells j >= kv_seq_len are
+ *         never read ([OPS] tree_attention() doc).  mask == NULL selects the
+ *         implicit causal rule of [TA] header: node i sees key j iff
+ *         j <= kv_seq_len - q_l + i.  An explicit mask that encodes that
+ *         same rule gives a byte-identical result.
+ *   nwg   number of KV splits (>= 1).  nwg == 1: the final result is written
+ *         to `out` and `partials` may be NULL.  nwg > 1: the per-split
+ *         results go to `partials` (size tree_attn_partials_bytes(n_heads,
+ *         head_dim, q_l, nwg)), `out` is not touched and may be NULL, and
+ *         tree_attn_reduce must follow on the same stream.
+ *   out   DEVICE f32  [q_l, n_heads, head_dim] -- query-outer, head-inner,
+ *         NOT Q's layout ([OPS] tree_attention() doc).
+ *
+ * head_dim must be 128, 256 or 512 ([OPS] validate_params); n_heads and
+ * n_kv_heads > 0 with n_heads % n_kv_heads == 0; kv_seq_len > 0;
+ * kv_capacity >= kv_seq_len; q_l > 0.  fp16 K/V are contracted with fp16
+ * operands and fp32 accumulation (Q rounded to fp16 after scaling); fp32 K/V
+ * are contracted in fp32.
+ */
+TA_API int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
+                      const void *v, int kv_dtype, size_t kv_bytes,
+                      const float *mask, size_t mask_bytes, float *partials,
+                      size_t partials_bytes, float *out, size_t out_bytes,
+                      uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                      uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
+                      uint32_t mask_stride, float scale, uint32_t nwg,
+                      void *stream);
+
+/*
+ * Log-sum-exp merge of split partial results (the reduce pass that [TA]
+ * header and [OPS] tree_attention() run after the main kernel).  For each
+ * row r, over the splits w with S_w > 0:
+ *   M* = max_w M_w,  S* = sum_w S_w 2^(M_w - M*),
+ *   out[r, :] = sum_w O_w[r, :] 2^(M_w - M*) / S*,  and 0 if no split saw a key.
+ *
+ *   partials  DEVICE f32, layout of tree_attn_partials_bytes, for `nrows`
+ *             rows, `head_dim` columns and `nwg` splits.
+ *   out       DEVICE out_dtype (TA_F32 or TA_F16) [nrows, head_dim];
+ *             fp16 results are rounded to nearest even.
+ * head_dim must be a multiple of 4 in [4, 512]; nwg >= 1.
+ */
+TA_API int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
+                     int out_dtype, size_t out_bytes, uint32_t nrows,
+                     uint32_t head_dim, uint32_t nwg, void *stream);
+
+/*
+ * Attention over an affine-quantized K/V cache ([FQS] Layout, base and
+ * float-mask kernel macros), generalised to q_l queries per head and split
+ * over KV ranges like tree_attn_forward.  For query row q_idx = b*n_q_heads
+ * + h (b < batch) and node i < q_l, kv stream kv = q_idx / (n_q_heads /
+ * n_kv_heads) ([FQS] GQA mapping), element d of token t is
+ *   x = scale_g * code + bias_g,  g = d / group_size,
+ *   code = (word[d / pf] >> ((d % pf) * bits)) & (2^bits - 1),  pf = 32/bits,
+ * and
+ *   logit_t = scale * dot(q[q_idx, i, :], K_t) + maskv(q_idx, i, t)
+ *   out[q_idx, i, :] = softmax over {keys, sink} of the values (sink value 0)
+ * The sink, when `sinks` is given, is one virtual key with raw logit
+ * sinks[q_idx % n_q_heads] (no scale, no mask) ([FQS] accumulator start).
+ * maskv is an additive fp16 bias ([FQS] float-mask macro): cell at element
+ * offset q_idx*mask_head_stride + i*mask_stride + t; cells <= TA_MASKED
+ * exclude the key.  mask_head_stride = q_l*mask_stride gives a per-row
+ * mask ([FQS] shape [B*nQ, tokens] when q_l = 1); 0 broadcasts one
+ * [q_l, mask_stride] tree mask to every head.  mask == NULL selects the
+ * implicit causal rule (every token when q_l = 1).
+ *
+ *   q          DEVICE f16 [batch*n_q_heads, q_l, dim]                (q_bytes)
+ *   k_packed   DEVICE u32 [batch*n_kv_heads, kv_capacity, dim/pf]    (kv_bytes[0])
+ *   k_scales   DEVICE f16 [batch*n_kv_heads, kv_capacity, dim/group] (kv_bytes[1])
+ *   k_biases   DEVICE f16 same shape as k_scales                     (kv_bytes[2])
+ *   v_packed, v_scales, v_biases: same shapes                (kv_bytes[3..5])
+ *   sinks      DEVICE f32 [n_q_heads] or NULL                        (sinks_bytes)
+ *   mask       DEVICE f16 or NULL                                    (mask_bytes)
+ *   partials   as tree_attn_forward with n_heads = batch*n_q_heads
+ *   out        DEVICE f16 [batch*n_q_heads, q_l, dim], written iff nwg == 1
+ *
+ * q_dtype must be TA_F16 (scales, biases, mask and out share it); bits is
+ * 4 or 8; dim is 64, 128, 256 or 512; group_size is 32, 64 or 128 and
+ * divides dim; kv_capacity >= kv_seq_len > 0; mask_stride >= kv_seq_len when
+ * a mask is given.  With nwg > 1 follow with tree_attn_reduce(out_dtype =
+ * TA_F16, nrows = batch*n_q_heads*q_l, head_dim = dim).
+ */
+TA_API int tree_attn_quant_forward(
+    const void *q, int q_dtype, size_t q_bytes, const uint32_t *k_packed,
+    const void *k_scales, const void *k_biases, const uint32_t *v_packed,
+    const void *v_scales, const void *v_biases, const size_t kv_bytes[6],
+    const float *sinks, size_t sinks_bytes, const void *mask,
+    size_t mask_bytes, uint64_t mask_head_stride, uint32_t mask_stride,
+    float *partials, size_t partials_bytes, void *out, size_t out_bytes,
+    uint32_t batch, uint32_t n_q_heads, uint32_t n_kv_heads, uint32_t dim,
+    uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l, uint32_t bits,
+    uint32_t group_size, float scale, uint32_t nwg, void *stream);
+
+/*
+ * Build the explicit tree mask on the device ([TA] header: chains, fixed
+ * and dynamic trees all reduce to a [q_l, kv_seq_len] mask of 0 / -65504).
+ * Node i sits at KV position kv_seq_len - q_l + i; row i is TA_ATTENDED on
+ * the prefix [0, kv_seq_len - q_l), on the positions of node i's ancestors
+ * and on its own position, and TA_MASKED everywhere else, including the
+ * padding columns [kv_seq_len, mask_stride).
+ *
+ *   parents  HOST i32 [q_l]: parents[0] == -1 and 0 <= parents[i] < i.
+ *            Read before the call returns; not retained.
+ *   mask     DEVICE f32 [q_l, mask_stride]   (mask_bytes >= q_l*mask_stride*4)
+ * 1 <= q_l <= 1024 (else TA_EUNSUPPORTED), q_l <= kv_seq_len <= mask_stride.
+ */
+TA_API int build_tree_mask(const int32_t *parents, uint32_t q_l, uint32_t kv_seq_len,
+                    uint32_t mask_stride, float *mask, size_t mask_bytes,
+                    void *stream);
+
+/* Message for the last error returned on the calling thread ("" if none). */
+TA_API const char *tree_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -1,0 +1,278 @@
+"""GPU parity of the fp path (tree mask, forward, reduce) against the oracle.
+
+Tolerances are the contract's: max-abs 1e-4 for fp32 K/V, 2e-3 for fp16
+K/V.  An explicit chain mask must reproduce the implicit causal path byte
+for byte ("tree_attention.metal" header: the "tree=1" parity gate).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tree_masked_decode_amd import inputs
+
+from helpers import assert_close, dev, host, note, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "f16": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def ta():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import tree_masked_decode_amd as ta
+    ta._api()  # the HIP library must load
+    return ta
+
+
+def gpu_case(c, mask_np):
+    return (dev(c["q"]), dev(c["k"]), dev(c["v"]),
+            None if mask_np is None else dev(mask_np))
+
+
+def run_verify(ta, c, mask_np, nwg=None, **kw):
+    import torch
+    q, k, v, m = gpu_case(c, mask_np)
+    out = ta.verify(q, k, v, m, kv_seq_len=c["kv_seq_len"], scale=c["scale"],
+                    nwg=nwg, **kw)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def small_case(seed, H, Hk, D, L, q_l, kvd, tree="dynamic", cap=None, stride=None):
+    return inputs.fp_case(dict(n_heads=H, n_kv_heads=Hk, head_dim=D, kv_seq_len=L,
+                               kv_capacity=cap or L + 7, q_l=q_l, tree=tree,
+                               mask_stride=stride or L, kv_dtype=kvd, kv_std=1.0),
+                          seed=seed)
+
+
+# --------------------------------------------------------------------------
+# tree mask
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("kind,q_l,L,stride", [
+    ("chain", 4, 256, 256), ("binary", 16, 4096, 4096), ("dynamic", 64, 32768, 32768),
+    ("chain", 8, 1000, 1003), ("dynamic", 1, 1, 1), ("dynamic", 300, 300, 301),
+    ("binary", 1024, 5000, 5000)])
+def test_tree_mask_bit_exact(ta, kind, q_l, L, stride):
+    import torch
+    note("tree_mask %s q_l=%d L=%d stride=%d" % (kind, q_l, L, stride))
+    parents = inputs.parents_for(kind, q_l, seed=0)
+    got = ta.build_tree_mask(parents, L, stride)
+    torch.cuda.synchronize()
+    ref = oracle.tree_mask(parents, L, stride)
+    assert np.array_equal(host(got), ref)
+
+
+# --------------------------------------------------------------------------
+# forward + reduce parity on small shapes (several tiles, ragged tails)
+# --------------------------------------------------------------------------
+SMALL = [
+    # seed, H, Hk, D, L, q_l, kv dtype, nwg
+    (0, 4, 2, 128, 333, 5, "f32", 1),
+    (1, 4, 2, 128, 333, 5, "f32", 3),
+    (2, 8, 2, 256, 1000, 7, "f32", None),
+    (3, 4, 4, 512, 257, 3, "f32", 2),
+    (4, 4, 2, 128, 1000, 5, "f16", 1),
+    (5, 12, 2, 256, 777, 16, "f16", 4),
+    (6, 24, 4, 256, 1500, 16, "f16", None),
+    (7, 8, 8, 512, 611, 9, "f16", 3),
+    (8, 6, 1, 128, 2049, 33, "f16", 5),   # 198 rows: 4 row tiles, last ragged
+    (9, 2, 1, 256, 65, 1, "f16", 7),      # more splits than tiles
+]
+
+
+@pytest.mark.parametrize("seed,H,Hk,D,L,q_l,kvd,nwg", SMALL)
+def test_forward_parity_small(ta, seed, H, Hk, D, L, q_l, kvd, nwg):
+    note("fp small seed=%d H=%d Hk=%d D=%d L=%d q_l=%d %s nwg=%s" %
+         (seed, H, Hk, D, L, q_l, kvd, nwg))
+    c = small_case(seed, H, Hk, D, L, q_l, kvd)
+    mask = oracle.tree_mask(c["parents"], L, c["mask_stride"])
+    got = run_verify(ta, c, mask, nwg=nwg)
+    ref = oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=Hk,
+                           kv_seq_len=L, scale=c["scale"])
+    assert_close(got, ref, TOL[kvd], "small %d" % seed)
+
+
+# --------------------------------------------------------------------------
+# the workloads at full size
+# --------------------------------------------------------------------------
+def test_workload_tiny_chain(ta):
+    note("workload tiny_chain")
+    c = inputs.fp_case("tiny_chain")
+    mask = oracle.tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"])
+    got = run_verify(ta, c, mask, nwg=c["nwg"])
+    ref = oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
+                           kv_seq_len=c["kv_seq_len"], scale=c["scale"])
+    assert_close(got, ref, TOL["f32"], "tiny_chain")
+    # byte identity with the implicit causal path
+    implicit = run_verify(ta, c, None, nwg=c["nwg"])
+    assert np.array_equal(got.view(np.uint32), implicit.view(np.uint32))
+
+
+def test_workload_fixed_tree(ta):
+    note("workload fixed_tree")
+    c = inputs.fp_case("fixed_tree")
+    mask = oracle.tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"])
+    got = run_verify(ta, c, mask)
+    ref = oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
+                           kv_seq_len=c["kv_seq_len"], scale=c["scale"])
+    assert_close(got, ref, TOL["f16"], "fixed_tree")
+
+
+def _sampled(ta, name, nrows, gpu_mask=True):
+    import torch
+    c = inputs.fp_case(name)
+    L, H = c["kv_seq_len"], c["n_heads"]
+    mask_np = oracle.tree_mask(c["parents"], L, c["mask_stride"])
+    q, k, v, _ = gpu_case(c, None)
+    m = ta.build_tree_mask(c["parents"], L, c["mask_stride"])
+    nwg = ta.pick_nwg(H, c["n_kv_heads"], c["head_dim"], L, c["q_l"], 1)
+    out = ta.verify(q, k, v, m, kv_seq_len=L, scale=c["scale"], nwg=nwg)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    rows = sample_rows(c["q_l"], H, nrows)
+    ref = oracle.attention(c["q"], c["k"], c["v"], mask_np, n_kv_heads=c["n_kv_heads"],
+                           kv_seq_len=L, scale=c["scale"], rows=rows)
+    sel = np.stack([got[i, h] for i, h in rows])
+    assert_close(sel, ref, TOL["f16"], name)
+    return c, (q, k, v, m), nwg, got
+
+
+def test_workload_dynamic_tree_32k(ta):
+    note("workload dynamic_tree_32k (sampled rows)")
+    _sampled(ta, "dynamic_tree_32k", 64)
+
+
+def test_workload_long_context_128k(ta):
+    import torch
+    note("workload long_context_128k (sampled rows) + byte identity")
+    c, (q, k, v, m), nwg, got = _sampled(ta, "long_context_128k", 16)
+    implicit = ta.verify(q, k, v, None, kv_seq_len=c["kv_seq_len"], scale=c["scale"],
+                         nwg=nwg)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint32), host(implicit).view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# byte identity, poison, determinism, edges
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("kvd,D,nwg", [("f32", 128, 3), ("f16", 256, 4), ("f16", 512, 1),
+                                       ("f16", 128, 1)])
+def test_chain_mask_byte_identical_to_implicit(ta, kvd, D, nwg):
+    note("byte identity %s D=%d nwg=%d" % (kvd, D, nwg))
+    c = small_case(11, 8, 2, D, 517, 9, kvd, tree="chain")
+    mask = oracle.tree_mask(c["parents"], 517, 517)
+    a = run_verify(ta, c, mask, nwg=nwg)
+    b = run_verify(ta, c, None, nwg=nwg)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("kvd", ["f32", "f16"])
+def test_unread_regions_poisoned(ta, kvd):
+    import torch
+    note("poison %s" % kvd)
+    L, stride, cap = 700, 709, 900
+    c = small_case(12, 8, 2, 256, L, 9, kvd, cap=cap, stride=stride)
+    mask = oracle.tree_mask(c["parents"], L, stride)
+    clean = run_verify(ta, c, mask, nwg=3)
+    # K/V capacity tail -> NaN; mask padding -> 0 ("attended" if it were read)
+    p = dict(c)
+    p["k"] = c["k"].copy()
+    p["v"] = c["v"].copy()
+    p["k"][:, L:] = np.nan
+    p["v"][:, L:] = np.nan
+    pm = mask.copy()
+    pm[:, L:] = 0.0
+    q, k, v, m = gpu_case(p, pm)
+    H, q_l, D = c["q"].shape
+    # partial scratch pre-filled with NaN; output with a canary tail
+    import tree_masked_decode_amd as T
+    part = torch.full((T.partials_bytes(H, D, q_l, 3) // 4,), float("nan"), device="cuda")
+    flat = torch.full((q_l * H * D + 64,), 12345.0, device="cuda")
+    out = flat[: q_l * H * D].view(q_l, H, D)
+    T.verify(q, k, v, m, kv_seq_len=L, scale=c["scale"], nwg=3, out=out, partials=part)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint32), clean.view(np.uint32))
+    assert torch.all(flat[q_l * H * D:] == 12345.0)
+
+
+def test_deterministic(ta):
+    note("determinism")
+    c = small_case(13, 24, 4, 256, 3000, 16, "f16", tree="binary")
+    mask = oracle.tree_mask(c["parents"], 3000)
+    a = run_verify(ta, c, mask)
+    b = run_verify(ta, c, mask)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("kvd", ["f32", "f16"])
+def test_edges(ta, kvd):
+    note("edges %s" % kvd)
+    tol = TOL[kvd]
+    # one key
+    c = small_case(14, 4, 2, 128, 1, 1, kvd, tree="chain", cap=1)
+    got = run_verify(ta, c, None, nwg=1)
+    ref = oracle.attention(c["q"], c["k"], c["v"], None, n_kv_heads=2, kv_seq_len=1,
+                           scale=c["scale"])
+    assert_close(got, ref, tol, "L=1")
+    # whole cache is the tree (no prefix), implicit rule with q_l > L
+    c = small_case(15, 4, 1, 256, 40, 40, kvd)
+    m = oracle.tree_mask(c["parents"], 40)
+    assert_close(run_verify(ta, c, m, nwg=2),
+                 oracle.attention(c["q"], c["k"], c["v"], m, n_kv_heads=1, kv_seq_len=40,
+                                  scale=c["scale"]), tol, "q_l=L")
+    c = small_case(16, 2, 1, 128, 5, 9, kvd, tree="chain")
+    assert_close(run_verify(ta, c, None, nwg=2),
+                 oracle.attention(c["q"], c["k"], c["v"], None, n_kv_heads=1, kv_seq_len=5,
+                                  scale=c["scale"]), tol, "q_l>L implicit")
+    # rows with no visible key -> 0; fully masked prefix -> ancestors only
+    c = small_case(17, 8, 2, 256, 1200, 12, kvd)
+    m = oracle.tree_mask(c["parents"], 1200)
+    m[:, :1200 - 12] = -65504.0
+    m[3, :] = -65504.0
+    got = run_verify(ta, c, m, nwg=4)
+    assert np.all(got[3] == 0.0)
+    assert_close(got, oracle.attention(c["q"], c["k"], c["v"], m, n_kv_heads=2,
+                                       kv_seq_len=1200, scale=c["scale"]), tol, "masked")
+    # additive (non-sentinel) mask values
+    c = small_case(18, 4, 2, 128, 300, 4, kvd)
+    m = np.random.default_rng(3).uniform(-4, 1, size=(4, 300)).astype(np.float32)
+    assert_close(run_verify(ta, c, m, nwg=2),
+                 oracle.attention(c["q"], c["k"], c["v"], m, n_kv_heads=2, kv_seq_len=300,
+                                  scale=c["scale"]), tol, "additive")
+
+
+def test_unaligned_mask_stride(ta):
+    note("odd mask stride (scalar mask path)")
+    c = small_case(19, 8, 2, 256, 501, 6, "f16", stride=503)
+    m = oracle.tree_mask(c["parents"], 501, 503)
+    assert_close(run_verify(ta, c, m, nwg=2),
+                 oracle.attention(c["q"], c["k"], c["v"], m, n_kv_heads=2, kv_seq_len=501,
+                                  scale=c["scale"]), TOL["f16"], "stride 503")
+
+
+def test_reduce_alone_on_oracle_partials(ta):
+    """Feed exact partials from the oracle's split into the reduce kernel."""
+    import torch
+    note("reduce alone")
+    c = small_case(20, 4, 2, 128, 90, 3, "f32")
+    m = oracle.tree_mask(c["parents"], 90)
+    bounds = [0, 0, 17, 50, 50, 90]
+    o_un, s, mx = oracle.attention_partials(c["q"], c["k"], c["v"], m, bounds,
+                                            n_kv_heads=2, kv_seq_len=90, scale=c["scale"])
+    nrows, nw, D = o_un.shape
+    # this library's layout: O[w][row][D], then (S, M) [w][row][2], M in base 2
+    po = np.transpose(o_un, (1, 0, 2)).astype(np.float32).ravel()
+    sm = np.stack([s.T, mx.T * (1.0 / math.log(2.0))], axis=-1).astype(np.float32).ravel()
+    part = dev(np.concatenate([po, sm]))
+    import tree_masked_decode_amd as T
+    for dt, tol in ((torch.float32, 1e-5), (torch.float16, 2e-3)):
+        out = torch.empty((nrows, D), dtype=dt, device="cuda")
+        T.tree_attn_reduce(part, out, nrows=nrows, head_dim=D, nwg=nw)
+        torch.cuda.synchronize()
+        assert_close(host(out), oracle.lse_combine(o_un, s, mx), tol, "reduce")

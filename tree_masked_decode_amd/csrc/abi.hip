@@ -1,0 +1,464 @@
+// abi.hip -- the extern "C" entry points of libtreeattn.so: argument and
+// buffer validation, launch planning and kernel dispatch.
+//
+// Validation follows "ops/tree_attention.rs" (mlx-native 0.9.2),
+// validate_params and validate_buffers: supported head dims, head counts
+// and divisibility, kv_seq_len / kv_capacity / q_l / mask_stride rules, and
+// byte-size checks done with overflow-checked arithmetic so that a huge
+// shape cannot wrap into a small requirement.  Every check runs before any
+// HIP call; a failing call enqueues nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/tree_attn.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return TA_OK;
+}
+
+// Overflow-checked products.
+bool mul_ok(uint64_t a, uint64_t b, uint64_t &r) {
+  if (a != 0 && b > UINT64_MAX / a) return false;
+  r = a * b;
+  return true;
+}
+bool mul3(uint64_t a, uint64_t b, uint64_t c, uint64_t &r) {
+  uint64_t t;
+  return mul_ok(a, b, t) && mul_ok(t, c, r);
+}
+bool mul4(uint64_t a, uint64_t b, uint64_t c, uint64_t d, uint64_t &r) {
+  uint64_t t;
+  return mul3(a, b, c, t) && mul_ok(t, d, r);
+}
+bool add_ok(uint64_t a, uint64_t b, uint64_t &r) {
+  if (b > UINT64_MAX - a) return false;
+  r = a + b;
+  return true;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess)
+    return fail(TA_EHIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Largest split count accepted (keeps every grid dimension and index in
+// range; far beyond any useful value).
+constexpr uint32_t kMaxNwg = 65536;
+
+uint64_t partials_bytes_u64(uint64_t nrows, uint64_t dim, uint64_t nwg,
+                            bool &overflow) {
+  uint64_t r;
+  overflow = !mul4(nrows, nwg, dim + 2, 4, r);
+  return overflow ? UINT64_MAX : r;
+}
+
+// Split count that gives about `target` workgroups, at least 2 tiles per
+// split and no more splits than tiles.
+uint32_t pick_splits(uint32_t units_per_split, uint32_t n_tiles,
+                     uint32_t num_cus, uint32_t waves_per_cu_target) {
+  if (num_cus == 0) num_cus = 256;
+  uint64_t target = (uint64_t)num_cus * waves_per_cu_target;
+  uint64_t nwg = (target + units_per_split - 1) / units_per_split;
+  uint64_t max_by_tiles = n_tiles >= 4 ? n_tiles / 2 : 1;
+  if (nwg > max_by_tiles) nwg = max_by_tiles;
+  if (nwg < 1) nwg = 1;
+  if (nwg > kMaxNwg) nwg = kMaxNwg;
+  return (uint32_t)nwg;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tree_attn_last_error(void) { return g_err.c_str(); }
+
+size_t tree_attn_partials_bytes(uint32_t n_heads, uint32_t head_dim,
+                                uint32_t q_l, uint32_t nwg) {
+  bool of;
+  uint64_t r = partials_bytes_u64((uint64_t)n_heads * q_l, head_dim, nwg, of);
+  if (of || r > (uint64_t)SIZE_MAX) return SIZE_MAX;
+  return (size_t)r;
+}
+
+uint32_t tree_attn_pick_nwg(uint32_t n_heads, uint32_t n_kv_heads,
+                            uint32_t head_dim, uint32_t kv_seq_len,
+                            uint32_t q_l, int kv_dtype, uint32_t num_cus) {
+  if (n_heads == 0 || n_kv_heads == 0 || kv_seq_len == 0 || q_l == 0 ||
+      n_heads % n_kv_heads != 0)
+    return 1;
+  uint32_t rows = q_l * (n_heads / n_kv_heads);
+  bool f16 = kv_dtype == TA_F16;
+  uint32_t rpw = f16 ? ta::kF16RowsPerWG : ta::kF32RowsPerWG;
+  uint32_t bn = f16 ? ta::f16_tile_keys(head_dim) : ta::f32_tile_keys(head_dim);
+  uint32_t units = n_kv_heads * ceil_div(rows, rpw);
+  // Two resident workgroups per CU for head_dim <= 256, one for 512.
+  uint32_t per_cu = (head_dim >= 512) ? 1u : 2u;
+  return pick_splits(units, ceil_div(kv_seq_len, bn), num_cus, per_cu);
+}
+
+uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
+                                  uint32_t n_kv_heads, uint32_t dim,
+                                  uint32_t kv_seq_len, uint32_t q_l,
+                                  uint32_t num_cus) {
+  if (batch == 0 || n_q_heads == 0 || n_kv_heads == 0 || kv_seq_len == 0 ||
+      q_l == 0 || n_q_heads % n_kv_heads != 0)
+    return 1;
+  uint32_t rows = q_l * (n_q_heads / n_kv_heads);
+  uint32_t units = batch * n_kv_heads * ceil_div(rows, ta::kQuantRowsPerWG);
+  return pick_splits(units, ceil_div(kv_seq_len, ta::quant_tile_keys(dim)),
+                     num_cus, 4u);
+}
+
+int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
+                      const void *v, int kv_dtype, size_t kv_bytes,
+                      const float *mask, size_t mask_bytes, float *partials,
+                      size_t partials_bytes, float *out, size_t out_bytes,
+                      uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                      uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
+                      uint32_t mask_stride, float scale, uint32_t nwg,
+                      void *stream) {
+  const char *fn = "tree_attn_forward";
+  // --- parameter contract ("ops/tree_attention.rs", validate_params) ---
+  if (head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(TA_EUNSUPPORTED, "%s: head_dim must be 128, 256, or 512, got %u",
+                fn, head_dim);
+  if (n_heads == 0 || n_kv_heads == 0)
+    return fail(TA_EINVAL, "%s: n_heads and n_kv_heads must be > 0", fn);
+  if (n_heads % n_kv_heads != 0)
+    return fail(TA_EINVAL, "%s: n_heads (%u) must be divisible by n_kv_heads (%u)",
+                fn, n_heads, n_kv_heads);
+  if (kv_seq_len == 0) return fail(TA_EINVAL, "%s: kv_seq_len must be > 0", fn);
+  if (kv_capacity < kv_seq_len)
+    return fail(TA_EINVAL, "%s: kv_capacity (%u) must be >= kv_seq_len (%u)", fn,
+                kv_capacity, kv_seq_len);
+  if (q_l == 0) return fail(TA_EINVAL, "%s: q_seq_len (q_l) must be > 0", fn);
+  if (mask != nullptr && mask_stride < kv_seq_len)
+    return fail(TA_EINVAL, "%s: mask_stride (%u) must be >= kv_seq_len (%u)", fn,
+                mask_stride, kv_seq_len);
+  if (kv_dtype != TA_F32 && kv_dtype != TA_F16)
+    return fail(TA_EUNSUPPORTED, "%s: k/v dtype must be TA_F32 or TA_F16, got %d",
+                fn, kv_dtype);
+  if (nwg == 0 || nwg > kMaxNwg)
+    return fail(TA_EINVAL, "%s: nwg must be in [1, %u], got %u", fn, kMaxNwg, nwg);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(TA_EINVAL, "%s: scale must be finite", fn);
+
+  // --- pointers ---
+  if (!q || !k || !v) return fail(TA_EINVAL, "%s: q, k and v must not be NULL", fn);
+  if (nwg == 1 && !out) return fail(TA_EINVAL, "%s: out must not be NULL when nwg == 1", fn);
+  if (nwg > 1 && !partials)
+    return fail(TA_EINVAL, "%s: partials must not be NULL when nwg > 1", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      (out && !aligned16(out)) || (partials && !aligned16(partials)) ||
+      (mask && ((uintptr_t)mask & 3u)))
+    return fail(TA_EINVAL, "%s: device pointers must be 16-byte aligned (mask 4-byte)", fn);
+
+  // --- byte-length contract ("ops/tree_attention.rs", validate_buffers) ---
+  const uint64_t esz = kv_dtype == TA_F16 ? 2 : 4;
+  uint64_t req_q, req_kv, req_mask = 0, req_out, req_part = 0;
+  if (!mul4(n_heads, q_l, head_dim, 4, req_q))
+    return fail(TA_EOVERFLOW, "%s: n_heads*q_l*head_dim*4 overflows", fn);
+  if (!mul4(n_kv_heads, kv_capacity, head_dim, esz, req_kv))
+    return fail(TA_EOVERFLOW, "%s: n_kv_heads*kv_capacity*head_dim*esize overflows", fn);
+  if (mask && !mul3(q_l, mask_stride, 4, req_mask))
+    return fail(TA_EOVERFLOW, "%s: q_l*mask_stride*4 overflows", fn);
+  req_out = req_q;
+  bool of = false;
+  if (nwg > 1) req_part = partials_bytes_u64((uint64_t)n_heads * q_l, head_dim, nwg, of);
+  if (of) return fail(TA_EOVERFLOW, "%s: partials size overflows", fn);
+  if (q_bytes < req_q)
+    return fail(TA_ESIZE, "%s: q buffer too small: have %zu bytes, need >= %llu", fn,
+                q_bytes, (unsigned long long)req_q);
+  if (kv_bytes < req_kv)
+    return fail(TA_ESIZE, "%s: k/v buffer too small: have %zu bytes, need >= %llu", fn,
+                kv_bytes, (unsigned long long)req_kv);
+  if (mask && mask_bytes < req_mask)
+    return fail(TA_ESIZE, "%s: tree_mask buffer too small: have %zu bytes, need >= %llu",
+                fn, mask_bytes, (unsigned long long)req_mask);
+  if (nwg == 1 && out_bytes < req_out)
+    return fail(TA_ESIZE, "%s: output buffer too small: have %zu bytes, need >= %llu", fn,
+                out_bytes, (unsigned long long)req_out);
+  if (nwg > 1 && partials_bytes < req_part)
+    return fail(TA_ESIZE, "%s: partials buffer too small: have %zu bytes, need >= %llu",
+                fn, partials_bytes, (unsigned long long)req_part);
+  // row count per kv head and the grid must fit the kernels' 32-bit indices
+  uint64_t rows = (uint64_t)q_l * (n_heads / n_kv_heads);
+  if ((uint64_t)n_heads * q_l > 0x7fffffffull || rows > 0x7fffffffull)
+    return fail(TA_EUNSUPPORTED, "%s: n_heads*q_l too large", fn);
+
+  // --- plan and launch ---
+  ta::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.mask = mask;
+  a.out = out;
+  a.n_heads = n_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.group = n_heads / n_kv_heads;
+  a.kv_seq_len = kv_seq_len;
+  a.kv_capacity = kv_capacity;
+  a.q_l = q_l;
+  a.mask_stride = mask ? mask_stride : kv_seq_len;
+  a.nwg = nwg;
+  a.rows = (uint32_t)rows;
+  a.qscale = scale * ta::kLog2e;
+  const bool f16 = kv_dtype == TA_F16;
+  const uint32_t rpw = f16 ? ta::kF16RowsPerWG : ta::kF32RowsPerWG;
+  const uint32_t bn = f16 ? ta::f16_tile_keys(head_dim) : ta::f32_tile_keys(head_dim);
+  a.row_tiles = ceil_div(a.rows, rpw);
+  a.n_tiles = ceil_div(kv_seq_len, bn);
+  uint64_t units = (uint64_t)n_kv_heads * nwg;
+  uint64_t blocks = (uint64_t)ta::kXcds * ((units + ta::kXcds - 1) / ta::kXcds) * a.row_tiles;
+  if (blocks > 0x7fffffffull)
+    return fail(TA_EUNSUPPORTED, "%s: grid too large (n_kv_heads*nwg*row tiles)", fn);
+  a.units = (uint32_t)units;
+  if (nwg > 1) {
+    a.part_o = partials;
+    a.part_sm = partials + (size_t)nwg * n_heads * q_l * head_dim;
+  } else {
+    a.part_o = a.part_sm = nullptr;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = f16 ? ta::launch_forward_f16(a, head_dim, s)
+                     : ta::launch_forward_f32(a, head_dim, s);
+  return hip_status(e, fn);
+}
+
+int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
+                     int out_dtype, size_t out_bytes, uint32_t nrows,
+                     uint32_t head_dim, uint32_t nwg, void *stream) {
+  const char *fn = "tree_attn_reduce";
+  if (nrows == 0) return fail(TA_EINVAL, "%s: nrows must be > 0", fn);
+  if (head_dim == 0 || head_dim % 4 != 0 || head_dim > 512)
+    return fail(TA_EUNSUPPORTED, "%s: head_dim must be a multiple of 4 in [4, 512], got %u",
+                fn, head_dim);
+  if (nwg == 0 || nwg > kMaxNwg)
+    return fail(TA_EINVAL, "%s: nwg must be in [1, %u], got %u", fn, kMaxNwg, nwg);
+  if (out_dtype != TA_F32 && out_dtype != TA_F16)
+    return fail(TA_EUNSUPPORTED, "%s: out dtype must be TA_F32 or TA_F16", fn);
+  if (!partials || !out) return fail(TA_EINVAL, "%s: partials and out must not be NULL", fn);
+  if (!aligned16(partials) || ((uintptr_t)out & 7u))
+    return fail(TA_EINVAL, "%s: partials must be 16-byte and out 8-byte aligned", fn);
+  bool of;
+  uint64_t req_part = partials_bytes_u64(nrows, head_dim, nwg, of);
+  uint64_t req_out;
+  if (of || !mul3(nrows, head_dim, out_dtype == TA_F16 ? 2 : 4, req_out))
+    return fail(TA_EOVERFLOW, "%s: size computation overflows", fn);
+  if (partials_bytes < req_part)
+    return fail(TA_ESIZE, "%s: partials buffer too small: have %zu bytes, need >= %llu",
+                fn, partials_bytes, (unsigned long long)req_part);
+  if (out_bytes < req_out)
+    return fail(TA_ESIZE, "%s: output buffer too small: have %zu bytes, need >= %llu", fn,
+                out_bytes, (unsigned long long)req_out);
+  if (nrows > 0x7ffffff0u) return fail(TA_EUNSUPPORTED, "%s: nrows too large", fn);
+  ta::ReduceArgs a;
+  a.part_o = partials;
+  a.part_sm = partials + (size_t)nwg * nrows * head_dim;
+  a.out = out;
+  a.nrows = nrows;
+  a.dim = head_dim;
+  a.nwg = nwg;
+  a.out_f16 = out_dtype == TA_F16;
+  return hip_status(ta::launch_reduce(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int tree_attn_quant_forward(
+    const void *q, int q_dtype, size_t q_bytes, const uint32_t *k_packed,
+    const void *k_scales, const void *k_biases, const uint32_t *v_packed,
+    const void *v_scales, const void *v_biases, const size_t kv_bytes[6],
+    const float *sinks, size_t sinks_bytes, const void *mask,
+    size_t mask_bytes, uint64_t mask_head_stride, uint32_t mask_stride,
+    float *partials, size_t partials_bytes, void *out, size_t out_bytes,
+    uint32_t batch, uint32_t n_q_heads, uint32_t n_kv_heads, uint32_t dim,
+    uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l, uint32_t bits,
+    uint32_t group_size, float scale, uint32_t nwg, void *stream) {
+  const char *fn = "tree_attn_quant_forward";
+  if (q_dtype != TA_F16)
+    return fail(TA_EUNSUPPORTED, "%s: queries/scales/biases/out dtype must be TA_F16", fn);
+  if (bits != 4 && bits != 8)
+    return fail(TA_EUNSUPPORTED, "%s: bits must be 4 or 8, got %u", fn, bits);
+  if (dim != 64 && dim != 128 && dim != 256 && dim != 512)
+    return fail(TA_EUNSUPPORTED, "%s: dim must be 64, 128, 256 or 512, got %u", fn, dim);
+  if (group_size != 32 && group_size != 64 && group_size != 128)
+    return fail(TA_EUNSUPPORTED, "%s: group_size must be 32, 64 or 128, got %u", fn,
+                group_size);
+  if (dim % group_size != 0)
+    return fail(TA_EINVAL, "%s: dim (%u) must be divisible by group_size (%u)", fn, dim,
+                group_size);
+  if (batch == 0 || n_q_heads == 0 || n_kv_heads == 0)
+    return fail(TA_EINVAL, "%s: batch, n_q_heads and n_kv_heads must be > 0", fn);
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(TA_EINVAL, "%s: n_q_heads (%u) must be divisible by n_kv_heads (%u)", fn,
+                n_q_heads, n_kv_heads);
+  if (kv_seq_len == 0) return fail(TA_EINVAL, "%s: kv_seq_len must be > 0", fn);
+  if (kv_capacity < kv_seq_len)
+    return fail(TA_EINVAL, "%s: kv_capacity (%u) must be >= kv_seq_len (%u)", fn,
+                kv_capacity, kv_seq_len);
+  if (q_l == 0) return fail(TA_EINVAL, "%s: q_seq_len (q_l) must be > 0", fn);
+  if (mask != nullptr && mask_stride < kv_seq_len)
+    return fail(TA_EINVAL, "%s: mask_stride (%u) must be >= kv_seq_len (%u)", fn,
+                mask_stride, kv_seq_len);
+  if (nwg == 0 || nwg > kMaxNwg)
+    return fail(TA_EINVAL, "%s: nwg must be in [1, %u], got %u", fn, kMaxNwg, nwg);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(TA_EINVAL, "%s: scale must be finite", fn);
+  if (!kv_bytes) return fail(TA_EINVAL, "%s: kv_bytes must not be NULL", fn);
+  if (!q || !k_packed || !k_scales || !k_biases || !v_packed || !v_scales || !v_biases)
+    return fail(TA_EINVAL, "%s: q and the six K/V buffers must not be NULL", fn);
+  if (nwg == 1 && !out) return fail(TA_EINVAL, "%s: out must not be NULL when nwg == 1", fn);
+  if (nwg > 1 && !partials)
+    return fail(TA_EINVAL, "%s: partials must not be NULL when nwg > 1", fn);
+  const void *ptrs[] = {q, k_packed, k_scales, k_biases, v_packed, v_scales, v_biases};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(TA_EINVAL, "%s: device pointers must be 16-byte aligned", fn);
+  if ((out && !aligned16(out)) || (partials && !aligned16(partials)) ||
+      (mask && ((uintptr_t)mask & 1u)) || (sinks && ((uintptr_t)sinks & 3u)))
+    return fail(TA_EINVAL, "%s: device pointers must be 16-byte aligned", fn);
+
+  const uint64_t BnQ = (uint64_t)batch * n_q_heads, BnKV = (uint64_t)batch * n_kv_heads;
+  const uint64_t pf = 32 / bits;
+  uint64_t req_q, req_packed, req_sb, req_out, req_sinks = 0, req_mask = 0, req_part = 0;
+  if (!mul4(BnQ, q_l, dim, 2, req_q) || !mul4(BnKV, kv_capacity, dim / pf, 4, req_packed) ||
+      !mul4(BnKV, kv_capacity, dim / group_size, 2, req_sb))
+    return fail(TA_EOVERFLOW, "%s: size computation overflows", fn);
+  req_out = req_q;
+  if (sinks) req_sinks = (uint64_t)n_q_heads * 4;
+  if (mask) {
+    // last cell: (BnQ-1)*mask_head_stride + (q_l-1)*mask_stride + (kv_seq_len-1)
+    uint64_t t1, t2, t3;
+    if (!mul_ok(BnQ - 1, mask_head_stride, t1) || !mul_ok(q_l - 1, mask_stride, t2) ||
+        !add_ok(t1, t2, t3) || !add_ok(t3, kv_seq_len, t3) || !mul_ok(t3, 2, req_mask))
+      return fail(TA_EOVERFLOW, "%s: mask extent overflows", fn);
+  }
+  bool of = false;
+  if (nwg > 1) req_part = partials_bytes_u64(BnQ * q_l, dim, nwg, of);
+  if (of) return fail(TA_EOVERFLOW, "%s: partials size overflows", fn);
+  if (q_bytes < req_q)
+    return fail(TA_ESIZE, "%s: q buffer too small: have %zu bytes, need >= %llu", fn, q_bytes,
+                (unsigned long long)req_q);
+  const char *names[6] = {"k_packed", "k_scales", "k_biases", "v_packed", "v_scales", "v_biases"};
+  for (int b = 0; b < 6; ++b) {
+    uint64_t need = (b % 3 == 0) ? req_packed : req_sb;
+    if (kv_bytes[b] < need)
+      return fail(TA_ESIZE, "%s: %s buffer too small: have %zu bytes, need >= %llu", fn,
+                  names[b], kv_bytes[b], (unsigned long long)need);
+  }
+  if (sinks && sinks_bytes < req_sinks)
+    return fail(TA_ESIZE, "%s: sinks buffer too small: have %zu bytes, need >= %llu", fn,
+                sinks_bytes, (unsigned long long)req_sinks);
+  if (mask && mask_bytes < req_mask)
+    return fail(TA_ESIZE, "%s: mask buffer too small: have %zu bytes, need >= %llu", fn,
+                mask_bytes, (unsigned long long)req_mask);
+  if (nwg == 1 && out_bytes < req_out)
+    return fail(TA_ESIZE, "%s: output buffer too small: have %zu bytes, need >= %llu", fn,
+                out_bytes, (unsigned long long)req_out);
+  if (nwg > 1 && partials_bytes < req_part)
+    return fail(TA_ESIZE, "%s: partials buffer too small: have %zu bytes, need >= %llu", fn,
+                partials_bytes, (unsigned long long)req_part);
+  uint64_t rows = (uint64_t)q_l * (n_q_heads / n_kv_heads);
+  if (BnQ * q_l > 0x7fffffffull || rows > 0x7fffffffull)
+    return fail(TA_EUNSUPPORTED, "%s: batch*n_q_heads*q_l too large", fn);
+
+  ta::QuantArgs a;
+  a.q = static_cast<const ta::half_t *>(q);
+  a.kp = k_packed;
+  a.vp = v_packed;
+  a.ks = static_cast<const ta::half_t *>(k_scales);
+  a.kb = static_cast<const ta::half_t *>(k_biases);
+  a.vs = static_cast<const ta::half_t *>(v_scales);
+  a.vb = static_cast<const ta::half_t *>(v_biases);
+  a.sinks = sinks;
+  a.mask = static_cast<const ta::half_t *>(mask);
+  a.out = static_cast<ta::half_t *>(out);
+  a.mask_head_stride = mask ? mask_head_stride : 0;
+  a.mask_stride = mask ? mask_stride : kv_seq_len;
+  a.batch = batch;
+  a.nq = n_q_heads;
+  a.nkv = n_kv_heads;
+  a.repeat = n_q_heads / n_kv_heads;
+  a.kv_seq_len = kv_seq_len;
+  a.kv_capacity = kv_capacity;
+  a.q_l = q_l;
+  a.nwg = nwg;
+  a.rows = (uint32_t)rows;
+  a.row_tiles = ceil_div(a.rows, ta::kQuantRowsPerWG);
+  a.n_tiles = ceil_div(kv_seq_len, ta::quant_tile_keys(dim));
+  uint64_t units = BnKV * nwg;
+  uint64_t blocks = (uint64_t)ta::kXcds * ((units + ta::kXcds - 1) / ta::kXcds) * a.row_tiles;
+  if (blocks > 0x7fffffffull)
+    return fail(TA_EUNSUPPORTED, "%s: grid too large", fn);
+  a.units = (uint32_t)units;
+  a.qscale = scale * ta::kLog2e;
+  if (nwg > 1) {
+    a.part_o = partials;
+    a.part_sm = partials + (size_t)nwg * BnQ * q_l * dim;
+  } else {
+    a.part_o = a.part_sm = nullptr;
+  }
+  return hip_status(ta::launch_quant_forward(a, dim, bits, group_size,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int build_tree_mask(const int32_t *parents, uint32_t q_l, uint32_t kv_seq_len,
+                    uint32_t mask_stride, float *mask, size_t mask_bytes,
+                    void *stream) {
+  const char *fn = "build_tree_mask";
+  if (q_l == 0) return fail(TA_EINVAL, "%s: q_l must be > 0", fn);
+  if (q_l > (uint32_t)ta::kMaxTreeNodes)
+    return fail(TA_EUNSUPPORTED, "%s: q_l must be <= %d, got %u", fn, ta::kMaxTreeNodes, q_l);
+  if (kv_seq_len < q_l)
+    return fail(TA_EINVAL, "%s: kv_seq_len (%u) must be >= q_l (%u)", fn, kv_seq_len, q_l);
+  if (mask_stride < kv_seq_len)
+    return fail(TA_EINVAL, "%s: mask_stride (%u) must be >= kv_seq_len (%u)", fn, mask_stride,
+                kv_seq_len);
+  if (!parents || !mask) return fail(TA_EINVAL, "%s: parents and mask must not be NULL", fn);
+  if ((uintptr_t)mask & 3u) return fail(TA_EINVAL, "%s: mask must be 4-byte aligned", fn);
+  if (parents[0] != -1)
+    return fail(TA_EINVAL, "%s: invalid topology: parents[0] must be -1, got %d", fn,
+                parents[0]);
+  for (uint32_t i = 1; i < q_l; ++i)
+    if (parents[i] < 0 || (uint32_t)parents[i] >= i)
+      return fail(TA_EINVAL, "%s: invalid topology: parents[%u] = %d (need 0 <= p < %u)", fn,
+                  i, parents[i], i);
+  uint64_t req;
+  if (!mul3(q_l, mask_stride, 4, req)) return fail(TA_EOVERFLOW, "%s: size overflows", fn);
+  if (mask_bytes < req)
+    return fail(TA_ESIZE, "%s: mask buffer too small: have %zu bytes, need >= %llu", fn,
+                mask_bytes, (unsigned long long)req);
+  ta::MaskArgs a;
+  memset(a.parents, 0, sizeof a.parents);
+  for (uint32_t i = 0; i < q_l; ++i) a.parents[i] = (int16_t)parents[i];
+  a.mask = mask;
+  a.q_l = q_l;
+  a.kv_seq_len = kv_seq_len;
+  a.mask_stride = mask_stride;
+  return hip_status(ta::launch_tree_mask(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// common.h -- types, parameter blocks and launcher declarations shared by the
+// HIP kernels of libtreeattn.so.  Internal: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ta {
+
+// Mask sentinel of the explicit tree mask: cells at or below it exclude the
+// key ("ops/tree_attention.rs", mask constants).
+constexpr float kMasked = -65504.0f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+typedef _Float16 half_t;
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// fp-path forward (f32 or f16 K/V).  Row r of a kv head is (node i, head in
+// group hh) with r = i * group + hh; the output row is i * n_heads + h.
+// ---------------------------------------------------------------------------
+struct FwdArgs {
+  const float *q;      // [n_heads, q_l, D] f32
+  const void *k;       // [n_kv_heads, kv_capacity, D]
+  const void *v;
+  const float *mask;   // [q_l, mask_stride] f32, or nullptr (implicit causal)
+  float *part_o;       // [nwg][nrows][D]     (nwg > 1)
+  float *part_sm;      // [nwg][nrows][2]     (nwg > 1)
+  float *out;          // [q_l, n_heads, D]   (nwg == 1)
+  uint32_t n_heads, n_kv_heads, group, kv_seq_len, kv_capacity, q_l;
+  uint32_t mask_stride;
+  uint32_t nwg;        // KV splits
+  uint32_t rows;       // rows per kv head = q_l * group
+  uint32_t row_tiles;  // ceil(rows / rows per workgroup)
+  uint32_t n_tiles;    // ceil(kv_seq_len / BN)
+  uint32_t units;      // n_kv_heads * nwg
+  float qscale;        // scale * log2(e): logits are kept in base-2 units
+};
+
+// ---------------------------------------------------------------------------
+// Quantized forward.
+// ---------------------------------------------------------------------------
+struct QuantArgs {
+  const half_t *q;            // [BnQ, q_l, dim]
+  const uint32_t *kp, *vp;    // [BnKV, cap, dim/pf]
+  const half_t *ks, *kb, *vs, *vb;  // [BnKV, cap, dim/G]
+  const float *sinks;         // [nQ] or nullptr
+  const half_t *mask;         // f16 additive or nullptr
+  float *part_o, *part_sm;
+  half_t *out;                // [BnQ, q_l, dim]
+  uint64_t mask_head_stride;
+  uint32_t mask_stride;
+  uint32_t batch, nq, nkv, repeat, kv_seq_len, kv_capacity, q_l;
+  uint32_t nwg, rows, row_tiles, n_tiles, units;
+  float qscale;               // scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// Reduce and mask construction.
+// ---------------------------------------------------------------------------
+struct ReduceArgs {
+  const float *part_o, *part_sm;
+  void *out;
+  uint32_t nrows, dim, nwg;
+  int out_f16;
+};
+
+constexpr int kMaxTreeNodes = 1024;
+struct MaskArgs {
+  int16_t parents[kMaxTreeNodes];
+  float *mask;
+  uint32_t q_l, kv_seq_len, mask_stride;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_forward_f32(const FwdArgs &a, uint32_t head_dim,
+                              hipStream_t s);
+hipError_t launch_forward_f16(const FwdArgs &a, uint32_t head_dim,
+                              hipStream_t s);
+hipError_t launch_quant_forward(const QuantArgs &a, uint32_t dim,
+                                uint32_t bits, uint32_t group, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
+hipError_t launch_tree_mask(const MaskArgs &a, hipStream_t s);
+
+// Rows handled by one workgroup of each forward kernel (host-side shape
+// planning needs them).
+constexpr uint32_t kF32RowsPerWG = 16;
+constexpr uint32_t kF16RowsPerWG = 64;
+constexpr uint32_t kQuantRowsPerWG = 16;
+uint32_t f16_tile_keys(uint32_t head_dim);
+uint32_t f32_tile_keys(uint32_t head_dim);
+uint32_t quant_tile_keys(uint32_t dim);
+
+// XCD-aware workgroup numbering.  MI355X hands consecutive workgroup ids to
+// its 8 XCDs in turn; every row tile of one (kv head, split) unit is placed
+// on the same XCD, in consecutive slots, so their shared K/V tiles meet in
+// that XCD's L2.
+constexpr uint32_t kXcds = 8;
+__host__ __device__ inline uint32_t grid_size(uint32_t units,
+                                              uint32_t row_tiles) {
+  return kXcds * ((units + kXcds - 1) / kXcds) * row_tiles;
+}
+__device__ inline void decode_block(uint32_t bid, uint32_t row_tiles,
+                                    uint32_t &unit, uint32_t &rt) {
+  uint32_t xcd = bid % kXcds;
+  uint32_t slot = bid / kXcds;
+  unit = (slot / row_tiles) * kXcds + xcd;
+  rt = slot % row_tiles;
+}
+
+// Balanced contiguous split of n_tiles tiles into nwg ranges.
+__device__ inline void split_range(uint32_t n_tiles, uint32_t nwg, uint32_t s,
+                                   uint32_t &t0, uint32_t &t1) {
+  t0 = (uint32_t)(((uint64_t)n_tiles * s) / nwg);
+  t1 = (uint32_t)(((uint64_t)n_tiles * (s + 1)) / nwg);
+}
+
+}  // namespace ta

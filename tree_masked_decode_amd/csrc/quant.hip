@@ -1,0 +1,436 @@
+// quant.hip -- attention over an affine-quantized (4/8-bit) K/V cache.
+//
+// "ffai/flash_quantized_sdpa.rs" (metaltile-std 0.1.0): element d of a token
+// is scale_g * code + bias_g with the code taken little-end first from a
+// 32-bit word, a query head maps to kv stream q_idx / repeat, an optional
+// sink is a virtual key with raw logit sinks[h] and value 0, and an optional
+// additive f16 mask biases the logits.  That page runs one 32-lane group per
+// query over all tokens; here one wavefront takes up to 16 query rows that
+// share a kv stream (heads of the GQA group x tree nodes) over one KV split,
+// and the contractions run on v_mfma_f32_16x16x32_f16 with the codes as exact
+// fp16 integers.  The affine map is factored out of the contractions:
+//
+//   q.k_t = sum_g s_tg * (sum_{d in g} q_d c_td) + b_tg * (sum_{d in g} q_d)
+//   o_d   = sum_t (p_t s^v_tg) c^v_td + sum_t p_t b^v_tg,      g = group of d
+//
+// so K codes feed the score MFMA directly (one accumulator per group), and
+// the PV MFMA takes codes as A and p*scale_g as B (one B operand per group);
+// the bias terms are short per-row dot products on the VALU.
+//
+// Codes become fp16 by OR-ing them into the mantissa of 1024.0 (0x6400) and
+// subtracting 1024 (exact).  K codes are read straight into MFMA operands
+// (a 32-bit word holds 8 or 4 consecutive dims of one token, and the order of
+// the dims inside an MFMA step is free as long as Q uses the same order).
+// V must be transposed (the PV operand wants 8 tokens of one dim per lane),
+// so each wavefront bounces its V words through LDS as [word][token].
+#include "common.h"
+
+namespace ta {
+
+namespace {
+
+constexpr int kThreads = 64;   // one wavefront per workgroup
+constexpr int BN = 32;         // keys per tile
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ inline uint32_t as_u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Two codes (already in bits 0..bits-1 of x0 / x1's lane slots) -> (c0, c1)
+// as exact fp16: OR into 1024.0's mantissa, then subtract 1024.
+__device__ inline uint32_t codes_to_h2(uint32_t packed_pair) {
+  half2_t h = as_h2(packed_pair | 0x64006400u);
+  const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
+  return as_u(h - k1024);
+}
+
+// 8 slots of one MFMA step from the lane's words.  4-bit: one word, slots
+// [c0 c4 c1 c5 c2 c6 c3 c7].  8-bit: two words, slots [c0 c2 c1 c3] each.
+template <int BITS>
+__device__ inline half8_t word_codes(const uint32_t *w) {
+  u32x4 r;
+  if (BITS == 4) {
+    r[0] = codes_to_h2(w[0] & 0x000F000Fu);
+    r[1] = codes_to_h2((w[0] >> 4) & 0x000F000Fu);
+    r[2] = codes_to_h2((w[0] >> 8) & 0x000F000Fu);
+    r[3] = codes_to_h2((w[0] >> 12) & 0x000F000Fu);
+  } else {
+    r[0] = codes_to_h2(w[0] & 0x00FF00FFu);
+    r[1] = codes_to_h2((w[0] >> 8) & 0x00FF00FFu);
+    r[2] = codes_to_h2(w[1] & 0x00FF00FFu);
+    r[3] = codes_to_h2((w[1] >> 8) & 0x00FF00FFu);
+  }
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// Dim index of slot j of a step whose first word is w0 (see word_codes).
+template <int BITS>
+__device__ inline uint32_t slot_dim(uint32_t w0, int j) {
+  if (BITS == 4) {
+    const int pi4[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    return 8u * w0 + pi4[j];
+  }
+  const int pi8[4] = {0, 2, 1, 3};
+  return 4u * (w0 + (uint32_t)(j >> 2)) + pi8[j & 3];
+}
+
+template <int DIM, int BITS, int G>
+struct QShape {
+  static constexpr int WPK = DIM * BITS / 32;  // 32-bit words per token row
+  static constexpr int NG = DIM / G;           // scale groups per token
+  static constexpr int WPS = BITS / 4;         // words per MFMA step per lane
+  static constexpr int SPG = G / 32;           // MFMA steps per group
+  static constexpr int RUN = SPG * WPS;        // lane's contiguous words per group
+  static constexpr int GW = G * BITS / 32;     // words per group
+  static constexpr int STEPS = DIM / 32;       // score MFMA steps
+  static constexpr int DB = DIM / 16;          // PV output blocks
+  static constexpr int VCH = BN * WPK / 4 / kThreads;  // V 16-byte chunks/lane
+  static constexpr int RS = BN + 4;            // LDS row stride (words)
+  static constexpr int SBW = 4 * NG / 2;       // u32 words of 4 keys' scales
+  static_assert(VCH >= 1, "tile too small");
+  static_assert(RUN * 4 == GW, "lane runs must tile a group");
+};
+
+// Word index of (group g, step-in-group sub, part) for lane group gp.
+template <int DIM, int BITS, int G>
+__device__ inline uint32_t step_word(int g, int sub, uint32_t gp) {
+  using S = QShape<DIM, BITS, G>;
+  return (uint32_t)(g * S::GW) + gp * S::RUN + (uint32_t)(sub * S::WPS);
+}
+
+template <int DIM, int BITS, int G, bool IMPLICIT>
+__global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
+  using S = QShape<DIM, BITS, G>;
+  constexpr int NG = S::NG, STEPS = S::STEPS, DB = S::DB;
+  __shared__ __attribute__((aligned(16))) uint32_t vlds[S::WPK * S::RS];
+
+  uint32_t unit, rt;
+  decode_block(blockIdx.x, a.row_tiles, unit, rt);
+  if (unit >= a.units) return;
+  const uint32_t kv = unit / a.nwg;          // kv stream: b * nkv + hk
+  const uint32_t split = unit % a.nwg;
+  const uint32_t lane = threadIdx.x;
+  const uint32_t n = lane & 15u, gp = lane >> 4;
+
+  const uint32_t gr = rt * 16u + n;          // row: node * repeat + head-in-group
+  const bool valid = gr < a.rows;
+  const uint32_t node = valid ? gr / a.repeat : 0u;
+  const uint32_t qidx = kv * a.repeat + (valid ? gr % a.repeat : 0u);
+
+  // ---- Q' = q * scale * log2(e) in fp16, in the K operand's slot order ----
+  half8_t qf[STEPS];
+  float qsum[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) qsum[g] = 0.0f;
+  {
+    const half_t *qrow = a.q + ((size_t)qidx * a.q_l + node) * DIM;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int sub = 0; sub < S::SPG; ++sub) {
+        const uint32_t w0 = step_word<DIM, BITS, G>(g, sub, gp);
+        half8_t f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float x = valid ? (float)qrow[slot_dim<BITS>(w0, j)] * a.qscale : 0.0f;
+          f[j] = (half_t)x;
+          qsum[g] += (float)f[j];
+        }
+        qf[g * S::SPG + sub] = f;
+      }
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    qsum[g] += __shfl_xor(qsum[g], 16);
+    qsum[g] += __shfl_xor(qsum[g], 32);
+  }
+
+  const size_t kvrow0 = (size_t)kv * a.kv_capacity;
+  const uint32_t *KP = a.kp + kvrow0 * S::WPK;
+  const uint32_t *VP = a.vp + kvrow0 * S::WPK;
+  const half_t *KS = a.ks + kvrow0 * NG, *KB = a.kb + kvrow0 * NG;
+  const half_t *VS = a.vs + kvrow0 * NG, *VB = a.vb + kvrow0 * NG;
+  const half_t *mrow = IMPLICIT ? nullptr
+                                : a.mask + (size_t)qidx * a.mask_head_stride +
+                                      (size_t)node * a.mask_stride;
+  const int64_t causal_last = (int64_t)a.kv_seq_len - (int64_t)a.q_l + (int64_t)node;
+  const uint32_t L = a.kv_seq_len;
+
+  // ---- per-tile registers ----
+  struct Tile {
+    uint32_t kw[2][NG][S::RUN];   // K words: key 16kb+n, group g
+    uint32_t ksb[2][2][S::SBW];   // K scales/biases: keys 16kb+4gp..+3, all groups
+    uint32_t vsb[2][2][S::SBW];   // V scales/biases: keys F(gp, 4h..4h+3)
+    u32x4 vw[S::VCH];             // V words for the LDS transpose
+    float m[2][4];                // mask cells (row n, keys 16kb+4gp+j)
+  };
+  auto load_tile = [&](uint32_t t, Tile &T) {
+    const uint32_t key0 = t * BN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t key = key0 + 16u * kb + n;
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int r = 0; r < S::RUN; ++r)
+          T.kw[kb][g][r] = key < L ? KP[(size_t)key * S::WPK + g * S::GW + gp * S::RUN + r] : 0u;
+      // scales/biases of keys 16kb + 4gp + 0..3 (K side) and
+      // 16h + 4gp + 0..3 (V side, the keys of B-operand half h)
+      const uint32_t k4 = key0 + 16u * kb + 4u * gp;
+#pragma unroll
+      for (int w = 0; w < S::SBW; ++w) {
+        const uint32_t key_w = k4 + (uint32_t)(2 * w) / NG;  // 2 halfs per word
+        const bool in = key_w < L;
+        const uint32_t *ks32 = reinterpret_cast<const uint32_t *>(KS + (size_t)k4 * NG);
+        const uint32_t *kb32 = reinterpret_cast<const uint32_t *>(KB + (size_t)k4 * NG);
+        const uint32_t *vs32 = reinterpret_cast<const uint32_t *>(VS + (size_t)k4 * NG);
+        const uint32_t *vb32 = reinterpret_cast<const uint32_t *>(VB + (size_t)k4 * NG);
+        T.ksb[kb][0][w] = in ? ks32[w] : 0u;
+        T.ksb[kb][1][w] = in ? kb32[w] : 0u;
+        T.vsb[kb][0][w] = in ? vs32[w] : 0u;
+        T.vsb[kb][1][w] = in ? vb32[w] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kk = k4 + j;
+        float mv;
+        if (IMPLICIT)
+          mv = (valid && kk < L && (int64_t)kk <= causal_last) ? 0.0f : kMasked;
+        else
+          mv = (valid && kk < L) ? (float)mrow[kk] : kMasked;
+        T.m[kb][j] = mv;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < S::VCH; ++u) {
+      const uint32_t c = lane + kThreads * u;
+      const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
+      T.vw[u] = (key0 + key < L)
+                    ? *reinterpret_cast<const u32x4 *>(VP + (size_t)(key0 + key) * S::WPK + 4 * q4)
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // V words -> LDS [word][position]; position of key (16h + 4g4 + j) is
+  // 8*g4 + 4h + j, so that lane group gp later reads its 8 keys contiguously.
+  auto store_v = [&](const Tile &T) {
+#pragma unroll
+    for (int u = 0; u < S::VCH; ++u) {
+      const uint32_t c = lane + kThreads * u;
+      const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
+      const uint32_t pos = 8u * ((key & 15u) >> 2) + 4u * (key >> 4) + (key & 3u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vlds[(4 * q4 + e) * S::RS + pos] = T.vw[u][e];
+    }
+  };
+
+  // ---- online-softmax state of the lane's row ----
+  float Mrow = -INFINITY, Srow = 0.0f;
+  float pb[NG];                     // sum_t p_t * vbias_tg (lane's keys)
+#pragma unroll
+  for (int g = 0; g < NG; ++g) pb[g] = 0.0f;
+  floatx4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (a.sinks != nullptr && split == 0 && valid) {
+    // the sink: a virtual key with raw logit sinks[h] and value zero
+    Mrow = a.sinks[qidx % a.nq] * kLog2e;
+    Srow = (gp == 0) ? 1.0f : 0.0f;
+  }
+
+  const uint32_t vshift = (BITS == 4) ? 4u * (n & 7u) : 8u * (n & 3u);
+  const uint32_t vmask = (1u << BITS) - 1u;
+
+  auto compute = [&](const Tile &T) {
+    // scores, one accumulator per scale group
+    floatx4 sacc[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[g][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sub = 0; sub < S::SPG; ++sub) {
+          half8_t kf = word_codes<BITS>(&T.kw[kb][g][sub * S::WPS]);
+          sacc[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[g * S::SPG + sub],
+                                                               sacc[g][kb], 0, 0, 0);
+        }
+      }
+    float s[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const half_t *ksc = reinterpret_cast<const half_t *>(T.ksb[kb][0]);
+      const half_t *kbi = reinterpret_cast<const half_t *>(T.ksb[kb][1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          x = fmaf((float)ksc[j * NG + g], sacc[g][kb][j], x);
+          x = fmaf((float)kbi[j * NG + g], qsum[g], x);
+        }
+        const float mv = T.m[kb][j];
+        x = (mv > kMasked) ? fmaf(mv, kLog2e, x) : -INFINITY;
+        s[kb][j] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(Mrow, tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(Mrow - m_use);
+    float p[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(s[0][j] - m_use);
+      p[4 + j] = __builtin_amdgcn_exp2f(s[1][j] - m_use);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) psum += p[j];
+    Srow = Srow * alpha + psum;
+    Mrow = m_new;
+    // B operands p * vscale_g, and the bias sums
+    half8_t pf[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const half_t *vsc = reinterpret_cast<const half_t *>(T.vsb[j >> 2][0]);
+        const half_t *vbi = reinterpret_cast<const half_t *>(T.vsb[j >> 2][1]);
+        pf[g][j] = (half_t)(p[j] * (float)vsc[(j & 3) * NG + g]);
+        acc = fmaf(p[j], (float)vbi[(j & 3) * NG + g], acc);
+      }
+      pb[g] = pb[g] * alpha + acc;
+    }
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    // PV: A = V codes of dim 16db+n for the lane's 8 keys (from LDS)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint32_t w = (16u * db + n) * BITS / 32u;
+      const u32x4 lo = *reinterpret_cast<const u32x4 *>(&vlds[w * S::RS + 8u * gp]);
+      const u32x4 hi = *reinterpret_cast<const u32x4 *>(&vlds[w * S::RS + 8u * gp + 4u]);
+      uint32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = (lo[j] >> vshift) & vmask;
+        c[4 + j] = (hi[j] >> vshift) & vmask;
+      }
+      u32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = codes_to_h2(c[2 * e] | (c[2 * e + 1] << 16));
+      const int g = (16 * db) / G;
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, r), pf[g],
+                                                        oacc[db], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop, next tile's loads in flight during the current one ----
+  uint32_t t0, t1;
+  split_range(a.n_tiles, a.nwg, split, t0, t1);
+  Tile cur, nxt;
+  if (t0 < t1) {
+    load_tile(t0, cur);
+    store_v(cur);
+  }
+  for (uint32_t t = t0; t < t1; ++t) {
+    const bool has_next = t + 1 < t1;
+    if (has_next) load_tile(t + 1, nxt);
+    int live = 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) live |= (cur.m[kb][j] > kMasked);
+    if (__any(live)) compute(cur);
+    if (has_next) {
+      __builtin_amdgcn_wave_barrier();
+      store_v(nxt);
+      __builtin_amdgcn_wave_barrier();
+      cur = nxt;
+    }
+  }
+
+  // ---- results ----
+  float stot = Srow + __shfl_xor(Srow, 16);
+  stot += __shfl_xor(stot, 32);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    pb[g] += __shfl_xor(pb[g], 16);
+    pb[g] += __shfl_xor(pb[g], 32);
+  }
+  if (!valid) return;
+  const size_t rid = (size_t)qidx * a.q_l + node;
+  // lane holds O[d = 16db + 4gp + j] of its row
+  if (a.nwg == 1) {
+    const float inv = (stot > 0.0f) ? 1.0f / stot : 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int g = (16 * db) / G;
+      floatx4 o = (oacc[db] + pb[g]) * inv;
+      half4_t h = {(half_t)o[0], (half_t)o[1], (half_t)o[2], (half_t)o[3]};
+      *reinterpret_cast<half4_t *>(a.out + rid * DIM + 16 * db + 4 * gp) = h;
+    }
+  } else {
+    const size_t nrows = (size_t)a.batch * a.nq * a.q_l;
+    const size_t prow = (size_t)split * nrows + rid;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int g = (16 * db) / G;
+      *reinterpret_cast<floatx4 *>(a.part_o + prow * DIM + 16 * db + 4 * gp) = oacc[db] + pb[g];
+    }
+    if (gp == 0) {
+      a.part_sm[prow * 2 + 0] = stot;
+      a.part_sm[prow * 2 + 1] = Mrow;
+    }
+  }
+}
+
+template <int DIM, int BITS, int G>
+hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
+  dim3 grid(grid_size(a.units, a.row_tiles));
+  if (a.mask == nullptr)
+    hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, false>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DIM, int BITS>
+hipError_t launch_qg(const QuantArgs &a, uint32_t G, hipStream_t s) {
+  switch (G) {
+    case 32: return launch_q<DIM, BITS, 32>(a, s);
+    case 64: return launch_q<DIM, BITS, 64>(a, s);
+    case 128:
+      if constexpr (DIM >= 128) return launch_q<DIM, BITS, 128>(a, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DIM>
+hipError_t launch_qb(const QuantArgs &a, uint32_t bits, uint32_t G, hipStream_t s) {
+  return bits == 4 ? launch_qg<DIM, 4>(a, G, s) : launch_qg<DIM, 8>(a, G, s);
+}
+
+}  // namespace
+
+uint32_t quant_tile_keys(uint32_t) { return (uint32_t)BN; }
+
+hipError_t launch_quant_forward(const QuantArgs &a, uint32_t dim, uint32_t bits,
+                                uint32_t group, hipStream_t s) {
+  switch (dim) {
+    case 64: return launch_qb<64>(a, bits, group, s);
+    case 128: return launch_qb<128>(a, bits, group, s);
+    case 256: return launch_qb<256>(a, bits, group, s);
+    case 512: return launch_qb<512>(a, bits, group, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ta
