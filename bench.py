@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of one tree-verify call (forward + log-sum-exp merge) on MI355X.
+
+Default workload: the 32K-context dynamic-tree verify (n_heads=24,
+n_kv_heads=4, head_dim=256, kv_seq_len=32768, kv_capacity=40960, q_l=64
+random-tree nodes, fp16 K/V).  A step is one full verify call over one set
+of inputs already resident in HBM; the timed steps rotate over identical
+input copies totalling >= 1 GiB so that each call reads its K/V from HBM,
+not from the 256 MB Infinity Cache (a warm, cache-resident figure is
+reported separately).
+
+Prints ONE JSON line.  value = effective HBM throughput of the whole call:
+algorithmic bytes (K/V rows below kv_seq_len, Q, the mask once, the
+output) / time per call.  roofline = the forward kernel's achieved rate,
+timed with HIP events on its own stream, against the MI355X peak of the
+unit that bounds it.  cpu_baseline = the CPU oracle timed on a sample of the
+same workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per tree-verify call + effective HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0     # dense fp16 matrix
+VALU_F32_PEAK_TFS = 157.3      # fp32 vector
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="dynamic_tree_32k")
+    p.add_argument("--nwg", type=int, default=0, help="0 = library's pick")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain copy of known size (for PMC byte scaling)")
+    return p.parse_args()
+
+
+# --------------------------------------------------------------------------
+# algorithmic sizes
+# --------------------------------------------------------------------------
+def fp_alg(c):
+    H, Hk, D = c["n_heads"], c["n_kv_heads"], c["head_dim"]
+    L, q_l = c["kv_seq_len"], c["q_l"]
+    esz = 2 if c["kv_dtype"] == "f16" else 4
+    kv = 2 * Hk * L * D * esz
+    qb = H * q_l * D * 4
+    mask = q_l * L * 4
+    out = q_l * H * D * 4
+    flops = 4 * (q_l * H) * L * D
+    return dict(bytes=kv + qb + mask + out, kv_bytes=kv, flops=flops)
+
+
+def quant_alg(c):
+    B, nQ, nKV, dim = c["batch"], c["n_q_heads"], c["n_kv_heads"], c["dim"]
+    L, q_l, bits, G = c["kv_seq_len"], c["q_l"], c["bits"], c["group_size"]
+    packed = 2 * B * nKV * L * dim * bits // 8
+    sb = 4 * B * nKV * L * (dim // G) * 2
+    qb = B * nQ * q_l * dim * 2
+    mask = 0 if c["mask"] is None else B * nQ * q_l * L * 2
+    sinks = 0 if c["sinks"] is None else nQ * 4
+    out = B * nQ * q_l * dim * 2
+    flops = 4 * (B * nQ * q_l) * L * dim
+    return dict(bytes=packed + sb + qb + mask + sinks + out, kv_bytes=packed + sb,
+                flops=flops)
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+FWD_SOURCES = {"f16": ["tree_masked_decode_amd/csrc/fwd_f16.hip",
+                       "tree_masked_decode_amd/csrc/common.h"],
+               "f32": ["tree_masked_decode_amd/csrc/fwd_f32.hip",
+                       "tree_masked_decode_amd/csrc/common.h"],
+               "quant": ["tree_masked_decode_amd/csrc/quant.hip",
+                         "tree_masked_decode_amd/csrc/common.h"]}
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per forward launch from the committed PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(FWD_SOURCES[kind]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of rows
+# --------------------------------------------------------------------------
+def cpu_baseline(name, c, alg, quant):
+    import oracle
+    import numpy as np
+    threads = max(1, min(16, os.cpu_count() or 1))
+    if quant:
+        nrows = c["q"].shape[0] * c["q"].shape[1]
+        rows = [(r // c["q_l"], r % c["q_l"]) for r in range(0, nrows, max(1, nrows // 32))]
+        mask = None if c["mask"] is None else np.ascontiguousarray(c["mask"]).ravel()
+        t = time.perf_counter()
+        oracle.quant_attention(c["q"], c["k_packed"], c["k_scales"], c["k_biases"],
+                               c["v_packed"], c["v_scales"], c["v_biases"],
+                               n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
+                               bits=c["bits"], group_size=c["group_size"],
+                               scale=c["scale"], sinks=c["sinks"], mask=mask,
+                               mask_head_stride=c["mask_head_stride"],
+                               mask_stride=c["mask_stride"], rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t
+    else:
+        H, q_l = c["n_heads"], c["q_l"]
+        nrows = H * q_l
+        step = max(1, nrows // 64)
+        rows = [(r // H, r % H) for r in range(0, nrows, step)]
+        mask = oracle.tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"])
+        t = time.perf_counter()
+        oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
+                         kv_seq_len=c["kv_seq_len"], scale=c["scale"], rows=rows,
+                         nthreads=threads)
+        dt = time.perf_counter() - t
+    us_call = dt * 1e6 * nrows / len(rows)
+    return {"value": round(alg["bytes"] / (us_call * 1e-6) / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "%d of %d output rows of %s (each row over all %d keys), "
+                      "%.2f s wall; scaled to the whole call"
+                      % (len(rows), nrows, name, c["kv_seq_len"], dt),
+            "us_per_call": round(us_call, 1)}
+
+
+# --------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
+              "(the sharded design is described in DESIGN.md)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_masked_decode_amd as ta
+    from tree_masked_decode_amd import _lib, inputs
+
+    lib = _lib.load()
+    torch.cuda.set_device(0)
+    quant = args.workload in inputs.QUANT_WORKLOADS
+    if quant:
+        c = inputs.quant_case(args.workload)
+        alg = quant_alg(c)
+        kind = "quant"
+    else:
+        c = inputs.fp_case(args.workload)
+        alg = fp_alg(c)
+        kind = c["kv_dtype"]
+
+    # ---- device inputs, rotated over copies totalling >= 1 GiB ----
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    ncopies = max(1, min(64, math.ceil(ROTATE_BYTES / alg["bytes"])))
+    if quant:
+        names = ("q", "k_packed", "k_scales", "k_biases", "v_packed", "v_scales", "v_biases")
+        base = {n: to_dev(c[n]) for n in names}
+        base["sinks"] = None if c["sinks"] is None else to_dev(c["sinks"])
+        base["mask"] = None if c["mask"] is None else to_dev(np.ascontiguousarray(c["mask"]).ravel())
+        B, nQ, nKV, dim = c["batch"], c["n_q_heads"], c["n_kv_heads"], c["dim"]
+        L, q_l = c["kv_seq_len"], c["q_l"]
+        nwg = args.nwg or ta.quant_pick_nwg(B, nQ, nKV, dim, L, q_l)
+        nrows, D = B * nQ * q_l, dim
+        out_dtype = torch.float16
+    else:
+        base = {"q": to_dev(c["q"]), "k": to_dev(c["k"]), "v": to_dev(c["v"])}
+        base["mask"] = ta.build_tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"])
+        H, Hk, D = c["n_heads"], c["n_kv_heads"], c["head_dim"]
+        L, q_l = c["kv_seq_len"], c["q_l"]
+        nwg = args.nwg or c.get("nwg") or ta.pick_nwg(H, Hk, D, L, q_l,
+                                                       1 if kind == "f16" else 0)
+        nrows = H * q_l
+        out_dtype = torch.float32
+    copies = [base] + [{n: (None if t is None else t.clone()) for n, t in base.items()}
+                       for _ in range(ncopies - 1)]
+    part = torch.empty(max(1, ta.partials_bytes(nrows, D, 1, nwg) // 4),
+                       dtype=torch.float32, device="cuda")
+    out = torch.empty((nrows, D), dtype=out_dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    # Pre-marshalled C calls (keeps host launch cost far below the GPU time).
+    import ctypes
+    vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    nb = lambda t: 0 if t is None else t.numel() * t.element_size()
+    P = part if nwg > 1 else None
+    O = out if nwg == 1 else None
+    calls = []
+    for cp in copies:
+        if quant:
+            kvb = (ctypes.c_size_t * 6)(*[nb(cp[n]) for n in names[1:]])
+            fargs = (vp(cp["q"]), 1, nb(cp["q"]), vp(cp["k_packed"]), vp(cp["k_scales"]),
+                     vp(cp["k_biases"]), vp(cp["v_packed"]), vp(cp["v_scales"]),
+                     vp(cp["v_biases"]), kvb, vp(cp["sinks"]), nb(cp["sinks"]),
+                     vp(cp["mask"]), nb(cp["mask"]), c["mask_head_stride"],
+                     c["mask_stride"], vp(P), nb(P), vp(O), nb(O), B, nQ, nKV, dim,
+                     L, c["kv_capacity"], q_l, c["bits"], c["group_size"], c["scale"],
+                     nwg, ctypes.c_void_p(sptr))
+            calls.append((lib.tree_attn_quant_forward, fargs))
+        else:
+            fargs = (vp(cp["q"]), nb(cp["q"]), vp(cp["k"]), vp(cp["v"]),
+                     1 if kind == "f16" else 0, nb(cp["k"]), vp(cp["mask"]), nb(cp["mask"]),
+                     vp(P), nb(P), vp(O), nb(O), H, Hk, D, L, c["kv_capacity"], q_l,
+                     c["mask_stride"], c["scale"], nwg, ctypes.c_void_p(sptr))
+            calls.append((lib.tree_attn_forward, fargs))
+    rargs = (vp(part), nb(part), vp(out), 1 if out_dtype == torch.float16 else 0,
+             nb(out), nrows, D, nwg, ctypes.c_void_p(sptr))
+
+    def step(i, ev=None):
+        fn, fa = calls[i % len(calls)]
+        if ev is not None:
+            ev[0].record(stream)
+        rc = fn(*fa)
+        if ev is not None:
+            ev[1].record(stream)
+        if rc != 0:
+            raise RuntimeError("forward failed: %s" % _lib.last_error())
+        if nwg > 1:
+            rc = lib.tree_attn_reduce(*rargs)
+            if rc != 0:
+                raise RuntimeError("reduce failed: %s" % _lib.last_error())
+
+    if args.copy_calibration:
+        # a plain device copy of known size, for scaling the PMC byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy calibration: 5 copies of %d bytes" % src.numel(), file=sys.stderr)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("warmup done: %d steps, nwg=%d, %d input copies" % (args.warmup, nwg, ncopies),
+          file=sys.stderr, flush=True)
+
+    # ---- timed region (cold: rotating copies) ----
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    fwd_ms = [a.elapsed_time(b) for a, b in evs]
+    fwd_avg_ms = statistics.fmean(fwd_ms)
+    print("timed: %d steps, %.3f ms/step" % (K, ms_step), file=sys.stderr, flush=True)
+
+    # ---- warm: one input set, back to back (cache-resident) ----
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    for _ in range(K):
+        step(0)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - tw0) * 1e3 / K
+
+    us_call = ms_step * 1e3
+    gbs = alg["bytes"] / (ms_step * 1e-3) / 1e9
+    fwd_s = fwd_avg_ms * 1e-3
+    fwd_gbs = alg["bytes"] / fwd_s / 1e9
+    fwd_tfs = alg["flops"] / fwd_s / 1e12
+    hbm_frac = fwd_gbs / HBM_PEAK_GBS
+    if kind == "f32":
+        bound, achieved, peak, unit = "alu", fwd_tfs, VALU_F32_PEAK_TFS, "TFLOP/s"
+    elif alg["flops"] / alg["bytes"] > MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        bound, achieved, peak, unit = "mfma", fwd_tfs, MFMA_F16_PEAK_TFS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", fwd_gbs, HBM_PEAK_GBS, "GB/s"
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if kind in ("f16", "quant") else "f32",
+        "data": "synthetic (seeded normal Q/K/V, random tree)",
+        "config": {"workload": args.workload, "nwg": nwg, "input_copies": ncopies,
+                   "alg_bytes": alg["bytes"], "alg_flops": alg["flops"],
+                   "parallelism": "single GPU"},
+        "us_per_call": round(us_call, 2),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "warm_us_per_call": round(warm_ms * 1e3, 2),
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(args.workload, kind),
+                     "kernel": "forward", "avg_launch_us": round(fwd_avg_ms * 1e3, 2),
+                     "hbm_frac": round(hbm_frac, 4),
+                     "mfma_frac": round(fwd_tfs / MFMA_F16_PEAK_TFS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.workload, c, alg, quant)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

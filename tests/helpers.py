@@ -30,14 +30,24 @@ def max_abs(a, b):
     return float(np.max(np.abs(a - b))) if a.size else 0.0
 
 
-def assert_close(got, ref, tol, what=""):
+def assert_close(got, ref, tol, what="", f16_out=False):
+    """max |got - ref| <= tol.  With f16_out the result was rounded to fp16 by
+    contract, so each element may also carry that rounding: half an fp16 ulp
+    of the exact value is added to its bound."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), "non-finite output " + what
-    err = max_abs(got, ref)
-    assert err <= tol, "%s max-abs error %.3e > %.1e" % (what, err, tol)
-    return err
+    diff = np.abs(got - ref)
+    bound = np.full(ref.shape, float(tol))
+    if f16_out:
+        ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        bound = bound + 0.5 * ulp
+    worst = int(np.argmax(diff - bound)) if diff.size else 0
+    ok = bool(np.all(diff <= bound))
+    assert ok, "%s error %.3e > bound %.3e at flat index %d (max-abs %.3e)" % (
+        what, diff.flat[worst], bound.flat[worst], worst, float(diff.max()))
+    return float(diff.max()) if diff.size else 0.0
 
 
 def sample_rows(q_l, n_heads, n, seed=0):

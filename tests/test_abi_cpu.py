@@ -217,6 +217,7 @@ def qf(lib, **kw):
     (dict(nwg=1, out_bytes=128 * 128 * 2 - 1), L.TA_ESIZE, "output"),
     (dict(vb=None), L.TA_EINVAL, "NULL"),
     (dict(mhs=1 << 62), L.TA_EOVERFLOW, "overflow"),
+    (dict(dim=64, G=64, cap=16385), L.TA_EUNSUPPORTED, "even"),
 ])
 def test_quant_validation(lib, kw, code, word):
     assert qf(lib, **kw) == code

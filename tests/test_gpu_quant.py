@@ -1,0 +1,141 @@
+"""GPU parity of the affine-quantized K/V path against the oracle.
+
+"ffai/flash_quantized_sdpa.rs" (metaltile-std 0.1.0): 4/8-bit codes with
+per-group f16 scales and biases, optional sinks, optional additive f16 mask.
+Output is f16: each element must be within 2e-3 of the exact result plus
+half an fp16 ulp of it (the rounding the f16 output type itself imposes).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tree_masked_decode_amd import inputs
+
+from helpers import assert_close, dev, host, note
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def ta():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import tree_masked_decode_amd as ta
+    ta._api()
+    return ta
+
+
+def qcase(seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, cap=None):
+    return inputs.quant_case(dict(batch=B, n_q_heads=nQ, n_kv_heads=nKV, dim=dim,
+                                  kv_seq_len=L, kv_capacity=cap or (L + 5 + (L + 5) % 2), q_l=q_l,
+                                  bits=bits, group_size=G, sinks=sinks, mask=mask),
+                             seed=seed)
+
+
+def gpu_run(ta, c, nwg=None):
+    import torch
+    t = {k: dev(c[k]) for k in ("q", "k_packed", "k_scales", "k_biases", "v_packed",
+                                "v_scales", "v_biases")}
+    sinks = None if c["sinks"] is None else dev(c["sinks"])
+    mask = None if c["mask"] is None else dev(np.ascontiguousarray(c["mask"]).ravel())
+    out = ta.quant_verify(t["q"], t["k_packed"], t["k_scales"], t["k_biases"],
+                          t["v_packed"], t["v_scales"], t["v_biases"],
+                          n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
+                          bits=c["bits"], group_size=c["group_size"], scale=c["scale"],
+                          nwg=nwg, sinks=sinks, mask=mask,
+                          mask_head_stride=c["mask_head_stride"],
+                          mask_stride=c["mask_stride"])
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def ref_run(c, rows=None):
+    return oracle.quant_attention(
+        c["q"], c["k_packed"], c["k_scales"], c["k_biases"], c["v_packed"],
+        c["v_scales"], c["v_biases"], n_kv_heads=c["n_kv_heads"],
+        kv_seq_len=c["kv_seq_len"], bits=c["bits"], group_size=c["group_size"],
+        scale=c["scale"], sinks=c["sinks"],
+        mask=None if c["mask"] is None else np.ascontiguousarray(c["mask"]).ravel(),
+        mask_head_stride=c["mask_head_stride"], mask_stride=c["mask_stride"], rows=rows)
+
+
+SMALL = [
+    # seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, nwg
+    (0, 1, 4, 1, 128, 100, 1, 4, 64, False, None, 1),
+    (1, 2, 8, 2, 128, 333, 1, 4, 64, True, "alibi", 3),
+    (2, 1, 4, 4, 64, 257, 1, 8, 32, True, None, 2),
+    (3, 2, 6, 2, 256, 190, 1, 4, 128, False, "alibi", None),
+    (4, 1, 8, 2, 128, 500, 1, 8, 64, True, "alibi", 4),
+    (5, 1, 2, 1, 512, 97, 1, 4, 32, True, None, 2),
+    (6, 1, 2, 2, 512, 65, 1, 8, 128, False, "alibi", 1),
+    (7, 1, 4, 2, 64, 1000, 3, 4, 64, False, None, 5),      # implicit causal, q_l = 3
+    (8, 3, 4, 1, 128, 77, 5, 4, 32, True, "alibi", 2),     # 20 rows: 2 row tiles
+    (9, 1, 2, 1, 128, 40, 1, 4, 64, False, None, 9),       # more splits than tiles
+    (10, 1, 2, 1, 64, 101, 1, 4, 64, True, "alibi", 2),   # one group per token
+    (11, 2, 4, 2, 64, 99, 2, 8, 64, False, None, 3),
+]
+
+
+@pytest.mark.parametrize("seed,B,nQ,nKV,dim,L,q_l,bits,G,sinks,mask,nwg", SMALL)
+def test_quant_parity_small(ta, seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, nwg):
+    note("quant small seed=%d dim=%d L=%d q_l=%d bits=%d G=%d sinks=%s mask=%s nwg=%s"
+         % (seed, dim, L, q_l, bits, G, sinks, mask, nwg))
+    c = qcase(seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask)
+    assert_close(gpu_run(ta, c, nwg), ref_run(c), TOL, "quant %d" % seed, f16_out=True)
+
+
+def test_quant_workload_4bit(ta):
+    note("workload quant_4bit (full)")
+    c = inputs.quant_case("quant_4bit", f16_out=True)
+    got = gpu_run(ta, c)
+    assert_close(got, ref_run(c), TOL, "quant_4bit", f16_out=True)
+
+
+def test_quant_workload_8bit_sampled(ta):
+    note("workload quant_4bit shape at 8 bits (sampled rows)")
+    c = inputs.quant_case("quant_4bit", bits=8)
+    got = gpu_run(ta, c)
+    rows = [(qi, 0) for qi in (0, 1, 31, 32, 64, 100, 127)]
+    sel = np.stack([got[qi, i] for qi, i in rows])
+    assert_close(sel, ref_run(c, rows), TOL, "quant_8bit", f16_out=True)
+
+
+def test_quant_tree_mask_broadcast(ta):
+    note("quant with a broadcast tree mask (q_l = 16, head stride 0)")
+    c = qcase(10, 1, 8, 2, 128, 600, 16, 4, 64, True, None)
+    tm = oracle.tree_mask(inputs.parents_binary(16), 600).astype(np.float16)
+    c["mask"] = tm
+    c["mask_head_stride"] = 0
+    c["mask_stride"] = 600
+    assert_close(gpu_run(ta, c, 3), ref_run(c), TOL, "tree mask", f16_out=True)
+
+
+def test_quant_masked_rows_and_poison(ta):
+    note("quant masked rows + poisoned capacity tail")
+    c = qcase(11, 1, 4, 1, 128, 300, 2, 4, 64, True, None, cap=400)
+    m = np.zeros((4, 2, 300), dtype=np.float16)
+    m[1, 1, :] = -65504.0        # row with no visible key -> sink only -> zeros
+    m[2, :, :250] = -np.inf      # -inf excludes as well
+    c["mask"] = m
+    c["mask_head_stride"] = 600
+    c["mask_stride"] = 300
+    ref = ref_run(c)
+    got = gpu_run(ta, c, 4)
+    assert np.all(got[1, 1] == 0.0)
+    assert_close(got, ref, TOL, "masked", f16_out=True)
+    # scales/biases past kv_seq_len -> NaN must not leak
+    for k in ("k_scales", "k_biases", "v_scales", "v_biases"):
+        c[k] = c[k].copy()
+        c[k][:, 300:] = np.nan
+    got2 = gpu_run(ta, c, 4)
+    assert np.array_equal(got2.view(np.uint16), got.view(np.uint16))
+
+
+def test_quant_deterministic(ta):
+    note("quant determinism")
+    c = qcase(12, 2, 8, 2, 128, 2000, 1, 4, 64, True, "alibi")
+    a = gpu_run(ta, c)
+    b = gpu_run(ta, c)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))

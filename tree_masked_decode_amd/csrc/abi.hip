@@ -76,15 +76,19 @@ uint64_t partials_bytes_u64(uint64_t nrows, uint64_t dim, uint64_t nwg,
   return overflow ? UINT64_MAX : r;
 }
 
-// Split count that gives about `target` workgroups, at least 2 tiles per
-// split and no more splits than tiles.
-uint32_t pick_splits(uint32_t units_per_split, uint32_t n_tiles,
-                     uint32_t num_cus, uint32_t waves_per_cu_target) {
+// Split count for `units_per_split` workgroups per split: as many splits as
+// fit in ONE round of resident workgroups (num_cus * per_cu), with at least
+// 8 key tiles per split and no more partial-result bytes (written once, read
+// once by the merge) than K/V bytes.
+uint32_t pick_splits(uint32_t units_per_split, uint32_t n_tiles, uint32_t num_cus,
+                     uint32_t per_cu, uint64_t kv_bytes, uint64_t partial_bytes_per_split) {
   if (num_cus == 0) num_cus = 256;
-  uint64_t target = (uint64_t)num_cus * waves_per_cu_target;
-  uint64_t nwg = (target + units_per_split - 1) / units_per_split;
-  uint64_t max_by_tiles = n_tiles >= 4 ? n_tiles / 2 : 1;
-  if (nwg > max_by_tiles) nwg = max_by_tiles;
+  const uint64_t slots = (uint64_t)num_cus * per_cu;
+  uint64_t nwg = slots / units_per_split;
+  const uint64_t by_tiles = n_tiles / 8;
+  if (nwg > by_tiles) nwg = by_tiles;
+  if (partial_bytes_per_split > 0 && nwg > kv_bytes / partial_bytes_per_split)
+    nwg = kv_bytes / partial_bytes_per_split;
   if (nwg < 1) nwg = 1;
   if (nwg > kMaxNwg) nwg = kMaxNwg;
   return (uint32_t)nwg;
@@ -112,12 +116,15 @@ uint32_t tree_attn_pick_nwg(uint32_t n_heads, uint32_t n_kv_heads,
     return 1;
   uint32_t rows = q_l * (n_heads / n_kv_heads);
   bool f16 = kv_dtype == TA_F16;
-  uint32_t rpw = f16 ? ta::kF16RowsPerWG : ta::kF32RowsPerWG;
+  uint32_t rpw = f16 ? 64u * ta::f16_row_blocks(head_dim, rows) : ta::kF32RowsPerWG;
   uint32_t bn = f16 ? ta::f16_tile_keys(head_dim) : ta::f32_tile_keys(head_dim);
   uint32_t units = n_kv_heads * ceil_div(rows, rpw);
-  // Two resident workgroups per CU for head_dim <= 256, one for 512.
-  uint32_t per_cu = (head_dim >= 512) ? 1u : 2u;
-  return pick_splits(units, ceil_div(kv_seq_len, bn), num_cus, per_cu);
+  // One resident fp16 workgroup per CU (its registers fill the SIMDs); the
+  // fp32 kernel fits two.
+  uint32_t per_cu = f16 ? 1u : 2u;
+  const uint64_t kv = 2ull * n_kv_heads * kv_seq_len * head_dim * (f16 ? 2u : 4u);
+  const uint64_t part = (uint64_t)n_heads * q_l * (head_dim + 2) * 4;
+  return pick_splits(units, ceil_div(kv_seq_len, bn), num_cus, per_cu, kv, part);
 }
 
 uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
@@ -129,8 +136,11 @@ uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
     return 1;
   uint32_t rows = q_l * (n_q_heads / n_kv_heads);
   uint32_t units = batch * n_kv_heads * ceil_div(rows, ta::kQuantRowsPerWG);
-  return pick_splits(units, ceil_div(kv_seq_len, ta::quant_tile_keys(dim)),
-                     num_cus, 4u);
+  // one-wavefront workgroups, several resident per CU
+  const uint64_t kv = 2ull * batch * n_kv_heads * kv_seq_len * dim / 2;
+  const uint64_t part = (uint64_t)batch * n_q_heads * q_l * (dim + 2) * 4;
+  return pick_splits(units, ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, 8u,
+                     kv, part);
 }
 
 int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
@@ -228,7 +238,7 @@ int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
   a.rows = (uint32_t)rows;
   a.qscale = scale * ta::kLog2e;
   const bool f16 = kv_dtype == TA_F16;
-  const uint32_t rpw = f16 ? ta::kF16RowsPerWG : ta::kF32RowsPerWG;
+  const uint32_t rpw = f16 ? 64u * ta::f16_row_blocks(head_dim, a.rows) : ta::kF32RowsPerWG;
   const uint32_t bn = f16 ? ta::f16_tile_keys(head_dim) : ta::f32_tile_keys(head_dim);
   a.row_tiles = ceil_div(a.rows, rpw);
   a.n_tiles = ceil_div(kv_seq_len, bn);
@@ -327,6 +337,9 @@ int tree_attn_quant_forward(
     return fail(TA_EINVAL, "%s: nwg must be in [1, %u], got %u", fn, kMaxNwg, nwg);
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(TA_EINVAL, "%s: scale must be finite", fn);
+  // Scales/biases are read four tokens at a time as 32-bit words.
+  if (group_size == dim && (kv_capacity & 1u))
+    return fail(TA_EUNSUPPORTED, "%s: kv_capacity must be even when group_size == dim", fn);
   if (!kv_bytes) return fail(TA_EINVAL, "%s: kv_bytes must not be NULL", fn);
   if (!q || !k_packed || !k_scales || !k_biases || !v_packed || !v_scales || !v_biases)
     return fail(TA_EINVAL, "%s: q and the six K/V buffers must not be NULL", fn);

@@ -91,9 +91,11 @@ hipError_t launch_tree_mask(const MaskArgs &a, hipStream_t s);
 // Rows handled by one workgroup of each forward kernel (host-side shape
 // planning needs them).
 constexpr uint32_t kF32RowsPerWG = 16;
-constexpr uint32_t kF16RowsPerWG = 64;
 constexpr uint32_t kQuantRowsPerWG = 16;
 uint32_t f16_tile_keys(uint32_t head_dim);
+// Row blocks of 16 per wavefront the fp16 kernel uses for this shape; a
+// workgroup then covers 64 * row_blocks rows.
+uint32_t f16_row_blocks(uint32_t head_dim, uint32_t rows);
 uint32_t f32_tile_keys(uint32_t head_dim);
 uint32_t quant_tile_keys(uint32_t dim);
 

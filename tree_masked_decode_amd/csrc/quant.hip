@@ -13,9 +13,12 @@
 //   q.k_t = sum_g s_tg * (sum_{d in g} q_d c_td) + b_tg * (sum_{d in g} q_d)
 //   o_d   = sum_t (p_t s^v_tg) c^v_td + sum_t p_t b^v_tg,      g = group of d
 //
-// so K codes feed the score MFMA directly (one accumulator per group), and
-// the PV MFMA takes codes as A and p*scale_g as B (one B operand per group);
-// the bias terms are short per-row dot products on the VALU.
+// so K codes feed the score MFMA directly (one accumulator per group; Q is
+// used exactly as given in fp16 and the attention scale is applied to the
+// fp32 dot products), and the PV MFMA takes codes as A and p*scale_g as B
+// (one B operand per group, split into an fp16 hi/lo pair so the product
+// keeps fp32-like precision); the bias terms are short per-row dot products
+// on the VALU.
 //
 // Codes become fp16 by OR-ing them into the mantissa of 1024.0 (0x6400) and
 // subtracting 1024 (exact).  K codes are read straight into MFMA operands
@@ -118,7 +121,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   const uint32_t node = valid ? gr / a.repeat : 0u;
   const uint32_t qidx = kv * a.repeat + (valid ? gr % a.repeat : 0u);
 
-  // ---- Q' = q * scale * log2(e) in fp16, in the K operand's slot order ----
+  // ---- Q as given (fp16, exact), in the K operand's slot order; the
+  // attention scale is applied to the fp32 dot products afterwards ----
   half8_t qf[STEPS];
   float qsum[NG];
 #pragma unroll
@@ -133,8 +137,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
         half8_t f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float x = valid ? (float)qrow[slot_dim<BITS>(w0, j)] * a.qscale : 0.0f;
-          f[j] = (half_t)x;
+          f[j] = valid ? qrow[slot_dim<BITS>(w0, j)] : (half_t)0.0f;
           qsum[g] += (float)f[j];
         }
         qf[g * S::SPG + sub] = f;
@@ -180,16 +183,21 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       const uint32_t k4 = key0 + 16u * kb + 4u * gp;
 #pragma unroll
       for (int w = 0; w < S::SBW; ++w) {
-        const uint32_t key_w = k4 + (uint32_t)(2 * w) / NG;  // 2 halfs per word
-        const bool in = key_w < L;
+        // word w holds halfs 2w and 2w+1 of the run; with one group per
+        // token these belong to two different tokens, each checked alone so
+        // that nothing past kv_seq_len is read or used.
+        const uint32_t key_lo = k4 + (uint32_t)(2 * w) / NG;
+        const uint32_t key_hi = k4 + (uint32_t)(2 * w + 1) / NG;
+        const bool in = key_lo < L;
+        const uint32_t keep = key_hi < L ? 0xffffffffu : 0x0000ffffu;
         const uint32_t *ks32 = reinterpret_cast<const uint32_t *>(KS + (size_t)k4 * NG);
         const uint32_t *kb32 = reinterpret_cast<const uint32_t *>(KB + (size_t)k4 * NG);
         const uint32_t *vs32 = reinterpret_cast<const uint32_t *>(VS + (size_t)k4 * NG);
         const uint32_t *vb32 = reinterpret_cast<const uint32_t *>(VB + (size_t)k4 * NG);
-        T.ksb[kb][0][w] = in ? ks32[w] : 0u;
-        T.ksb[kb][1][w] = in ? kb32[w] : 0u;
-        T.vsb[kb][0][w] = in ? vs32[w] : 0u;
-        T.vsb[kb][1][w] = in ? vb32[w] : 0u;
+        T.ksb[kb][0][w] = in ? (ks32[w] & keep) : 0u;
+        T.ksb[kb][1][w] = in ? (kb32[w] & keep) : 0u;
+        T.vsb[kb][0][w] = in ? (vs32[w] & keep) : 0u;
+        T.vsb[kb][1][w] = in ? (vb32[w] & keep) : 0u;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
           x = fmaf((float)kbi[j * NG + g], qsum[g], x);
         }
         const float mv = T.m[kb][j];
-        x = (mv > kMasked) ? fmaf(mv, kLog2e, x) : -INFINITY;
+        x = (mv > kMasked) ? fmaf(x, a.qscale, mv * kLog2e) : -INFINITY;
         s[kb][j] = x;
         tmax = fmaxf(tmax, x);
       }
@@ -292,8 +300,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     for (int j = 0; j < 8; ++j) psum += p[j];
     Srow = Srow * alpha + psum;
     Mrow = m_new;
-    // B operands p * vscale_g, and the bias sums
-    half8_t pf[NG];
+    // B operands p * vscale_g as an fp16 pair hi + lo (the pair carries
+    // about 22 bits of the fp32 product, so the fp16 operand width does not
+    // limit the result), and the bias sums
+    half8_t pf[NG], pl[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       float acc = 0.0f;
@@ -301,7 +311,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       for (int j = 0; j < 8; ++j) {
         const half_t *vsc = reinterpret_cast<const half_t *>(T.vsb[j >> 2][0]);
         const half_t *vbi = reinterpret_cast<const half_t *>(T.vsb[j >> 2][1]);
-        pf[g][j] = (half_t)(p[j] * (float)vsc[(j & 3) * NG + g]);
+        const float w = p[j] * (float)vsc[(j & 3) * NG + g];
+        const half_t hi = (half_t)w;
+        pf[g][j] = hi;
+        pl[g][j] = (half_t)(w - (float)hi);
         acc = fmaf(p[j], (float)vbi[(j & 3) * NG + g], acc);
       }
       pb[g] = pb[g] * alpha + acc;
@@ -326,8 +339,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = codes_to_h2(c[2 * e] | (c[2 * e + 1] << 16));
       const int g = (16 * db) / G;
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, r), pf[g],
-                                                        oacc[db], 0, 0, 0);
+      const half8_t vf = __builtin_bit_cast(half8_t, r);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[g], oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[g], oacc[db], 0, 0, 0);
     }
   };
 
