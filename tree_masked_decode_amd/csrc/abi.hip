@@ -76,15 +76,19 @@ uint64_t partials_bytes_u64(uint64_t nrows, uint64_t dim, uint64_t nwg,
   return overflow ? UINT64_MAX : r;
 }
 
-// Split count for `units_per_split` workgroups per split: as many splits as
-// fit in ONE round of resident workgroups (num_cus * per_cu), with at least
-// 8 key tiles per split and no more partial-result bytes (written once, read
-// once by the merge) than K/V bytes.
-uint32_t pick_splits(uint32_t units_per_split, uint32_t n_tiles, uint32_t num_cus,
+// Split count for `heads` independent (kv head) streams of `row_tiles`
+// workgroups each.  Workgroup ids go to the 8 XCDs in turn and every row tile
+// of one (head, split) unit sits on one XCD, so an XCD holds
+// ceil(heads * nwg / 8) * row_tiles workgroups: as many splits as keep that
+// within ONE round of the XCD's resident slots (CUs per XCD * per_cu), with at
+// least 8 key tiles per split and no more partial-result bytes (written once,
+// read once by the merge) than K/V bytes.
+uint32_t pick_splits(uint32_t heads, uint32_t row_tiles, uint32_t n_tiles, uint32_t num_cus,
                      uint32_t per_cu, uint64_t kv_bytes, uint64_t partial_bytes_per_split) {
   if (num_cus == 0) num_cus = 256;
-  const uint64_t slots = (uint64_t)num_cus * per_cu;
-  uint64_t nwg = slots / units_per_split;
+  const uint64_t slots_per_xcd = (uint64_t)(num_cus / ta::kXcds) * per_cu;
+  const uint64_t units_per_xcd = row_tiles ? slots_per_xcd / row_tiles : 0;
+  uint64_t nwg = units_per_xcd * ta::kXcds / heads;
   const uint64_t by_tiles = n_tiles / 8;
   if (nwg > by_tiles) nwg = by_tiles;
   if (partial_bytes_per_split > 0 && nwg > kv_bytes / partial_bytes_per_split)
@@ -116,15 +120,15 @@ uint32_t tree_attn_pick_nwg(uint32_t n_heads, uint32_t n_kv_heads,
     return 1;
   uint32_t rows = q_l * (n_heads / n_kv_heads);
   bool f16 = kv_dtype == TA_F16;
-  uint32_t rpw = f16 ? 64u * ta::f16_row_blocks(head_dim, rows) : ta::kF32RowsPerWG;
+  uint32_t rpw = f16 ? ta::f16_rows_per_wg(head_dim, rows) : ta::kF32RowsPerWG;
   uint32_t bn = f16 ? ta::f16_tile_keys(head_dim) : ta::f32_tile_keys(head_dim);
-  uint32_t units = n_kv_heads * ceil_div(rows, rpw);
   // One resident fp16 workgroup per CU (its registers fill the SIMDs); the
   // fp32 kernel fits two.
   uint32_t per_cu = f16 ? 1u : 2u;
   const uint64_t kv = 2ull * n_kv_heads * kv_seq_len * head_dim * (f16 ? 2u : 4u);
   const uint64_t part = (uint64_t)n_heads * q_l * (head_dim + 2) * 4;
-  return pick_splits(units, ceil_div(kv_seq_len, bn), num_cus, per_cu, kv, part);
+  return pick_splits(n_kv_heads, ceil_div(rows, rpw), ceil_div(kv_seq_len, bn), num_cus,
+                     per_cu, kv, part);
 }
 
 uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
@@ -135,12 +139,11 @@ uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
       q_l == 0 || n_q_heads % n_kv_heads != 0)
     return 1;
   uint32_t rows = q_l * (n_q_heads / n_kv_heads);
-  uint32_t units = batch * n_kv_heads * ceil_div(rows, ta::kQuantRowsPerWG);
   // one-wavefront workgroups, several resident per CU
   const uint64_t kv = 2ull * batch * n_kv_heads * kv_seq_len * dim / 2;
   const uint64_t part = (uint64_t)batch * n_q_heads * q_l * (dim + 2) * 4;
-  return pick_splits(units, ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, 8u,
-                     kv, part);
+  return pick_splits(batch * n_kv_heads, ceil_div(rows, ta::kQuantRowsPerWG),
+                     ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, 8u, kv, part);
 }
 
 int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
@@ -237,8 +240,9 @@ int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
   a.nwg = nwg;
   a.rows = (uint32_t)rows;
   a.qscale = scale * ta::kLog2e;
+  a.scale = scale;
   const bool f16 = kv_dtype == TA_F16;
-  const uint32_t rpw = f16 ? 64u * ta::f16_row_blocks(head_dim, a.rows) : ta::kF32RowsPerWG;
+  const uint32_t rpw = f16 ? ta::f16_rows_per_wg(head_dim, a.rows) : ta::kF32RowsPerWG;
   const uint32_t bn = f16 ? ta::f16_tile_keys(head_dim) : ta::f32_tile_keys(head_dim);
   a.row_tiles = ceil_div(a.rows, rpw);
   a.n_tiles = ceil_div(kv_seq_len, bn);

@@ -40,7 +40,8 @@ struct FwdArgs {
   uint32_t row_tiles;  // ceil(rows / rows per workgroup)
   uint32_t n_tiles;    // ceil(kv_seq_len / BN)
   uint32_t units;      // n_kv_heads * nwg
-  float qscale;        // scale * log2(e): logits are kept in base-2 units
+  float qscale;        // scale * log2(e): logits in base-2 units (fp32 kernel)
+  float scale;         // softmax scale: logits in natural units (fp16 kernel)
 };
 
 // ---------------------------------------------------------------------------
@@ -93,9 +94,8 @@ hipError_t launch_tree_mask(const MaskArgs &a, hipStream_t s);
 constexpr uint32_t kF32RowsPerWG = 16;
 constexpr uint32_t kQuantRowsPerWG = 16;
 uint32_t f16_tile_keys(uint32_t head_dim);
-// Row blocks of 16 per wavefront the fp16 kernel uses for this shape; a
-// workgroup then covers 64 * row_blocks rows.
-uint32_t f16_row_blocks(uint32_t head_dim, uint32_t rows);
+// Rows one workgroup of the fp16 kernel covers for this shape.
+uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows);
 uint32_t f32_tile_keys(uint32_t head_dim);
 uint32_t quant_tile_keys(uint32_t dim);
 

@@ -12,64 +12,103 @@
 //
 // With this orientation every lane owns one query row in both the score and
 // the output accumulators, so the softmax state (M, S) and the rescale factor
-// stay in the lane.  Q' = Q * scale * log2(e) is rounded to fp16 once; logits
-// are kept in base-2 units and exponentiated with exp2.
+// stay in the lane.  Q' = Q * scale is rounded to fp16 once.  The score
+// instruction's accumulator input is the tile's mask (the additive cell, or
+// -inf for an excluded key), so S^T comes out with the mask already added;
+// p = exp2(s * log2(e) - M * log2(e)).  The row sum S is a matrix
+// instruction too: a block of ones times P^T, i.e. the sum of the same fp16
+// p that weight O.
 //
-// Workgroup = 4 wavefronts; each wavefront owns RB blocks of 16 rows and
-// feeds every K/V operand it reads from LDS to RB matrix instructions, which
-// keeps LDS traffic below the matrix-core rate (LDS delivers ~128 B/clk/CU;
-// one 16x16x32 instruction consumes 1 KB of A operand for 16 kflop).
+// Workgroup = W wavefronts; each owns RB blocks of 16 rows and feeds every
+// K/V operand it reads from LDS to RB matrix instructions.  head_dim 256
+// runs W = 8 (two wavefronts per SIMD, RB = 1): with one barrier per tile
+// keeping the wavefronts in step, a second wavefront per SIMD is what lets
+// LDS waits and the softmax of one overlap the matrix work of the other.
 //
-// K/V tiles of 32 keys move global -> registers during the previous tile's
-// arithmetic and registers -> LDS after it (double-buffered LDS, one barrier
-// per tile).  K and V are both stored row-major with a 16-byte-chunk XOR swizzle
-// (chunk c of row r lives at c ^ (r & 15)), which makes every operand read
-// bank-conflict free; V^T operands come from ds_read_b64_tr_b16, which
-// transposes 4x16 blocks of 16-bit values on the way out of LDS.
+// Memory pipeline: tiles of 32 keys (K, V and the raw mask cells of the
+// workgroup's tree nodes) go straight from global memory into a ring of NS
+// LDS stages with global_load_lds_dwordx4, NS - 1 tiles ahead of the
+// arithmetic, so about (NS - 1) * 32 KB per CU is in flight to cover the
+// latency of HBM; no registers hold staged data.  One barrier per tile; a
+// tile's K copies go out right after it and its V and mask copies after the
+// scores, so that they drain behind the arithmetic rather than in a burst.
+// K and V are stored row-major with a 16-byte-chunk XOR swizzle (chunk c of
+// row r lives at c ^ (r & 15)): every lane of a copy picks the global chunk
+// that belongs at its LDS slot, and every operand read is bank-conflict free.
+// V^T operands come from ds_read_b64_tr_b16, which transposes 4x16 blocks of
+// 16-bit values on the way out of LDS.
 //
-// The explicit mask tile of the workgroup's tree nodes is staged in LDS with
-// the K/V tile.  A wavefront whose rows have every cell of a tile at or below
-// -65504 skips that tile's arithmetic ("tree_attention.metal" skips fully
-// masked chunks); the tile's K/V is still fetched for the other wavefronts.
+// A wavefront whose rows have every cell of a tile excluded (mask at or below
+// -65504, or past the causal limit) skips that tile's arithmetic
+// ("tree_attention.metal" skips fully masked chunks); the tile is still
+// fetched for the other wavefronts.
 #include "common.h"
+
+#include <type_traits>
 
 namespace ta {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int BN = 32;   // keys per tile
-constexpr int MST = BN + 4;  // mask tile row stride (floats)
+constexpr int BN = 32;                // keys per tile
+constexpr int kLdsBytes = 160 * 1024;
 // Lazy-rescale threshold of the running max, in base-2 logit units.
 constexpr float kLazy = 8.0f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-template <int D, int RB, int MROWS = 64 * RB> struct F16Shape {
-  static constexpr int RPW = kWaves * 16 * RB;           // rows per workgroup
-  static constexpr int CH = D / 8;                       // 16-byte chunks per row
-  static constexpr int KB = BN / 16;                     // 16-key score blocks
-  static constexpr int DS = D / 32;                      // QK steps over d
-  static constexpr int DB = D / 16;                      // PV output blocks over d
-  static constexpr int KVCH = BN * CH / kThreads;        // K (and V) chunks per thread
-  static constexpr int MCH = (MROWS * (BN / 4) + kThreads - 1) / kThreads;  // mask float4/thread
-  static constexpr size_t KV_LDS = 2 * 2 * (size_t)BN * D * sizeof(half_t);
-  static_assert(KVCH >= 1, "tile too small for the workgroup");
+// Asynchronous global -> LDS copies: every lane moves 16 (or 4) bytes from its
+// own global address to lds + 16 * lane (4 * lane), `lds` being the
+// wavefront's LDS byte address.  They are issued from inline assembly so that
+// the compiler adds no waits of its own; the kernel waits with wait_vm<N>(),
+// N = copies the wavefront issued later that may stay in flight.
+__device__ inline void dma_b128(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ inline void dma_b32(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+template <int N> __device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
+
+// MROWS: tree nodes a stage's mask tile holds (0 for the implicit causal
+// mask).  VEC: mask rows 16-byte aligned, copied 16 bytes per lane.
+template <int D, int RB, int MROWS, bool VEC, int W> struct F16Shape {
+  static constexpr int kThreads = 64 * W;             // W wavefronts
+  static constexpr int RPW = W * 16 * RB;             // rows per workgroup
+  static constexpr int CH = D / 8;                    // 16-byte chunks per K/V row
+  static constexpr int KB = BN / 16;                  // 16-key score blocks
+  static constexpr int DS = D / 32;                   // QK steps over d
+  static constexpr int DB = D / 16;                   // PV output blocks over d
+  static constexpr int KV_BYTES = BN * D * 2;         // K (or V) bytes of a tile
+  static constexpr int KV_PW = KV_BYTES / 1024 / W;   // 1 KB copies per wavefront
+  static constexpr int M_BYTES = MROWS * BN * 4;      // mask cells of a tile
+  static constexpr int M_PW = MROWS == 0 ? 0 : VEC ? M_BYTES / 1024 / W : M_BYTES / 256 / W;
+  static constexpr int STAGE = 2 * KV_BYTES + M_BYTES;
+  static constexpr int NS = cmin(4, kLdsBytes / STAGE);
+  static constexpr int PER_TILE = 2 * KV_PW + M_PW;   // copies per wavefront per tile
+  static_assert(KV_PW >= 1 && KV_BYTES % (1024 * W) == 0, "tile / workgroup shape");
+  static_assert(MROWS % (VEC ? 8 * W : 2 * W) == 0, "mask rows per wavefront");
+  static_assert(NS >= 2, "LDS too small for two stages");
+  static_assert(PER_TILE * (NS - 2) <= 63, "vmcnt range");
 };
 
 __device__ inline uint32_t swz(uint32_t row, uint32_t chunk) { return chunk ^ (row & 15u); }
 
-// MROWS: tree nodes the workgroup's mask tile can hold (64, or every row).
-template <int D, int RB, int MROWS, bool IMPLICIT, bool VEC_MASK>
-__global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
-  using S = F16Shape<D, RB, MROWS>;
-  constexpr int KB = S::KB, DS = S::DS, DB = S::DB, KVCH = S::KVCH, MCH = S::MCH;
-  extern __shared__ __attribute__((aligned(16))) half_t lds_h[];
-  half_t *Ks0 = lds_h;                        // [2][BN][D] swizzled
-  half_t *Vs0 = lds_h + 2 * BN * D;           // [2][BN][D] swizzled
-  float *Ms0 = reinterpret_cast<float *>(lds_h + 4 * BN * D);  // [2][nodes][MST]
+template <int D, int RB, int MROWS, bool VEC, int W>
+__global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
+  constexpr bool IMPLICIT = MROWS == 0;
+  using S = F16Shape<D, RB, MROWS, VEC, W>;
+  constexpr int KB = S::KB, DS = S::DS, DB = S::DB, NS = S::NS;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) char *)lds);
 
   uint32_t unit, rt;
   decode_block(blockIdx.x, a.row_tiles, unit, rt);
@@ -77,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
   const uint32_t hk = unit / a.nwg;
   const uint32_t split = unit % a.nwg;
   const uint32_t tid = threadIdx.x;
-  const uint32_t wave = tid / kWave;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const uint32_t lane = tid % kWave;
   const uint32_t n = lane & 15u;   // the lane's query row within a 16-row block
   const uint32_t gp = lane >> 4;   // lane group
@@ -105,8 +144,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
         x0 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp);
         x1 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp + 4);
       }
-      x0 *= a.qscale;
-      x1 *= a.qscale;
+      x0 *= a.scale;
+      x1 *= a.scale;
       qf[rb][ds] = half8_t{(half_t)x0[0], (half_t)x0[1], (half_t)x0[2], (half_t)x0[3],
                            (half_t)x1[0], (half_t)x1[1], (half_t)x1[2], (half_t)x1[3]};
     }
@@ -117,86 +156,88 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
   const half_t *V = static_cast<const half_t *>(a.v) + kvbase;
   const uint32_t L = a.kv_seq_len;
 
-  // ---- global -> register staging of one tile (K, V and the mask tile) ----
-  struct Stage {
-    u32x4 k[KVCH], v[KVCH];
-    floatx4 m[IMPLICIT ? 1 : MCH];
+  // ---- copies of one tile into its stage ----
+  // K/V: copy i of this wavefront fills LDS chunks p = 64 (W_i) + lane of the
+  // tile, W_i = wave * KV_PW + i; chunk p is row p / CH, physical chunk
+  // p % CH, holding logical chunk (p % CH) ^ (row & 15).
+  uint32_t kv_row[S::KV_PW], kv_col[S::KV_PW];
+#pragma unroll
+  for (int i = 0; i < S::KV_PW; ++i) {
+    const uint32_t p = (wave * S::KV_PW + i) * 64u + lane;
+    kv_row[i] = p / S::CH;
+    kv_col[i] = 8u * swz(kv_row[i], p % S::CH);
+  }
+  // mask: node rows of BN cells (128 bytes) back to back; a 16-byte copy
+  // covers 8 rows (lane / 8, cells 4 (lane % 8) ..), a 4-byte copy 2 rows
+  // (lane / 32, cell lane % 32).  Rows past the workgroup's nodes re-read
+  // node0's row and are never used.
+  constexpr int M_RPC = VEC ? 8 : 2;   // mask rows per copy
+  uint32_t m_row[S::M_PW > 0 ? S::M_PW : 1];
+  const uint32_t m_col = VEC ? 4u * (lane % 8u) : lane % 32u;
+#pragma unroll
+  for (int j = 0; j < S::M_PW; ++j) {
+    const uint32_t r = (wave * S::M_PW + j) * M_RPC + lane / (64u / M_RPC);
+    m_row[j] = r < nnodes ? r : 0u;
+  }
+  auto stage_addr = [&](uint32_t t, uint32_t t0) -> uint32_t {
+    return lds0 + ((t - t0) % NS) * S::STAGE;
   };
-  auto load = [&](uint32_t t, Stage &st) {
+  // part 0: the K copies; part 1: the V and mask copies.  The two parts go
+  // out at different points of a tile's arithmetic, so that the copies
+  // drain behind it instead of queueing in one burst.
+  auto issue = [&](uint32_t t, uint32_t t0, auto part) {
+    constexpr int PART = decltype(part)::value;
     const uint32_t key0 = t * BN;
-    if (key0 + BN <= L) {  // whole tile in range: no per-lane checks
+    const uint32_t sb = stage_addr(t, t0);
+    const bool full = key0 + BN <= L;
 #pragma unroll
-      for (int u = 0; u < KVCH; ++u) {
-        const uint32_t c = tid + kThreads * u;
-        const size_t off = (size_t)key0 * D + (size_t)(c / S::CH) * D + 8 * (c % S::CH);
-        st.k[u] = *reinterpret_cast<const u32x4 *>(K + off);
-        st.v[u] = *reinterpret_cast<const u32x4 *>(V + off);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < KVCH; ++u) {
-        const uint32_t c = tid + kThreads * u;
-        const uint32_t key = c / S::CH, ch = c % S::CH;
-        const bool in = key0 + key < L;
-        const size_t off = (size_t)(key0 + key) * D + 8 * ch;
-        st.k[u] = in ? *reinterpret_cast<const u32x4 *>(K + off) : u32x4{0u, 0u, 0u, 0u};
-        st.v[u] = in ? *reinterpret_cast<const u32x4 *>(V + off) : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < S::KV_PW; ++i) {
+      // keys past kv_seq_len re-read the last valid row (never used)
+      uint32_t key = key0 + kv_row[i];
+      if (!full) key = min(key, L - 1u);
+      const size_t off = (size_t)key * D + kv_col[i];
+      const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
+      if (PART == 0)
+        dma_b128(K + off, la);
+      else
+        dma_b128(V + off, la + S::KV_BYTES);
     }
-    if (!IMPLICIT) {
+    if (PART == 1) {
 #pragma unroll
-      for (int u = 0; u < MCH; ++u) {
-        const uint32_t e = tid + kThreads * u;        // float4 index in the tile
-        const uint32_t nd = e / (BN / 4), k4 = 4u * (e % (BN / 4));
-        floatx4 x = {kMasked, kMasked, kMasked, kMasked};
-        if (nd < nnodes) {
-          const float *mr = a.mask + (size_t)(node0 + nd) * a.mask_stride + key0 + k4;
-          if (VEC_MASK && key0 + k4 + 3u < L) {
-            x = *reinterpret_cast<const floatx4 *>(mr);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (key0 + k4 + j < L) x[j] = mr[j];
-          }
-        }
-        st.m[u] = x;
+      for (int j = 0; j < S::M_PW; ++j) {
+        uint32_t key = key0 + m_col;
+        // past kv_seq_len: stay inside the row (16-byte chunks: the chunk
+        // that holds cell L - 1, which ends before mask_stride)
+        if (key >= L) key = VEC ? ((L - 1u) & ~3u) : L - 1u;
+        const float *g = a.mask + (size_t)(node0 + m_row[j]) * a.mask_stride + key;
+        const uint32_t la = sb + 2u * S::KV_BYTES + (wave * S::M_PW + j) * (VEC ? 1024u : 256u);
+        if (VEC)
+          dma_b128(g, la);
+        else
+          dma_b32(g, la);
       }
     }
   };
-  auto store = [&](const Stage &st, uint32_t buf) {
-    half_t *Ks = Ks0 + buf * BN * D;
-    half_t *Vs = Vs0 + buf * BN * D;
-#pragma unroll
-    for (int u = 0; u < KVCH; ++u) {
-      const uint32_t c = tid + kThreads * u;
-      const uint32_t key = c / S::CH, ch = c % S::CH;
-      const uint32_t pos = key * D + 8 * swz(key, ch);
-      *reinterpret_cast<u32x4 *>(Ks + pos) = st.k[u];
-      *reinterpret_cast<u32x4 *>(Vs + pos) = st.v[u];
-    }
-    if (!IMPLICIT) {
-      float *Ms = Ms0 + buf * (size_t)MROWS * MST;
-#pragma unroll
-      for (int u = 0; u < MCH; ++u) {
-        const uint32_t e = tid + kThreads * u;
-        const uint32_t nd = e / (BN / 4), k4 = 4u * (e % (BN / 4));
-        // stored as the base-2 logit offset: log2(e) * m, or -inf when the
-        // cell excludes the key (m <= -65504)
-        floatx4 x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = st.m[u][j] > kMasked ? st.m[u][j] * kLog2e : -INFINITY;
-        if (nd < nnodes) *reinterpret_cast<floatx4 *>(Ms + nd * MST + k4) = x;
-      }
-    }
+  // wait until tile t has landed; `after` later tiles (0 .. NS - 2) may stay in flight
+  auto wait_tile = [&](uint32_t after) {
+    if (NS >= 4 && after >= 2)
+      wait_vm<(NS >= 4 ? 2 * S::PER_TILE : 0)>();
+    else if (NS >= 3 && after >= 1)
+      wait_vm<(NS >= 3 ? S::PER_TILE : 0)>();
+    else
+      wait_vm<0>();
   };
 
   // ---- online-softmax state of the lane's rows ----
-  float Mrow[RB], Srow[RB];
-  floatx4 oacc[RB][DB];
+  // M in natural units; nml = -M * log2(e) (0 while M is -inf, when O and S
+  // are still zero); S and O accumulate in matrix-core registers.
+  float Mrow[RB], nml[RB];
+  floatx4 oacc[RB][DB], sacc_sum[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     Mrow[rb] = -INFINITY;
-    Srow[rb] = 0.0f;
+    nml[rb] = 0.0f;
+    sacc_sum[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[rb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -205,50 +246,56 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
   for (int rb = 0; rb < RB; ++rb)
     causal_last[rb] = (int64_t)L - (int64_t)a.q_l + (int64_t)node[rb];
 
-  // Scores and online softmax of tile t (buffer buf) for the lane's rows.
-  // Sets pf (the P^T operands) and alpha (the rescale of O each row needs,
-  // 1 almost always); returns 0 if none of the wavefront's cells is live.
-  auto qk_softmax = [&](uint32_t t, uint32_t buf, float (&alpha_out)[RB],
-                        half8_t (&pf)[RB]) -> int {
+  // Scores and online softmax of tile t (stage at LDS byte address sb) for the
+  // lane's rows.  Sets pf (the P^T operands) and alpha (the rescale of O each
+  // row needs, 1 almost always); returns 0 if none of the wavefront's cells
+  // is live.  GENERAL: the tile may hold keys past kv_seq_len or (implicit
+  // mask) past a row's causal limit, so every cell is checked; otherwise every
+  // key is in range and, with the implicit mask, attended by every row.
+  auto qk_softmax = [&](uint32_t t, uint32_t sb, float (&alpha_out)[RB], half8_t (&pf)[RB],
+                        auto general) -> int {
+    constexpr bool GENERAL = decltype(general)::value;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) alpha_out[rb] = 1.0f;
-    const half_t *Ks = Ks0 + buf * BN * D;
-    const half_t *Vs = Vs0 + buf * BN * D;
-    const float *Ms = Ms0 + buf * (size_t)MROWS * MST;
+    const half_t *Ks = reinterpret_cast<const half_t *>(lds + (sb - lds0));
+    const float *Ms = reinterpret_cast<const float *>(lds + (sb - lds0) + 2 * S::KV_BYTES);
     const uint32_t key0 = t * BN;
-    // base-2 logit offsets of the lane's rows, keys 16kb + 4gp + j: log2(e)
-    // times the mask cell, -inf for an excluded key.  Rows past the end use
-    // node0's cells; their Q is zero and their results are never written.
-    float m[RB][KB][4];
-    float mmax = -INFINITY;
+    // accumulator inputs: the lane's cells, keys 16kb + 4gp + j -- the
+    // additive mask value, or -inf for an excluded key.  Rows past the end
+    // use node0's cells; their Q is zero and their results are never written.
+    floatx4 sacc[RB][KB];
+    if (IMPLICIT && !GENERAL) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if (IMPLICIT) {
+        for (int kb = 0; kb < KB; ++kb) sacc[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      float mmax = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          floatx4 x;
+          if (!IMPLICIT)
+            x = *reinterpret_cast<const floatx4 *>(Ms + (node[rb] - node0) * BN + 16 * kb + 4 * gp);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t key = key0 + 16u * kb + 4u * gp + j;
-            const bool in = key < L && (int64_t)key <= causal_last[rb];
-            m[rb][kb][j] = in ? 0.0f : -INFINITY;
+            bool in;
+            if (IMPLICIT)
+              in = key < L && (int64_t)key <= causal_last[rb];
+            else if (GENERAL)
+              in = x[j] > kMasked && key < L;
+            else
+              in = x[j] > kMasked;
+            sacc[rb][kb][j] = in ? (IMPLICIT ? 0.0f : x[j]) : -INFINITY;
+            mmax = fmaxf(mmax, sacc[rb][kb][j]);
           }
-        } else {
-          const floatx4 x = *reinterpret_cast<const floatx4 *>(
-              Ms + (node[rb] - node0) * MST + 16 * kb + 4 * gp);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) m[rb][kb][j] = x[j];
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mmax = fmaxf(mmax, m[rb][kb][j]);
-      }
-    if (!__any(mmax > -INFINITY)) return 0;
+      if (!__any(mmax > -INFINITY)) return 0;
+    }
 
-    // S^T: each K operand feeds RB instructions
-    floatx4 sacc[RB][KB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) sacc[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // S^T (+ mask): each K operand feeds RB instructions
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
 #pragma unroll
@@ -264,48 +311,49 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
     // online softmax per row block; P^T operands
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float s = sacc[rb][kb][j] + m[rb][kb][j];
-          sacc[rb][kb][j] = s;
-          tmax = fmaxf(tmax, s);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      float tmax = fmaxf(fmaxf(fmaxf(sacc[rb][0][0], sacc[rb][0][1]), fmaxf(sacc[rb][0][2], sacc[rb][0][3])),
+                         fmaxf(fmaxf(sacc[rb][1][0], sacc[rb][1][1]), fmaxf(sacc[rb][1][2], sacc[rb][1][3])));
+      // the row's 32 cells sit in lanes n, n + 16, n + 32, n + 48
+      {
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      }
       // Lazy rescale: the reference max moves (and O, S are rescaled) only
       // when the tile's max exceeds it by more than kLazy (base 2); until
-      // then p = 2^(s - M) <= 2^kLazy, exact in fp16 and fp32.  O, S and M
-      // stay consistent, so the result is the same softmax.
+      // then p <= 2^kLazy, exact in fp16 and fp32.  O, S and M stay
+      // consistent, so the result is the same softmax.
       float alpha = 1.0f;
-      if (tmax > Mrow[rb] + kLazy) {
+      if (tmax > Mrow[rb] + kLazy * kLn2) {
+        const float nml_new = -tmax * kLog2e;
         // (O and S are still zero when M is -inf: nothing to rescale)
-        alpha = (Mrow[rb] == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(Mrow[rb] - tmax);
+        alpha = (Mrow[rb] == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(nml_new - nml[rb]);
         Mrow[rb] = tmax;
+        nml[rb] = nml_new;
       }
-      const float m_use = (Mrow[rb] == -INFINITY) ? 0.0f : Mrow[rb];
-      float p[8], psum = 0.0f;
+      float p[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(sacc[rb][0][j] - m_use);
-        p[4 + j] = __builtin_amdgcn_exp2f(sacc[rb][1][j] - m_use);
+        p[j] = __builtin_amdgcn_exp2f(fmaf(sacc[rb][0][j], kLog2e, nml[rb]));
+        p[4 + j] = __builtin_amdgcn_exp2f(fmaf(sacc[rb][1][j], kLog2e, nml[rb]));
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) psum += p[j];
-      Srow[rb] = Srow[rb] * alpha + psum;
       pf[rb] = half8_t{(half_t)p[0], (half_t)p[1], (half_t)p[2], (half_t)p[3],
                        (half_t)p[4], (half_t)p[5], (half_t)p[6], (half_t)p[7]};
       alpha_out[rb] = alpha;
     }
     return 1;
   };
-  // O^T += V^T P^T for tile buffer buf.
-  auto pv = [&](uint32_t buf, const half8_t (&pf)[RB]) {
-    const half_t *Vs = Vs0 + buf * BN * D;
-    // O^T += V^T P^T: V^T operand of d-block db for keys F(gp, 0..7) read as
-    // two transposed 4x16 blocks (keys 4gp..4gp+3 and 16+4gp..16+4gp+3)
+  // O^T += V^T P^T and S += 1 P^T for the stage at LDS byte address sb.
+  const half8_t ones = {(half_t)1.0f, (half_t)1.0f, (half_t)1.0f, (half_t)1.0f,
+                        (half_t)1.0f, (half_t)1.0f, (half_t)1.0f, (half_t)1.0f};
+  auto pv = [&](uint32_t sb, const half8_t (&pf)[RB]) {
+    const half_t *Vs = reinterpret_cast<const half_t *>(lds + (sb - lds0) + S::KV_BYTES);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      sacc_sum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[rb], sacc_sum[rb], 0, 0, 0);
+    // V^T operand of d-block db for keys F(gp, 0..7) read as two transposed
+    // 4x16 blocks (keys 4gp..4gp+3 and 16+4gp..16+4gp+3)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       short4_t lo, hi;
@@ -325,36 +373,62 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
         oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[rb], oacc[rb][db], 0, 0, 0);
     }
   };
-  // The rare rescale of O: kept out of the tile loop below so that the
-  // output accumulators stay in the matrix-core registers inside it.
+  // The rare rescale of O and S: kept out of the tile loop below so that the
+  // accumulators stay in the matrix-core registers inside it.
   auto rescale = [&](const float (&alpha)[RB]) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb) {
+      sacc_sum[rb] *= alpha[rb];
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha[rb];
+    }
   };
 
-  // ---- main loop: tile t on the matrix cores while t+1 is in flight ----
+  // ---- main loop ----
   uint32_t t0, t1;
   split_range(a.n_tiles, a.nwg, split, t0, t1);
-  Stage st;
-  if (t0 < t1) {
-    load(t0, st);
-    store(st, 0);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (t0 + s < t1) {
+      issue(t0 + s, t0, std::integral_constant<int, 0>{});
+      issue(t0 + s, t0, std::integral_constant<int, 1>{});
+    }
+  // Top of tile t: wait for its copies, barrier (every wavefront is done with
+  // tile t - 1), then start refilling tile t - 1's stage with tile t + NS - 1
+  // (K now, V and mask once the scores are out: refill_rest).
+  // With two stages (the widest heads) the single tile in flight is refilled
+  // in one go.
+  auto begin_tile = [&](uint32_t t) {
+    wait_tile(min(t1 - 1u - t, (uint32_t)(NS - 2)));
     __syncthreads();
-  }
-  uint32_t t = t0;
+    if (t + NS - 1 < t1) {
+      issue(t + NS - 1, t0, std::integral_constant<int, 0>{});
+      if (NS == 2) issue(t + NS - 1, t0, std::integral_constant<int, 1>{});
+    }
+  };
+  auto refill_rest = [&](uint32_t t) {
+    if (NS > 2 && t + NS - 1 < t1) issue(t + NS - 1, t0, std::integral_constant<int, 1>{});
+  };
   float alpha[RB];
   half8_t pf[RB];
-  while (t < t1) {
+  // Tiles before `fast` hold only keys below kv_seq_len and, with the
+  // implicit mask, keys every row of the workgroup attends: there the mask
+  // needs no per-cell key checks.
+  uint32_t fast = L / BN;
+  if (IMPLICIT) fast = min(fast, (uint32_t)(((int64_t)L - a.q_l + node0 + 1) / BN));
+  fast = min(max(fast, t0), t1);
+  uint32_t t = t0;
+  while (t < fast) {
     // Inner loop: nothing but matrix instructions touches O.  A wavefront
     // that must rescale leaves it; every wavefront still passes exactly one
-    // barrier per tile, here or in the rescale path below.
+    // barrier per tile.
     bool need = false;
-    for (; t < t1; ++t) {
-      const uint32_t buf = (t - t0) & 1u;
-      if (t + 1 < t1) load(t + 1, st);
-      const int live = qk_softmax(t, buf, alpha, pf);
+    uint32_t sb = 0;
+    for (; t < fast; ++t) {
+      begin_tile(t);
+      sb = stage_addr(t, t0);
+      const int live = qk_softmax(t, sb, alpha, pf, std::false_type{});
+      refill_rest(t);
       bool r = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) r |= alpha[rb] != 1.0f;
@@ -362,25 +436,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
         need = true;
         break;
       }
-      if (live) pv(buf, pf);
-      if (t + 1 < t1) store(st, buf ^ 1u);
-      __syncthreads();
+      if (live) pv(sb, pf);
     }
     if (!need) break;
-    const uint32_t buf = (t - t0) & 1u;
     rescale(alpha);
-    pv(buf, pf);
-    if (t + 1 < t1) store(st, buf ^ 1u);
-    __syncthreads();
+    pv(sb, pf);
     ++t;
+  }
+  // the remaining few tiles (at the end of the key range) check every cell
+  for (t = fast; t < t1; ++t) {
+    begin_tile(t);
+    const uint32_t sb = stage_addr(t, t0);
+    const int live = qk_softmax(t, sb, alpha, pf, std::true_type{});
+    refill_rest(t);
+    if (live) {
+      rescale(alpha);
+      pv(sb, pf);
+    }
   }
 
   // ---- results ----
   const size_t nrows = (size_t)a.n_heads * a.q_l;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    float stot = Srow[rb] + __shfl_xor(Srow[rb], 16);
-    stot += __shfl_xor(stot, 32);
+    const float stot = sacc_sum[rb][0];
     if (!valid[rb]) continue;
     const uint32_t gr = row0 + wave * 16u * RB + 16u * rb + n;
     const uint32_t head = hk * a.group + gr % a.group;
@@ -396,50 +475,57 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f16_kernel(FwdArgs a) {
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<floatx4 *>(a.part_o + prow * D + 16 * db + 4 * gp) = oacc[rb][db];
       if (gp == 0) {
+        // M in base-2 units: p was taken relative to 2^(-nml)
         a.part_sm[prow * 2 + 0] = stot;
-        a.part_sm[prow * 2 + 1] = Mrow[rb];
+        a.part_sm[prow * 2 + 1] = Mrow[rb] == -INFINITY ? -INFINITY : -nml[rb];
       }
     }
   }
 }
 
-template <int D, int RB, int MROWS, bool IMPLICIT, bool VEC>
+template <int D, int RB, int MROWS, bool VEC, int W>
 hipError_t launch_v(const FwdArgs &a, hipStream_t s) {
-  using Sh = F16Shape<D, RB, MROWS>;
-  const size_t lds = Sh::KV_LDS + (IMPLICIT ? 0 : 2 * (size_t)MROWS * MST * sizeof(float));
+  using Sh = F16Shape<D, RB, MROWS, VEC, W>;
+  const size_t lds = (size_t)Sh::NS * Sh::STAGE;
   static const bool attr_set = [] {
-    (void)hipFuncSetAttribute((const void *)fwd_f16_kernel<D, RB, MROWS, IMPLICIT, VEC>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void *)fwd_f16_kernel<D, RB, MROWS, VEC, W>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     return true;
   }();
   (void)attr_set;
   dim3 grid(grid_size(a.units, a.row_tiles));
-  hipLaunchKernelGGL((fwd_f16_kernel<D, RB, MROWS, IMPLICIT, VEC>), grid, dim3(kThreads), lds,
-                     s, a);
+  hipLaunchKernelGGL((fwd_f16_kernel<D, RB, MROWS, VEC, W>), grid, dim3(Sh::kThreads), lds, s, a);
   return hipGetLastError();
 }
 
-template <int D, int RB>
+template <int D, int RB, int W>
 hipError_t launch_rb(const FwdArgs &a, hipStream_t s) {
-  constexpr int RPW = 64 * RB;
-  if (a.mask == nullptr) return launch_v<D, RB, 64, true, false>(a, s);
+  constexpr int RPW = W * 16 * RB;
+  constexpr int M0 = 8 * W;  // smallest mask tile the wavefronts split evenly
+  if (a.mask == nullptr) return launch_v<D, RB, 0, false, W>(a, s);
   // a row tile spans at most floor((RPW - 1) / group) + 2 tree nodes
-  const bool narrow = (RPW - 1) / a.group + 2 <= 64u;
+  const uint32_t nodes = min((RPW - 1u) / a.group + 2u, a.q_l);
   const bool vec = ((uintptr_t)a.mask % 16u == 0) && (a.mask_stride % 4u == 0);
-  if (narrow)
-    return vec ? launch_v<D, RB, 64, false, true>(a, s) : launch_v<D, RB, 64, false, false>(a, s);
-  return vec ? launch_v<D, RB, RPW, false, true>(a, s) : launch_v<D, RB, RPW, false, false>(a, s);
+  if (nodes <= M0)
+    return vec ? launch_v<D, RB, M0, true, W>(a, s) : launch_v<D, RB, M0, false, W>(a, s);
+  if (nodes <= 2 * M0)
+    return vec ? launch_v<D, RB, 2 * M0, true, W>(a, s) : launch_v<D, RB, 2 * M0, false, W>(a, s);
+  return vec ? launch_v<D, RB, RPW, true, W>(a, s) : launch_v<D, RB, RPW, false, W>(a, s);
 }
 
 }  // namespace
 
 uint32_t f16_tile_keys(uint32_t) { return (uint32_t)BN; }
 
-// Row blocks per wavefront: as many as registers allow without spilling (3
-// for head_dim 128, 2 for 256, 1 for 512), fewer when that wastes fewer
-// padded rows.
-uint32_t f16_row_blocks(uint32_t head_dim, uint32_t rows) {
-  const uint32_t max_rb = head_dim >= 512 ? 1u : head_dim >= 256 ? 2u : 3u;
+// Launch plan: W wavefronts of RB 16-row blocks.  head_dim 256 runs two
+// wavefronts per SIMD (W = 8, RB = 1) so that one wavefront's softmax and LDS
+// waits overlap the other's matrix instructions; 128 and 512 run one per SIMD
+// (W = 4) with as many row blocks as registers allow without spilling, fewer
+// when that wastes fewer padded rows.
+struct F16Plan { uint32_t w, rb; };
+static F16Plan f16_plan(uint32_t head_dim, uint32_t rows) {
+  if (head_dim == 256) return F16Plan{8u, 1u};
+  const uint32_t max_rb = head_dim >= 512 ? 1u : 3u;
   uint32_t best = 1, best_waste = 0xffffffffu;
   for (uint32_t rb = max_rb; rb >= 1; --rb) {
     const uint32_t rpw = 64u * rb;
@@ -449,18 +535,23 @@ uint32_t f16_row_blocks(uint32_t head_dim, uint32_t rows) {
       best_waste = waste;
     }
   }
-  return best;
+  return F16Plan{4u, best};
+}
+
+uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows) {
+  const F16Plan p = f16_plan(head_dim, rows);
+  return 16u * p.w * p.rb;
 }
 
 hipError_t launch_forward_f16(const FwdArgs &a, uint32_t head_dim, hipStream_t s) {
-  const uint32_t rb = f16_row_blocks(head_dim, a.rows);
+  const F16Plan p = f16_plan(head_dim, a.rows);
   switch (head_dim) {
     case 128:
-      return rb == 3 ? launch_rb<128, 3>(a, s) : rb == 2 ? launch_rb<128, 2>(a, s)
-                                                         : launch_rb<128, 1>(a, s);
+      return p.rb == 3 ? launch_rb<128, 3, 4>(a, s) : p.rb == 2 ? launch_rb<128, 2, 4>(a, s)
+                                                                : launch_rb<128, 1, 4>(a, s);
     case 256:
-      return rb == 2 ? launch_rb<256, 2>(a, s) : launch_rb<256, 1>(a, s);
-    case 512: return launch_rb<512, 1>(a, s);
+      return launch_rb<256, 1, 8>(a, s);
+    case 512: return launch_rb<512, 1, 4>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

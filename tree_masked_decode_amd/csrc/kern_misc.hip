@@ -51,9 +51,16 @@ hipError_t launch_tree_mask(const MaskArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of split partials.  One wavefront per output row; splits are visited
-// in index order so the result does not depend on timing.  M is in base-2
-// units, so the rescale factor of split w is 2^(M_w - M*).
+// Merge of split partials (log-sum-exp combine).  M is in base-2 units, so
+// split w's rescale factor is 2^(M_w - M*), M* the largest M of a non-empty
+// split; the row is sum_w O_w 2^(M_w - M*) / sum_w S_w 2^(M_w - M*), and an
+// empty row (no non-empty split) is 0.
+//
+// A block of 256 threads owns RPB rows.  Phase 1: wavefront v finds M* and
+// 1/S* of rows v, v+4, ... (lanes over splits) and leaves them in LDS.
+// Phase 2: TPR threads per row each own float4 columns of the row and walk the
+// splits in index order, eight independent loads at a time, so the sum does
+// not depend on timing and enough loads are in flight to cover latency.
 // ---------------------------------------------------------------------------
 __device__ inline float wave_max(float x) {
 #pragma unroll
@@ -66,64 +73,104 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-template <bool OUT_F16>
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t r = blockIdx.x * 4u + (threadIdx.x >> 6);
-  if (r >= a.nrows) return;
-  const float *sm = a.part_sm;
-  const size_t nrows = a.nrows;
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
-  float mstar = -INFINITY;
-  for (uint32_t w = lane; w < a.nwg; w += 64u) {
-    float s = sm[((size_t)w * nrows + r) * 2 + 0];
-    float m = sm[((size_t)w * nrows + r) * 2 + 1];
-    if (s > 0.0f) mstar = fmaxf(mstar, m);
-  }
-  mstar = wave_max(mstar);
-  float sstar = 0.0f;
-  if (mstar != -INFINITY) {
-    for (uint32_t w = lane; w < a.nwg; w += 64u) {
-      float s = sm[((size_t)w * nrows + r) * 2 + 0];
-      float m = sm[((size_t)w * nrows + r) * 2 + 1];
-      if (s > 0.0f) sstar += s * exp2f(m - mstar);
+template <bool OUT_F16, uint32_t TPR>
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+  constexpr uint32_t RPB = 256u / TPR;
+  constexpr uint32_t U = 8;
+  __shared__ float s_mstar[RPB], s_inv[RPB];
+  const uint32_t wv = threadIdx.x >> 6, lane = threadIdx.x & 63u;
+  const size_t nrows = a.nrows;
+  const float2_t *sm = reinterpret_cast<const float2_t *>(a.part_sm);  // (S, M)
+  const uint32_t row0 = blockIdx.x * RPB;
+
+  for (uint32_t rr = wv; rr < RPB; rr += 4u) {
+    const size_t r = row0 + rr;
+    float mstar = -INFINITY, ssum = 0.0f;
+    if (r < nrows) {
+      for (uint32_t w = lane; w < a.nwg; w += 64u) {
+        const float2_t v = sm[(size_t)w * nrows + r];
+        if (v.x > 0.0f) mstar = fmaxf(mstar, v.y);
+      }
+      mstar = wave_max(mstar);
+      if (mstar != -INFINITY) {
+        for (uint32_t w = lane; w < a.nwg; w += 64u) {
+          const float2_t v = sm[(size_t)w * nrows + r];
+          if (v.x > 0.0f) ssum += v.x * exp2f(v.y - mstar);
+        }
+      }
+      ssum = wave_sum(ssum);
+    }
+    if (lane == 0) {
+      s_mstar[rr] = mstar;
+      s_inv[rr] = ssum > 0.0f ? 1.0f / ssum : 0.0f;
     }
   }
-  sstar = wave_sum(sstar);
-  const float inv = (sstar > 0.0f) ? 1.0f / sstar : 0.0f;
+  __syncthreads();
 
-  for (uint32_t d4 = lane; d4 < a.dim / 4u; d4 += 64u) {
-    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (sstar > 0.0f) {
-      for (uint32_t w = 0; w < a.nwg; ++w) {
-        float s = sm[((size_t)w * nrows + r) * 2 + 0];
-        if (!(s > 0.0f)) continue;
-        float f = exp2f(sm[((size_t)w * nrows + r) * 2 + 1] - mstar);
-        const floatx4 o = *reinterpret_cast<const floatx4 *>(
-            a.part_o + ((size_t)w * nrows + r) * a.dim + 4u * d4);
-        acc += o * f;
+  const uint32_t rr = threadIdx.x / TPR, t = threadIdx.x % TPR;
+  const size_t r = row0 + rr;
+  if (r >= nrows) return;
+  const float mstar = s_mstar[rr], inv = s_inv[rr];
+  const uint32_t d4n = a.dim / 4u;
+  const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (uint32_t d4 = t; d4 < d4n; d4 += TPR) {
+    floatx4 acc = zero;
+    if (inv > 0.0f) {
+      const floatx4 *po = reinterpret_cast<const floatx4 *>(a.part_o) + r * d4n + d4;
+      const size_t wstride = nrows * d4n;
+      uint32_t w = 0;
+      for (; w + U <= a.nwg; w += U) {
+        floatx4 o[U];
+        float2_t v[U];
+#pragma unroll
+        for (uint32_t j = 0; j < U; ++j) {
+          v[j] = sm[(size_t)(w + j) * nrows + r];
+          o[j] = po[(size_t)(w + j) * wstride];
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < U; ++j) {
+          // an empty split (S = 0) contributes nothing, whatever its O holds
+          const bool use = v[j].x > 0.0f;
+          const float f = use ? exp2f(v[j].y - mstar) : 0.0f;
+          acc += (use ? o[j] : zero) * f;
+        }
+      }
+      for (; w < a.nwg; ++w) {
+        const float2_t v = sm[(size_t)w * nrows + r];
+        const floatx4 o = po[(size_t)w * wstride];
+        const bool use = v.x > 0.0f;
+        const float f = use ? exp2f(v.y - mstar) : 0.0f;
+        acc += (use ? o : zero) * f;
       }
     }
     acc *= inv;
     if (OUT_F16) {
-      half4_t h = {(half_t)acc[0], (half_t)acc[1], (half_t)acc[2],
-                   (half_t)acc[3]};
-      *reinterpret_cast<half4_t *>(static_cast<half_t *>(a.out) +
-                                   (size_t)r * a.dim + 4u * d4) = h;
+      half4_t h = {(half_t)acc[0], (half_t)acc[1], (half_t)acc[2], (half_t)acc[3]};
+      reinterpret_cast<half4_t *>(a.out)[r * d4n + d4] = h;
     } else {
-      *reinterpret_cast<floatx4 *>(static_cast<float *>(a.out) +
-                                   (size_t)r * a.dim + 4u * d4) = acc;
+      reinterpret_cast<floatx4 *>(a.out)[r * d4n + d4] = acc;
     }
   }
 }
 
-hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s) {
-  dim3 grid((a.nrows + 3u) / 4u);
+template <uint32_t TPR>
+hipError_t launch_reduce_t(const ReduceArgs &a, hipStream_t s) {
+  constexpr uint32_t RPB = 256u / TPR;
+  dim3 grid((a.nrows + RPB - 1u) / RPB);
   if (a.out_f16)
-    hipLaunchKernelGGL(reduce_kernel<true>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((reduce_kernel<true, TPR>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(reduce_kernel<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((reduce_kernel<false, TPR>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s) {
+  const uint32_t d4n = a.dim / 4u;
+  if (d4n >= 64u) return launch_reduce_t<64>(a, s);
+  if (d4n >= 32u) return launch_reduce_t<32>(a, s);
+  return launch_reduce_t<16>(a, s);
 }
 
 }  // namespace ta
