@@ -50,6 +50,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain copy of known size (for PMC byte scaling)")
+    p.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) "
+                        "of a --copy-calibration run into profiles/traffic_<workload>.json "
+                        "and exit")
     return p.parse_args()
 
 
@@ -109,6 +113,51 @@ def measured_traffic(workload, kind):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20     # the --copy-calibration copy: reads and writes this much
+
+
+def record_traffic(workload, fetch_csv, write_csv):
+    """HBM bytes per forward launch from two rocprofv3 --pmc runs.
+
+    FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by
+    COPY_BYTES / (what the same counter reads for the calibration copy), so
+    that a plain copy of known size counts exactly its size.  The forward
+    kernel is the dispatch whose name holds "fwd"/"quant_fwd"; its dispatches
+    are averaged."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        return acc
+
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        acc = per_kernel(path, name)
+        copy = [v for (k, _), v in acc.items() if "copy" in k.lower() or "elementwise" in k.lower()]
+        fwd = [v for (k, _), v in acc.items() if "fwd" in k]
+        if not copy or not fwd:
+            raise SystemExit("record-traffic: no copy or forward dispatches in %s" % path)
+        copy_kib = max(copy)  # the 256 MiB copies (other copies are small)
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        out[name] = {"kib_per_launch": statistics.fmean(fwd), "copy_kib": copy_kib,
+                     "scale": scale, "dispatches": len(fwd)}
+    from tree_masked_decode_amd import inputs
+    kind = ("quant" if workload in inputs.QUANT_WORKLOADS
+            else inputs.WORKLOADS[workload]["kv_dtype"])
+    total = sum(v["kib_per_launch"] * 1024.0 * v["scale"] for v in out.values())
+    rec = {"workload": workload, "kernel": "forward", "bytes_per_launch": round(total),
+           "counters": out, "source_sha": source_sha(FWD_SOURCES[kind])}
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 # --------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample of rows
 # --------------------------------------------------------------------------
@@ -152,9 +201,12 @@ def cpu_baseline(name, c, alg, quant):
 # --------------------------------------------------------------------------
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
-              "(the sharded design is described in DESIGN.md)" % args.gpus, file=sys.stderr)
+        print("bench.py: measures one GPU only; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
