@@ -81,15 +81,16 @@ uint64_t partials_bytes_u64(uint64_t nrows, uint64_t dim, uint64_t nwg,
 // of one (head, split) unit sits on one XCD, so an XCD holds
 // ceil(heads * nwg / 8) * row_tiles workgroups: as many splits as keep that
 // within ONE round of the XCD's resident slots (CUs per XCD * per_cu), with at
-// least 8 key tiles per split and no more partial-result bytes (written once,
-// read once by the merge) than K/V bytes.
+// least min_tiles key tiles per split and no more partial-result bytes
+// (written once, read once by the merge) than K/V bytes.
 uint32_t pick_splits(uint32_t heads, uint32_t row_tiles, uint32_t n_tiles, uint32_t num_cus,
-                     uint32_t per_cu, uint64_t kv_bytes, uint64_t partial_bytes_per_split) {
+                     uint32_t per_cu, uint32_t min_tiles, uint64_t kv_bytes,
+                     uint64_t partial_bytes_per_split) {
   if (num_cus == 0) num_cus = 256;
   const uint64_t slots_per_xcd = (uint64_t)(num_cus / ta::kXcds) * per_cu;
   const uint64_t units_per_xcd = row_tiles ? slots_per_xcd / row_tiles : 0;
   uint64_t nwg = units_per_xcd * ta::kXcds / heads;
-  const uint64_t by_tiles = n_tiles / 8;
+  const uint64_t by_tiles = n_tiles / min_tiles;
   if (nwg > by_tiles) nwg = by_tiles;
   if (partial_bytes_per_split > 0 && nwg > kv_bytes / partial_bytes_per_split)
     nwg = kv_bytes / partial_bytes_per_split;
@@ -128,7 +129,7 @@ uint32_t tree_attn_pick_nwg(uint32_t n_heads, uint32_t n_kv_heads,
   const uint64_t kv = 2ull * n_kv_heads * kv_seq_len * head_dim * (f16 ? 2u : 4u);
   const uint64_t part = (uint64_t)n_heads * q_l * (head_dim + 2) * 4;
   return pick_splits(n_kv_heads, ceil_div(rows, rpw), ceil_div(kv_seq_len, bn), num_cus,
-                     per_cu, kv, part);
+                     per_cu, 2u, kv, part);
 }
 
 uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
@@ -143,7 +144,7 @@ uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
   const uint64_t kv = 2ull * batch * n_kv_heads * kv_seq_len * dim / 2;
   const uint64_t part = (uint64_t)batch * n_q_heads * q_l * (dim + 2) * 4;
   return pick_splits(batch * n_kv_heads, ceil_div(rows, ta::kQuantRowsPerWG),
-                     ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, 8u, kv, part);
+                     ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, 8u, 8u, kv, part);
 }
 
 int tree_attn_forward(const float *q, size_t q_bytes, const void *k,

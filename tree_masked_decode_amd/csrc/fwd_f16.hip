@@ -32,9 +32,10 @@
 // latency of HBM; no registers hold staged data.  One barrier per tile; a
 // tile's K copies go out right after it and its V and mask copies after the
 // scores, so that they drain behind the arithmetic rather than in a burst.
-// K and V are stored row-major with a 16-byte-chunk XOR swizzle (chunk c of
-// row r lives at c ^ (r & 15)): every lane of a copy picks the global chunk
-// that belongs at its LDS slot, and every operand read is bank-conflict free.
+// K and V are stored row-major with a 16-byte-chunk XOR swizzle (K: chunk c
+// of row r lives at c ^ (r & 15); V: at c ^ 2 (r & 15), for reads of chunk
+// pairs): every lane of a copy picks the global chunk that belongs at its LDS
+// slot, and the operand reads are free of bank conflicts.
 // V^T operands come from ds_read_b64_tr_b16, which transposes 4x16 blocks of
 // 16-bit values on the way out of LDS.
 //
@@ -101,6 +102,12 @@ template <int D, int RB, int MROWS, bool VEC, int W> struct F16Shape {
 };
 
 __device__ inline uint32_t swz(uint32_t row, uint32_t chunk) { return chunk ^ (row & 15u); }
+// V tiles use pairs of chunks: the transposing reads take 32 bytes (two
+// chunks) from each of four rows per 16 lanes, so rows are spread over chunk
+// pairs: chunk c of row r lives at c ^ (2 (r & 15)) (mod chunks per row).
+template <int CH> __device__ inline uint32_t swz_v(uint32_t row, uint32_t chunk) {
+  return chunk ^ ((2u * (row & 15u)) & (uint32_t)(CH - 1));
+}
 
 template <int D, int RB, int MROWS, bool VEC, int W>
 __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
@@ -160,12 +167,13 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   // K/V: copy i of this wavefront fills LDS chunks p = 64 (W_i) + lane of the
   // tile, W_i = wave * KV_PW + i; chunk p is row p / CH, physical chunk
   // p % CH, holding logical chunk (p % CH) ^ (row & 15).
-  uint32_t kv_row[S::KV_PW], kv_col[S::KV_PW];
+  uint32_t kv_row[S::KV_PW], kv_col[S::KV_PW], v_col[S::KV_PW];
 #pragma unroll
   for (int i = 0; i < S::KV_PW; ++i) {
     const uint32_t p = (wave * S::KV_PW + i) * 64u + lane;
     kv_row[i] = p / S::CH;
     kv_col[i] = 8u * swz(kv_row[i], p % S::CH);
+    v_col[i] = 8u * swz_v<S::CH>(kv_row[i], p % S::CH);
   }
   // mask: node rows of BN cells (128 bytes) back to back; a 16-byte copy
   // covers 8 rows (lane / 8, cells 4 (lane % 8) ..), a 4-byte copy 2 rows
@@ -195,12 +203,11 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
       // keys past kv_seq_len re-read the last valid row (never used)
       uint32_t key = key0 + kv_row[i];
       if (!full) key = min(key, L - 1u);
-      const size_t off = (size_t)key * D + kv_col[i];
       const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
       if (PART == 0)
-        dma_b128(K + off, la);
+        dma_b128(K + (size_t)key * D + kv_col[i], la);
       else
-        dma_b128(V + off, la + S::KV_BYTES);
+        dma_b128(V + (size_t)key * D + v_col[i], la + S::KV_BYTES);
     }
     if (PART == 1) {
 #pragma unroll
@@ -361,9 +368,9 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
         const uint32_t r0 = 4u * gp + (n >> 2), r1 = r0 + 16u;
         const uint32_t ch = 2u * db + ((n & 3u) >> 1), half_off = 4u * (n & 1u);
         lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4 *)(Vs + r0 * D + 8 * swz(r0, ch) + half_off));
+            (lds_short4 *)(Vs + r0 * D + 8 * swz_v<S::CH>(r0, ch) + half_off));
         hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4 *)(Vs + r1 * D + 8 * swz(r1, ch) + half_off));
+            (lds_short4 *)(Vs + r1 * D + 8 * swz_v<S::CH>(r1, ch) + half_off));
       }
       const half8_t vf = __builtin_bit_cast(half8_t,
           (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],

@@ -56,11 +56,12 @@ hipError_t launch_tree_mask(const MaskArgs &a, hipStream_t s) {
 // split; the row is sum_w O_w 2^(M_w - M*) / sum_w S_w 2^(M_w - M*), and an
 // empty row (no non-empty split) is 0.
 //
-// A block of 256 threads owns RPB rows.  Phase 1: wavefront v finds M* and
-// 1/S* of rows v, v+4, ... (lanes over splits) and leaves them in LDS.
-// Phase 2: TPR threads per row each own float4 columns of the row and walk the
-// splits in index order, eight independent loads at a time, so the sum does
-// not depend on timing and enough loads are in flight to cover latency.
+// One block of 256 threads per output row.  Phase 1: wavefront 0 finds M*
+// and 1/S* (lanes over splits).  Phase 2: thread (g, t) owns float4 columns
+// t, t + T, ... of the row and sums splits g, g + G, g + 2G, ... in index
+// order (G = 256 / T split groups, so every thread has few splits and all of
+// its loads are in flight together); the G group sums are then added in
+// group order through LDS.  The result does not depend on timing.
 // ---------------------------------------------------------------------------
 __device__ inline float wave_max(float x) {
 #pragma unroll
@@ -75,102 +76,118 @@ __device__ inline float wave_sum(float x) {
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-template <bool OUT_F16, uint32_t TPR>
+template <bool OUT_F16, uint32_t T, uint32_t C>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
-  constexpr uint32_t RPB = 256u / TPR;
-  constexpr uint32_t U = 8;
-  __shared__ float s_mstar[RPB], s_inv[RPB];
-  const uint32_t wv = threadIdx.x >> 6, lane = threadIdx.x & 63u;
+  // T threads per column set, C float4 columns per thread (dim = 4 T C at
+  // most), G split groups
+  constexpr uint32_t G = 256u / T;
+  __shared__ float s_mstar, s_inv;
+  __shared__ floatx4 s_part[G][T * C];
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const size_t nrows = a.nrows;
+  const size_t r = blockIdx.x;
   const float2_t *sm = reinterpret_cast<const float2_t *>(a.part_sm);  // (S, M)
-  const uint32_t row0 = blockIdx.x * RPB;
 
-  for (uint32_t rr = wv; rr < RPB; rr += 4u) {
-    const size_t r = row0 + rr;
+  if (tid < 64) {
     float mstar = -INFINITY, ssum = 0.0f;
-    if (r < nrows) {
+    for (uint32_t w = lane; w < a.nwg; w += 64u) {
+      const float2_t v = sm[(size_t)w * nrows + r];
+      if (v.x > 0.0f) mstar = fmaxf(mstar, v.y);
+    }
+    mstar = wave_max(mstar);
+    if (mstar != -INFINITY) {
       for (uint32_t w = lane; w < a.nwg; w += 64u) {
         const float2_t v = sm[(size_t)w * nrows + r];
-        if (v.x > 0.0f) mstar = fmaxf(mstar, v.y);
+        if (v.x > 0.0f) ssum += v.x * exp2f(v.y - mstar);
       }
-      mstar = wave_max(mstar);
-      if (mstar != -INFINITY) {
-        for (uint32_t w = lane; w < a.nwg; w += 64u) {
-          const float2_t v = sm[(size_t)w * nrows + r];
-          if (v.x > 0.0f) ssum += v.x * exp2f(v.y - mstar);
-        }
-      }
-      ssum = wave_sum(ssum);
     }
+    ssum = wave_sum(ssum);
     if (lane == 0) {
-      s_mstar[rr] = mstar;
-      s_inv[rr] = ssum > 0.0f ? 1.0f / ssum : 0.0f;
+      s_mstar = mstar;
+      s_inv = ssum > 0.0f ? 1.0f / ssum : 0.0f;
     }
   }
   __syncthreads();
-
-  const uint32_t rr = threadIdx.x / TPR, t = threadIdx.x % TPR;
-  const size_t r = row0 + rr;
-  if (r >= nrows) return;
-  const float mstar = s_mstar[rr], inv = s_inv[rr];
+  const float mstar = s_mstar, inv = s_inv;
+  const uint32_t g = tid / T, t = tid % T;
   const uint32_t d4n = a.dim / 4u;
   const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (uint32_t d4 = t; d4 < d4n; d4 += TPR) {
-    floatx4 acc = zero;
-    if (inv > 0.0f) {
-      const floatx4 *po = reinterpret_cast<const floatx4 *>(a.part_o) + r * d4n + d4;
-      const size_t wstride = nrows * d4n;
-      uint32_t w = 0;
-      for (; w + U <= a.nwg; w += U) {
-        floatx4 o[U];
-        float2_t v[U];
+  const floatx4 *po = reinterpret_cast<const floatx4 *>(a.part_o) + r * d4n;
+  const size_t wstride = nrows * d4n;
+  floatx4 acc[C];
 #pragma unroll
-        for (uint32_t j = 0; j < U; ++j) {
-          v[j] = sm[(size_t)(w + j) * nrows + r];
-          o[j] = po[(size_t)(w + j) * wstride];
-        }
+  for (uint32_t c = 0; c < C; ++c) acc[c] = zero;
+  if (inv > 0.0f) {
+    constexpr uint32_t U = 4;
+    uint32_t w = g;
+    for (; w + (U - 1) * G < a.nwg; w += U * G) {
+      float2_t v[U];
+      floatx4 o[U][C];
 #pragma unroll
-        for (uint32_t j = 0; j < U; ++j) {
-          // an empty split (S = 0) contributes nothing, whatever its O holds
-          const bool use = v[j].x > 0.0f;
-          const float f = use ? exp2f(v[j].y - mstar) : 0.0f;
-          acc += (use ? o[j] : zero) * f;
+      for (uint32_t j = 0; j < U; ++j) {
+        v[j] = sm[(size_t)(w + j * G) * nrows + r];
+#pragma unroll
+        for (uint32_t c = 0; c < C; ++c) {
+          const uint32_t d4 = t + c * T;
+          o[j][c] = d4 < d4n ? po[(size_t)(w + j * G) * wstride + d4] : zero;
         }
       }
-      for (; w < a.nwg; ++w) {
-        const float2_t v = sm[(size_t)w * nrows + r];
-        const floatx4 o = po[(size_t)w * wstride];
-        const bool use = v.x > 0.0f;
-        const float f = use ? exp2f(v.y - mstar) : 0.0f;
-        acc += (use ? o : zero) * f;
+#pragma unroll
+      for (uint32_t j = 0; j < U; ++j) {
+        // an empty split (S = 0) contributes nothing, whatever its O holds
+        const bool use = v[j].x > 0.0f;
+        const float f = use ? exp2f(v[j].y - mstar) : 0.0f;
+#pragma unroll
+        for (uint32_t c = 0; c < C; ++c) acc[c] += (use ? o[j][c] : zero) * f;
       }
     }
-    acc *= inv;
+    for (; w < a.nwg; w += G) {
+      const float2_t v = sm[(size_t)w * nrows + r];
+      const bool use = v.x > 0.0f;
+      const float f = use ? exp2f(v.y - mstar) : 0.0f;
+#pragma unroll
+      for (uint32_t c = 0; c < C; ++c) {
+        const uint32_t d4 = t + c * T;
+        const floatx4 o = d4 < d4n ? po[(size_t)w * wstride + d4] : zero;
+        acc[c] += (use ? o : zero) * f;
+      }
+    }
+  }
+#pragma unroll
+  for (uint32_t c = 0; c < C; ++c) s_part[g][t + c * T] = acc[c];
+  __syncthreads();
+  // group sums in group order; thread tid < T * C finishes column tid
+  for (uint32_t d4 = tid; d4 < d4n && d4 < T * C; d4 += 256u) {
+    floatx4 sum = s_part[0][d4];
+#pragma unroll
+    for (uint32_t gg = 1; gg < G; ++gg) sum += s_part[gg][d4];
+    sum *= inv;
     if (OUT_F16) {
-      half4_t h = {(half_t)acc[0], (half_t)acc[1], (half_t)acc[2], (half_t)acc[3]};
+      half4_t h = {(half_t)sum[0], (half_t)sum[1], (half_t)sum[2], (half_t)sum[3]};
       reinterpret_cast<half4_t *>(a.out)[r * d4n + d4] = h;
     } else {
-      reinterpret_cast<floatx4 *>(a.out)[r * d4n + d4] = acc;
+      reinterpret_cast<floatx4 *>(a.out)[r * d4n + d4] = sum;
     }
   }
 }
 
-template <uint32_t TPR>
+template <uint32_t T, uint32_t C>
 hipError_t launch_reduce_t(const ReduceArgs &a, hipStream_t s) {
-  constexpr uint32_t RPB = 256u / TPR;
-  dim3 grid((a.nrows + RPB - 1u) / RPB);
+  dim3 grid(a.nrows);
   if (a.out_f16)
-    hipLaunchKernelGGL((reduce_kernel<true, TPR>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((reduce_kernel<true, T, C>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((reduce_kernel<false, TPR>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((reduce_kernel<false, T, C>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+// dim <= 512 (checked by the caller): T C >= dim / 4
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s) {
   const uint32_t d4n = a.dim / 4u;
-  if (d4n >= 64u) return launch_reduce_t<64>(a, s);
-  if (d4n >= 32u) return launch_reduce_t<32>(a, s);
-  return launch_reduce_t<16>(a, s);
+  if (d4n > 64u) return launch_reduce_t<64, 2>(a, s);
+  if (d4n > 32u) return launch_reduce_t<64, 1>(a, s);
+  if (d4n > 16u) return launch_reduce_t<32, 1>(a, s);
+  return launch_reduce_t<16, 1>(a, s);
 }
 
 }  // namespace ta
