@@ -99,6 +99,25 @@ uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows);
 uint32_t f32_tile_keys(uint32_t head_dim);
 uint32_t quant_tile_keys(uint32_t dim);
 
+// Asynchronous global -> LDS copies: every lane moves 16 (or 4) bytes from its
+// own global address to lds + 16 * lane (4 * lane), `lds` being the
+// wavefront's LDS byte address (wave-uniform).  They are issued from inline
+// assembly so that the compiler adds no waits of its own; the kernels wait
+// with wait_vm<N>(), N = vector-memory operations the wavefront issued later
+// that may stay in flight (an undercount of those is never allowed; extra
+// later operations only make the wait stricter).
+__device__ inline void dma_b128(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ inline void dma_b32(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+template <int N> __device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // XCD-aware workgroup numbering.  MI355X hands consecutive workgroup ids to
 // its 8 XCDs in turn; every row tile of one (kv head, split) unit is placed
 // on the same XCD, in consecutive slots, so their shared K/V tiles meet in

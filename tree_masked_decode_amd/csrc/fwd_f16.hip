@@ -60,23 +60,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-// Asynchronous global -> LDS copies: every lane moves 16 (or 4) bytes from its
-// own global address to lds + 16 * lane (4 * lane), `lds` being the
-// wavefront's LDS byte address.  They are issued from inline assembly so that
-// the compiler adds no waits of its own; the kernel waits with wait_vm<N>(),
-// N = copies the wavefront issued later that may stay in flight.
-__device__ inline void dma_b128(const void *g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-__device__ inline void dma_b32(const void *g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-template <int N> __device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 constexpr int cmin(int x, int y) { return x < y ? x : y; }
 
 // MROWS: tree nodes a stage's mask tile holds (0 for the implicit causal

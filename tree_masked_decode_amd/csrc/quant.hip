@@ -20,6 +20,13 @@
 // keeps fp32-like precision); the bias terms are short per-row dot products
 // on the VALU.
 //
+// Memory pipeline: every tile of 32 keys -- K words, V words, the four
+// scale/bias slices and the mask cells of the workgroup's rows -- is copied
+// global -> LDS with coalesced global_load_lds instructions into a ring of NS
+// stages, NS - 1 tiles ahead; the workgroup is one wavefront, so waits are
+// its own vmcnt counts and no barrier is needed.  The arithmetic then reads
+// the tile from LDS.
+//
 // Codes become fp16 by OR-ing them into the mantissa of 1024.0 (0x6400) and
 // subtracting 1024 (exact).  K codes are read straight into MFMA operands
 // (a 32-bit word holds 8 or 4 consecutive dims of one token, and the order of
@@ -93,6 +100,30 @@ struct QShape {
   static constexpr int SBW = 4 * NG / 2;       // u32 words of 4 keys' scales
   static_assert(VCH >= 1, "tile too small");
   static_assert(RUN * 4 == GW, "lane runs must tile a group");
+  // LDS stage: K words, V words, K scales, K biases, V scales, V biases, mask
+  static constexpr int KT = BN * WPK * 4;              // bytes of a K (or V) tile
+  static constexpr int KT_I = KT / 1024;               // 16-byte-per-lane copies
+  static constexpr int SBB = BN * NG * 2;              // bytes of one scale/bias slice
+  static constexpr int SB_I = (SBB + 255) / 256;       // 4-byte-per-lane copies
+  static constexpr int SBP = (SBB + 15) / 16 * 16;     // padded slice
+  static constexpr int MB = 16 * BN * 2;               // mask cells of 16 rows
+  static constexpr int VL = WPK * RS * 4;              // V transpose area
+  static_assert(KT % 1024 == 0, "K tile copies");
+};
+
+// Mask modes: none (implicit causal), 16-byte copies (row starts and
+// kv_seq_len multiples of 8 cells), 4-byte copies (multiples of 2), or
+// per-lane register loads (any alignment).
+enum { kMaskNone = 0, kMaskB128 = 1, kMaskB32 = 2, kMaskReg = 3 };
+template <int DIM, int BITS, int G, int MM> struct QStage {
+  using S = QShape<DIM, BITS, G>;
+  static constexpr int MASK_I = MM == kMaskB128 ? 1 : MM == kMaskB32 ? 4 : 0;
+  static constexpr int HAS_M = (MM == kMaskB128 || MM == kMaskB32) ? 1 : 0;
+  static constexpr int BYTES = 2 * S::KT + 4 * S::SBP + HAS_M * S::MB;
+  static constexpr int PER_TILE = 2 * S::KT_I + 4 * S::SB_I + MASK_I;
+  static constexpr int NS = (3 * BYTES + S::VL <= 48 * 1024) ? 3 : 2;
+  static constexpr int LDS = NS * BYTES + S::VL;
+  static_assert(PER_TILE <= 63, "vmcnt range");
 };
 
 // Word index of (group g, step-in-group sub, part) for lane group gp.
@@ -102,11 +133,15 @@ __device__ inline uint32_t step_word(int g, int sub, uint32_t gp) {
   return (uint32_t)(g * S::GW) + gp * S::RUN + (uint32_t)(sub * S::WPS);
 }
 
-template <int DIM, int BITS, int G, bool IMPLICIT>
+template <int DIM, int BITS, int G, int MM>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   using S = QShape<DIM, BITS, G>;
-  constexpr int NG = S::NG, STEPS = S::STEPS, DB = S::DB;
-  __shared__ __attribute__((aligned(16))) uint32_t vlds[S::WPK * S::RS];
+  using ST = QStage<DIM, BITS, G, MM>;
+  constexpr bool IMPLICIT = MM == kMaskNone;
+  constexpr int NG = S::NG, STEPS = S::STEPS, DB = S::DB, NS = ST::NS;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) char *)lds);
+  uint32_t *vlds = reinterpret_cast<uint32_t *>(lds + NS * ST::BYTES);
 
   uint32_t unit, rt;
   decode_block(blockIdx.x, a.row_tiles, unit, rt);
@@ -168,45 +203,105 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     u32x4 vw[S::VCH];             // V words for the LDS transpose
     float m[2][4];                // mask cells (row n, keys 16kb+4gp+j)
   };
+  // ---- copies of tile t into stage (t - t0) % NS ----
+  // Keys past kv_seq_len re-read row L - 1 (or the word that holds it), so
+  // that nothing outside the buffers is read; they are excluded below.
+  const uint32_t t_first = [&] { uint32_t x0, x1; split_range(a.n_tiles, a.nwg, split, x0, x1); return x0; }();
+  auto stage_off = [&](uint32_t t) -> uint32_t { return ((t - t_first) % NS) * ST::BYTES; };
+  // mask row of the workgroup's row r (rows past the end reuse row 0)
+  auto mask_row = [&](uint32_t r) -> const half_t * {
+    uint32_t g2 = rt * 16u + r;
+    if (g2 >= a.rows) g2 = rt * 16u;
+    const uint32_t q2 = kv * a.repeat + g2 % a.repeat;
+    return a.mask + (size_t)q2 * a.mask_head_stride + (size_t)(g2 / a.repeat) * a.mask_stride;
+  };
+  auto issue = [&](uint32_t t) {
+    const uint32_t key0 = t * BN;
+    const uint32_t sb = lds0 + stage_off(t);
+#pragma unroll
+    for (int i = 0; i < S::KT_I; ++i) {
+      const uint32_t o = 1024u * i + 16u * lane;          // byte in the tile
+      uint32_t key = key0 + o / (4u * S::WPK);
+      if (key >= L) key = L - 1u;
+      const size_t go = (size_t)key * (4u * S::WPK) + o % (4u * S::WPK);
+      dma_b128(reinterpret_cast<const char *>(KP) + go, sb + 1024u * i);
+      dma_b128(reinterpret_cast<const char *>(VP) + go, sb + S::KT + 1024u * i);
+    }
+    const half_t *sarr[4] = {KS, KB, VS, VB};
+#pragma unroll
+    for (int arr = 0; arr < 4; ++arr)
+#pragma unroll
+      for (int i = 0; i < S::SB_I; ++i) {
+        const uint32_t o = 256u * i + 4u * lane;           // byte in the slice
+        if (o < (uint32_t)S::SBB) {
+          const uint32_t h = o / 2u;                        // first half of the word
+          uint32_t key = key0 + h / NG;
+          if (key >= L) key = NG == 1 ? ((L - 1u) & ~1u) : L - 1u;
+          dma_b32(sarr[arr] + (size_t)key * NG + h % NG,
+                  sb + 2u * S::KT + (uint32_t)arr * S::SBP + 256u * i);
+        }
+      }
+    if (MM == kMaskB128) {
+      // lane: row lane / 4, cells 8 (lane % 4) .. + 7
+      uint32_t key = key0 + 8u * (lane % 4u);
+      if (key >= L) key = L - 8u;
+      dma_b128(mask_row(lane / 4u) + key, sb + 2u * S::KT + 4u * S::SBP);
+    } else if (MM == kMaskB32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // lane: row 4i + lane / 16, cells 2 (lane % 16), + 1
+        uint32_t key = key0 + 2u * (lane % 16u);
+        if (key >= L) key = L - 2u;
+        dma_b32(mask_row(4u * i + lane / 16u) + key, sb + 2u * S::KT + 4u * S::SBP + 256u * i);
+      }
+    }
+  };
+  // wait until tile t has landed; `after` later tiles may stay in flight
+  auto wait_tile = [&](uint32_t after) {
+    if (NS >= 3 && after >= 1)
+      wait_vm<(NS >= 3 ? ST::PER_TILE : 0)>();
+    else
+      wait_vm<0>();
+  };
   auto load_tile = [&](uint32_t t, Tile &T) {
     const uint32_t key0 = t * BN;
+    const char *st = lds + stage_off(t);
+    const uint32_t *Kl = reinterpret_cast<const uint32_t *>(st);
+    const uint32_t *Vl = reinterpret_cast<const uint32_t *>(st + S::KT);
+    const uint32_t *SBl[4];
+#pragma unroll
+    for (int arr = 0; arr < 4; ++arr)
+      SBl[arr] = reinterpret_cast<const uint32_t *>(st + 2 * S::KT + arr * S::SBP);
+    const half_t *Ml = reinterpret_cast<const half_t *>(st + 2 * S::KT + 4 * S::SBP);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t key = key0 + 16u * kb + n;
+      const uint32_t kr = 16u * kb + n;   // key within the tile
 #pragma unroll
       for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int r = 0; r < S::RUN; ++r)
-          T.kw[kb][g][r] = key < L ? KP[(size_t)key * S::WPK + g * S::GW + gp * S::RUN + r] : 0u;
+          T.kw[kb][g][r] = Kl[kr * S::WPK + g * S::GW + gp * S::RUN + r];
       // scales/biases of keys 16kb + 4gp + 0..3 (K side) and
       // 16h + 4gp + 0..3 (V side, the keys of B-operand half h)
-      const uint32_t k4 = key0 + 16u * kb + 4u * gp;
+      const uint32_t k4 = 16u * kb + 4u * gp;
 #pragma unroll
       for (int w = 0; w < S::SBW; ++w) {
-        // word w holds halfs 2w and 2w+1 of the run; with one group per
-        // token these belong to two different tokens, each checked alone so
-        // that nothing past kv_seq_len is read or used.
-        const uint32_t key_lo = k4 + (uint32_t)(2 * w) / NG;
-        const uint32_t key_hi = k4 + (uint32_t)(2 * w + 1) / NG;
-        const bool in = key_lo < L;
-        const uint32_t keep = key_hi < L ? 0xffffffffu : 0x0000ffffu;
-        const uint32_t *ks32 = reinterpret_cast<const uint32_t *>(KS + (size_t)k4 * NG);
-        const uint32_t *kb32 = reinterpret_cast<const uint32_t *>(KB + (size_t)k4 * NG);
-        const uint32_t *vs32 = reinterpret_cast<const uint32_t *>(VS + (size_t)k4 * NG);
-        const uint32_t *vb32 = reinterpret_cast<const uint32_t *>(VB + (size_t)k4 * NG);
-        T.ksb[kb][0][w] = in ? (ks32[w] & keep) : 0u;
-        T.ksb[kb][1][w] = in ? (kb32[w] & keep) : 0u;
-        T.vsb[kb][0][w] = in ? (vs32[w] & keep) : 0u;
-        T.vsb[kb][1][w] = in ? (vb32[w] & keep) : 0u;
+        const uint32_t wi = (k4 * NG) / 2u + w;
+        T.ksb[kb][0][w] = SBl[0][wi];
+        T.ksb[kb][1][w] = SBl[1][wi];
+        T.vsb[kb][0][w] = SBl[2][wi];
+        T.vsb[kb][1][w] = SBl[3][wi];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t kk = k4 + j;
+        const uint32_t kk = key0 + k4 + j;
         float mv;
         if (IMPLICIT)
           mv = (valid && kk < L && (int64_t)kk <= causal_last) ? 0.0f : kMasked;
-        else
+        else if (MM == kMaskReg)
           mv = (valid && kk < L) ? (float)mrow[kk] : kMasked;
+        else
+          mv = (valid && kk < L) ? (float)Ml[n * BN + k4 + j] : kMasked;
         T.m[kb][j] = mv;
       }
     }
@@ -214,9 +309,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     for (int u = 0; u < S::VCH; ++u) {
       const uint32_t c = lane + kThreads * u;
       const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
-      T.vw[u] = (key0 + key < L)
-                    ? *reinterpret_cast<const u32x4 *>(VP + (size_t)(key0 + key) * S::WPK + 4 * q4)
-                    : u32x4{0u, 0u, 0u, 0u};
+      T.vw[u] = *reinterpret_cast<const u32x4 *>(Vl + key * S::WPK + 4 * q4);
     }
   };
   // V words -> LDS [word][position]; position of key (16h + 4g4 + j) is
@@ -345,28 +438,30 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     }
   };
 
-  // ---- main loop, next tile's loads in flight during the current one ----
+  // ---- main loop: tile t from LDS while tiles t + 1 .. t + NS - 1 land ----
   uint32_t t0, t1;
   split_range(a.n_tiles, a.nwg, split, t0, t1);
-  Tile cur, nxt;
-  if (t0 < t1) {
-    load_tile(t0, cur);
-    store_v(cur);
-  }
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (t0 + i < t1) issue(t0 + i);
+  Tile cur;
   for (uint32_t t = t0; t < t1; ++t) {
-    const bool has_next = t + 1 < t1;
-    if (has_next) load_tile(t + 1, nxt);
+    wait_tile(min(t1 - 1u - t, (uint32_t)(NS - 2)));
+    // the stage of tile t - 1 was read by the previous iteration; its reads
+    // have returned before the copies into it start
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t + NS - 1 < t1) issue(t + NS - 1);
+    load_tile(t, cur);
     int live = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) live |= (cur.m[kb][j] > kMasked);
-    if (__any(live)) compute(cur);
-    if (has_next) {
+    if (__any(live)) {
       __builtin_amdgcn_wave_barrier();
-      store_v(nxt);
+      store_v(cur);
       __builtin_amdgcn_wave_barrier();
-      cur = nxt;
+      compute(cur);
     }
   }
 
@@ -405,14 +500,28 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   }
 }
 
+template <int DIM, int BITS, int G, int MM>
+hipError_t launch_qm(const QuantArgs &a, hipStream_t s) {
+  using ST = QStage<DIM, BITS, G, MM>;
+  static const bool attr_set = [] {
+    (void)hipFuncSetAttribute((const void *)quant_kernel<DIM, BITS, G, MM>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    return true;
+  }();
+  (void)attr_set;
+  dim3 grid(grid_size(a.units, a.row_tiles));
+  hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, MM>), grid, dim3(kThreads), ST::LDS, s, a);
+  return hipGetLastError();
+}
+
 template <int DIM, int BITS, int G>
 hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
-  dim3 grid(grid_size(a.units, a.row_tiles));
-  if (a.mask == nullptr)
-    hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, true>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, false>), grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  if (a.mask == nullptr) return launch_qm<DIM, BITS, G, kMaskNone>(a, s);
+  const uint64_t all = a.mask_head_stride | a.mask_stride | a.kv_seq_len |
+                       (uint64_t)((uintptr_t)a.mask / sizeof(half_t));
+  if (all % 8 == 0) return launch_qm<DIM, BITS, G, kMaskB128>(a, s);
+  if (all % 2 == 0) return launch_qm<DIM, BITS, G, kMaskB32>(a, s);
+  return launch_qm<DIM, BITS, G, kMaskReg>(a, s);
 }
 
 template <int DIM, int BITS>
