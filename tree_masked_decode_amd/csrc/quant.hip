@@ -54,22 +54,38 @@ __device__ inline uint32_t codes_to_h2(uint32_t packed_pair) {
   const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
   return as_u(h - k1024);
 }
+// The same from an unmasked word: (x & m) | 0x64006400 is one v_and_or_b32
+// when the nibble/byte mask m sits in a register (it is kept out of the
+// compiler's sight so that it is not folded back into a second literal).
+__device__ inline uint32_t masked_codes_to_h2(uint32_t x, uint32_t m) {
+  half2_t h = as_h2((x & m) | 0x64006400u);
+  const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
+  return as_u(h - k1024);
+}
+template <int BITS> __device__ inline uint32_t code_pair_mask() {
+  uint32_t m;
+  if (BITS == 4)
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m));
+  else
+    asm volatile("v_mov_b32 %0, 0x00ff00ff" : "=v"(m));
+  return m;
+}
 
 // 8 slots of one MFMA step from the lane's words.  4-bit: one word, slots
 // [c0 c4 c1 c5 c2 c6 c3 c7].  8-bit: two words, slots [c0 c2 c1 c3] each.
 template <int BITS>
-__device__ inline half8_t word_codes(const uint32_t *w) {
+__device__ inline half8_t word_codes(const uint32_t *w, uint32_t m) {
   u32x4 r;
   if (BITS == 4) {
-    r[0] = codes_to_h2(w[0] & 0x000F000Fu);
-    r[1] = codes_to_h2((w[0] >> 4) & 0x000F000Fu);
-    r[2] = codes_to_h2((w[0] >> 8) & 0x000F000Fu);
-    r[3] = codes_to_h2((w[0] >> 12) & 0x000F000Fu);
+    r[0] = masked_codes_to_h2(w[0], m);
+    r[1] = masked_codes_to_h2(w[0] >> 4, m);
+    r[2] = masked_codes_to_h2(w[0] >> 8, m);
+    r[3] = masked_codes_to_h2(w[0] >> 12, m);
   } else {
-    r[0] = codes_to_h2(w[0] & 0x00FF00FFu);
-    r[1] = codes_to_h2((w[0] >> 8) & 0x00FF00FFu);
-    r[2] = codes_to_h2(w[1] & 0x00FF00FFu);
-    r[3] = codes_to_h2((w[1] >> 8) & 0x00FF00FFu);
+    r[0] = masked_codes_to_h2(w[0], m);
+    r[1] = masked_codes_to_h2(w[0] >> 8, m);
+    r[2] = masked_codes_to_h2(w[1], m);
+    r[3] = masked_codes_to_h2(w[1] >> 8, m);
   }
   return __builtin_bit_cast(half8_t, r);
 }
@@ -104,8 +120,11 @@ struct QShape {
   static constexpr int KT = BN * WPK * 4;              // bytes of a K (or V) tile
   static constexpr int KT_I = KT / 1024;               // 16-byte-per-lane copies
   static constexpr int SBB = BN * NG * 2;              // bytes of one scale/bias slice
-  static constexpr int SB_I = (SBB + 255) / 256;       // 4-byte-per-lane copies
-  static constexpr int SBP = (SBB + 15) / 16 * 16;     // padded slice
+  // the four slices back to back (4 SBB = 256 NG bytes) move in SB_I
+  // 4-byte-per-lane copies; lane l of copy i takes byte 256 i + 4 l of that
+  // region, i.e. slice (256 i + 4 l) / SBB
+  static constexpr int SB_I = 4 * SBB / 256;
+  static constexpr int SBP = SBB;
   static constexpr int MB = 16 * BN * 2;               // mask cells of 16 rows
   static constexpr int VL = WPK * RS * 4;              // V transpose area
   static_assert(KT % 1024 == 0, "K tile copies");
@@ -120,7 +139,7 @@ template <int DIM, int BITS, int G, int MM> struct QStage {
   static constexpr int MASK_I = MM == kMaskB128 ? 1 : MM == kMaskB32 ? 4 : 0;
   static constexpr int HAS_M = (MM == kMaskB128 || MM == kMaskB32) ? 1 : 0;
   static constexpr int BYTES = 2 * S::KT + 4 * S::SBP + HAS_M * S::MB;
-  static constexpr int PER_TILE = 2 * S::KT_I + 4 * S::SB_I + MASK_I;
+  static constexpr int PER_TILE = 2 * S::KT_I + S::SB_I + MASK_I;
   static constexpr int NS = (3 * BYTES + S::VL <= 48 * 1024) ? 3 : 2;
   static constexpr int LDS = NS * BYTES + S::VL;
   static_assert(PER_TILE <= 63, "vmcnt range");
@@ -215,37 +234,63 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     const uint32_t q2 = kv * a.repeat + g2 % a.repeat;
     return a.mask + (size_t)q2 * a.mask_head_stride + (size_t)(g2 / a.repeat) * a.mask_stride;
   };
+  // Per-lane source pointers of the copies: a tile's K words, V words and
+  // each scale/bias slice are contiguous in memory, so every copy of a full
+  // tile is the lane's pointer plus a wave-uniform tile offset.  A tile that
+  // reaches past kv_seq_len takes the clamped path instead.
+  const char *kp_l = reinterpret_cast<const char *>(KP) + 16u * lane;
+  const char *vp_l = reinterpret_cast<const char *>(VP) + 16u * lane;
+  const half_t *sarr[4] = {KS, KB, VS, VB};
+  const char *sb_l[S::SB_I];
+#pragma unroll
+  for (int i = 0; i < S::SB_I; ++i) {
+    const uint32_t o = 256u * i + 4u * lane;
+    sb_l[i] = reinterpret_cast<const char *>(sarr[o / S::SBB]) + o % S::SBB;
+  }
+  const half_t *mrow_l = nullptr;
+  if (MM == kMaskB128) mrow_l = mask_row(lane / 4u) + 8u * (lane % 4u);
   auto issue = [&](uint32_t t) {
     const uint32_t key0 = t * BN;
     const uint32_t sb = lds0 + stage_off(t);
+    if (key0 + BN <= L) {
+      const size_t kvo = (size_t)key0 * (4u * S::WPK);
 #pragma unroll
-    for (int i = 0; i < S::KT_I; ++i) {
-      const uint32_t o = 1024u * i + 16u * lane;          // byte in the tile
-      uint32_t key = key0 + o / (4u * S::WPK);
-      if (key >= L) key = L - 1u;
-      const size_t go = (size_t)key * (4u * S::WPK) + o % (4u * S::WPK);
-      dma_b128(reinterpret_cast<const char *>(KP) + go, sb + 1024u * i);
-      dma_b128(reinterpret_cast<const char *>(VP) + go, sb + S::KT + 1024u * i);
-    }
-    const half_t *sarr[4] = {KS, KB, VS, VB};
+      for (int i = 0; i < S::KT_I; ++i) {
+        dma_b128(kp_l + kvo + 1024u * i, sb + 1024u * i);
+        dma_b128(vp_l + kvo + 1024u * i, sb + S::KT + 1024u * i);
+      }
+      const size_t so = (size_t)key0 * (2u * NG);
 #pragma unroll
-    for (int arr = 0; arr < 4; ++arr)
+      for (int i = 0; i < S::SB_I; ++i) dma_b32(sb_l[i] + so, sb + 2u * S::KT + 256u * i);
+    } else {
+      // keys past kv_seq_len re-read row L - 1 (or the word that holds it)
+#pragma unroll
+      for (int i = 0; i < S::KT_I; ++i) {
+        const uint32_t o = 1024u * i + 16u * lane;
+        uint32_t key = key0 + o / (4u * S::WPK);
+        if (key >= L) key = L - 1u;
+        const size_t go = (size_t)key * (4u * S::WPK) + o % (4u * S::WPK);
+        dma_b128(reinterpret_cast<const char *>(KP) + go, sb + 1024u * i);
+        dma_b128(reinterpret_cast<const char *>(VP) + go, sb + S::KT + 1024u * i);
+      }
 #pragma unroll
       for (int i = 0; i < S::SB_I; ++i) {
-        const uint32_t o = 256u * i + 4u * lane;           // byte in the slice
-        if (o < (uint32_t)S::SBB) {
-          const uint32_t h = o / 2u;                        // first half of the word
-          uint32_t key = key0 + h / NG;
-          if (key >= L) key = NG == 1 ? ((L - 1u) & ~1u) : L - 1u;
-          dma_b32(sarr[arr] + (size_t)key * NG + h % NG,
-                  sb + 2u * S::KT + (uint32_t)arr * S::SBP + 256u * i);
-        }
+        const uint32_t o = 256u * i + 4u * lane;
+        const uint32_t h = (o % S::SBB) / 2u;               // first half of the word
+        uint32_t key = key0 + h / NG;
+        if (key >= L) key = NG == 1 ? ((L - 1u) & ~1u) : L - 1u;
+        dma_b32(sarr[o / S::SBB] + (size_t)key * NG + h % NG, sb + 2u * S::KT + 256u * i);
       }
+    }
     if (MM == kMaskB128) {
       // lane: row lane / 4, cells 8 (lane % 4) .. + 7
-      uint32_t key = key0 + 8u * (lane % 4u);
-      if (key >= L) key = L - 8u;
-      dma_b128(mask_row(lane / 4u) + key, sb + 2u * S::KT + 4u * S::SBP);
+      if (key0 + BN <= L) {
+        dma_b128(mrow_l + key0, sb + 2u * S::KT + 4u * S::SBP);
+      } else {
+        uint32_t key = key0 + 8u * (lane % 4u);
+        if (key >= L) key = L - 8u;
+        dma_b128(mask_row(lane / 4u) + key, sb + 2u * S::KT + 4u * S::SBP);
+      }
     } else if (MM == kMaskB32) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -296,12 +341,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       for (int j = 0; j < 4; ++j) {
         const uint32_t kk = key0 + k4 + j;
         float mv;
-        if (IMPLICIT)
+        if (IMPLICIT) {
           mv = (valid && kk < L && (int64_t)kk <= causal_last) ? 0.0f : kMasked;
-        else if (MM == kMaskReg)
+        } else if (MM == kMaskReg) {
           mv = (valid && kk < L) ? (float)mrow[kk] : kMasked;
-        else
-          mv = (valid && kk < L) ? (float)Ml[n * BN + k4 + j] : kMasked;
+        } else {
+          const float x = (float)Ml[n * BN + k4 + j];  // always in the stage
+          mv = (valid && kk < L) ? x : kMasked;
+        }
         T.m[kb][j] = mv;
       }
     }
@@ -341,6 +388,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 
   const uint32_t vshift = (BITS == 4) ? 4u * (n & 7u) : 8u * (n & 3u);
   const uint32_t vmask = (1u << BITS) - 1u;
+  const uint32_t cmask = code_pair_mask<BITS>();
 
   auto compute = [&](const Tile &T) {
     // scores, one accumulator per scale group
@@ -352,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
         sacc[g][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sub = 0; sub < S::SPG; ++sub) {
-          half8_t kf = word_codes<BITS>(&T.kw[kb][g][sub * S::WPS]);
+          half8_t kf = word_codes<BITS>(&T.kw[kb][g][sub * S::WPS], cmask);
           sacc[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[g * S::SPG + sub],
                                                                sacc[g][kb], 0, 0, 0);
         }
