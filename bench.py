@@ -122,8 +122,8 @@ def record_traffic(workload, fetch_csv, write_csv):
     FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by
     COPY_BYTES / (what the same counter reads for the calibration copy), so
     that a plain copy of known size counts exactly its size.  The forward
-    kernel is the dispatch whose name holds "fwd"/"quant_fwd"; its dispatches
-    are averaged."""
+    kernel is the dispatch whose name holds "fwd_" or "quant_kernel"; its
+    dispatches are averaged."""
     import csv
 
     def per_kernel(path, counter):
@@ -139,7 +139,7 @@ def record_traffic(workload, fetch_csv, write_csv):
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         acc = per_kernel(path, name)
         copy = [v for (k, _), v in acc.items() if "copy" in k.lower() or "elementwise" in k.lower()]
-        fwd = [v for (k, _), v in acc.items() if "fwd" in k]
+        fwd = [v for (k, _), v in acc.items() if "fwd_" in k or "quant_kernel" in k]
         if not copy or not fwd:
             raise SystemExit("record-traffic: no copy or forward dispatches in %s" % path)
         copy_kib = max(copy)  # the 256 MiB copies (other copies are small)
