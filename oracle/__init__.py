@@ -86,6 +86,12 @@ def _load():
                                                 U, U, U, U, U, ctypes.c_double,
                                                 P, U, P, ctypes.c_int]
             lib.orc_quant_attention.restype = ctypes.c_int
+            lib.orc_quant_attention_ex.argtypes = [P, P, P, P, P, P, P, P, P, P,
+                                                   ctypes.c_uint64, U, U, U, U,
+                                                   U, U, U, U, U, U, U,
+                                                   ctypes.c_double, P, U, P,
+                                                   ctypes.c_int]
+            lib.orc_quant_attention_ex.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -218,14 +224,18 @@ def lse_combine(o_un, s, m):
 
 def quant_attention(q, k_packed, k_scales, k_biases, v_packed, v_scales,
                     v_biases, *, n_kv_heads, kv_seq_len, bits, group_size, scale,
-                    sinks=None, mask=None, mask_head_stride=0, mask_stride=None,
-                    rows=None, nthreads=None):
+                    sinks=None, mask=None, mask_bool=None, mask_head_stride=0,
+                    mask_stride=None, window_size=0, rows=None, nthreads=None):
     """Affine-quantized K/V attention in double ("ffai/flash_quantized_sdpa.rs").
 
     q: [B*nQ, q_l, dim] float16.  k_packed: [B*nKV, cap, dim/(32/bits)] uint32.
     k_scales/k_biases: [B*nKV, cap, dim/G] float16.  V the same.
     sinks: [nQ] float32 or None.  mask: float16 array (flat), cell
     (q_idx, i, t) at q_idx*mask_head_stride + i*mask_stride + t, or None.
+    mask_bool: uint32 array with the same cell layout (0 drops the key), or
+    None; at most one of mask and mask_bool.  window_size: W > 0 keeps only
+    tokens t with t + W > kv_seq_len - 1 (the bool- and float-mask macros'
+    sliding-window gate); 0 keeps all.
     Returns [B*nQ, q_l, dim] float64 or [len(rows), dim] for (q_idx, i) rows.
     """
     q = _c(q, np.float16)
@@ -243,6 +253,8 @@ def quant_attention(q, k_packed, k_scales, k_biases, v_packed, v_scales,
         sinks = _c(sinks, np.float32)
     if mask is not None:
         mask = _c(mask, np.float16)
+    if mask_bool is not None:
+        mask_bool = _c(mask_bool, np.uint32)
     stride = kv_seq_len if mask_stride is None else int(mask_stride)
     if rows is None:
         sel, nsel = None, 0
@@ -252,12 +264,12 @@ def quant_attention(q, k_packed, k_scales, k_biases, v_packed, v_scales,
         nsel = sel.shape[0]
         out = np.empty((nsel, dim), dtype=np.float64)
     h = lambda a: None if a is None else a.view(np.uint16)
-    rc = _load().orc_quant_attention(
+    rc = _load().orc_quant_attention_ex(
         _ptr(h(q)), _ptr(k_packed), _ptr(h(k_scales)), _ptr(h(k_biases)),
         _ptr(v_packed), _ptr(h(v_scales)), _ptr(h(v_biases)), _ptr(sinks),
-        _ptr(h(mask)), int(mask_head_stride), stride, batch, nq, n_kv_heads, dim,
-        kv_seq_len, cap, q_l, bits, group_size, float(scale), _ptr(sel), nsel,
-        _ptr(out), _threads(nthreads))
+        _ptr(h(mask)), _ptr(mask_bool), int(mask_head_stride), stride,
+        int(window_size), batch, nq, n_kv_heads, dim, kv_seq_len, cap, q_l, bits,
+        group_size, float(scale), _ptr(sel), nsel, _ptr(out), _threads(nthreads))
     if rc != 0:
         raise OracleError("invalid quantized problem")
     return out

@@ -43,6 +43,14 @@
  *   R-Q Quantized-path mask cells obey R1 as well; when no mask is given
  *       the quantized path applies R8 (for q_l == 1 this attends every
  *       token, as [FQS] does with window_size 0).
+ *   R-B A bool mask holds one u32 per (query row, token): 0 drops the key,
+ *       any other value keeps it with no bias.  With a mask (float or bool)
+ *       the mask alone decides, as in [FQS] Mask variants and the
+ *       bool-mask macro.
+ *   R-W A window size W > 0 keeps token t only if t + W > kv_seq_len - 1,
+ *       i.e. the last W tokens, for every query row and every mask kind
+ *       ([FQS] base, bool- and float-mask macros: the causal / sliding
+ *       window gate with causal_upper = tokens - 1).  W = 0 keeps all.
  */
 #include <math.h>
 #include <pthread.h>
@@ -413,6 +421,8 @@ typedef struct {
     const uint16_t *vs, *vb;
     const float *sinks;
     const uint16_t *mask;
+    const uint32_t *mask_bool; /* R-B; at most one of mask, mask_bool */
+    uint32_t window;           /* R-W */
     uint64_t mask_head_stride;
     uint32_t mask_stride;
     uint32_t batch, nq, nkv, dim, kv_seq_len, kv_capacity, q_l, bits, group;
@@ -441,9 +451,11 @@ static double q_dequant(const uint32_t *packed, const uint16_t *scales,
 static double q_mask_cell(const orc_q_problem *p, uint32_t q_idx, uint32_t i,
                           uint32_t t)
 {
+    size_t cell = (size_t)q_idx * p->mask_head_stride + (size_t)i * p->mask_stride + t;
     if (p->mask)
-        return orc_f16_to_f64(p->mask[(size_t)q_idx * p->mask_head_stride +
-                                      (size_t)i * p->mask_stride + t]);
+        return orc_f16_to_f64(p->mask[cell]);
+    if (p->mask_bool)
+        return p->mask_bool[cell] != 0u ? 0.0 : ORC_MASKED; /* R-B */
     int64_t last = (int64_t)p->kv_seq_len - (int64_t)p->q_l + (int64_t)i;
     return ((int64_t)t <= last) ? 0.0 : ORC_MASKED;
 }
@@ -451,6 +463,9 @@ static double q_mask_cell(const orc_q_problem *p, uint32_t q_idx, uint32_t i,
 static int q_logit(const orc_q_problem *p, uint32_t q_idx, uint32_t i,
                    uint32_t t, double *logit)
 {
+    /* R-W: the window gate comes before the mask */
+    if (p->window > 0u && (uint64_t)t + p->window <= (uint64_t)p->kv_seq_len - 1u)
+        return 0;
     double m = q_mask_cell(p, q_idx, i, t);
     if (m <= ORC_MASKED)
         return 0;
@@ -508,10 +523,72 @@ static void q_row(void *vctx, uint32_t r)
 }
 
 /*
- * orc_quant_attention: out[r * dim + d]; sel == NULL means every row with
- * r = q_idx * q_l + i; otherwise sel holds nsel (q_idx, i) pairs.
- * Returns 0, or -1 on an invalid problem.
+ * orc_quant_attention_ex: out[r * dim + d]; sel == NULL means every row with
+ * r = q_idx * q_l + i; otherwise sel holds nsel (q_idx, i) pairs.  mask
+ * (f16 bits) and mask_bool (u32) share the cell layout; at most one may be
+ * given.  window: R-W.  Returns 0, or -1 on an invalid problem.
  */
+int orc_quant_attention_ex(const uint16_t *q, const uint32_t *k_packed,
+                           const uint16_t *k_scales, const uint16_t *k_biases,
+                           const uint32_t *v_packed, const uint16_t *v_scales,
+                           const uint16_t *v_biases, const float *sinks,
+                           const uint16_t *mask, const uint32_t *mask_bool,
+                           uint64_t mask_head_stride, uint32_t mask_stride,
+                           uint32_t window, uint32_t batch, uint32_t n_q_heads,
+                           uint32_t n_kv_heads, uint32_t dim, uint32_t kv_seq_len,
+                           uint32_t kv_capacity, uint32_t q_l, uint32_t bits,
+                           uint32_t group_size, double scale, const uint32_t *sel,
+                           uint32_t nsel, double *out, int nthreads)
+{
+    if (batch == 0 || n_q_heads == 0 || n_kv_heads == 0 ||
+        n_q_heads % n_kv_heads || dim == 0 || kv_seq_len == 0 ||
+        kv_capacity < kv_seq_len || q_l == 0)
+        return -1;
+    if (bits != 4 && bits != 8)
+        return -1;
+    if (group_size == 0 || dim % group_size || dim % (32u / bits))
+        return -1;
+    if (mask && mask_bool)
+        return -1;
+    if ((mask || mask_bool) && mask_stride < kv_seq_len)
+        return -1;
+    if (sel)
+        for (uint32_t r = 0; r < nsel; ++r)
+            if (sel[2 * r] >= batch * n_q_heads || sel[2 * r + 1] >= q_l)
+                return -1;
+    orc_q_problem p;
+    memset(&p, 0, sizeof p);
+    p.q = q;
+    p.kp = k_packed;
+    p.ks = k_scales;
+    p.kb = k_biases;
+    p.vp = v_packed;
+    p.vs = v_scales;
+    p.vb = v_biases;
+    p.sinks = sinks;
+    p.mask = mask;
+    p.mask_bool = mask_bool;
+    p.window = window;
+    p.mask_head_stride = mask_head_stride;
+    p.mask_stride = mask_stride;
+    p.batch = batch;
+    p.nq = n_q_heads;
+    p.nkv = n_kv_heads;
+    p.dim = dim;
+    p.kv_seq_len = kv_seq_len;
+    p.kv_capacity = kv_capacity;
+    p.q_l = q_l;
+    p.bits = bits;
+    p.group = group_size;
+    p.scale = scale;
+    p.sel = sel;
+    p.out = out;
+    uint32_t nrows = sel ? nsel : batch * n_q_heads * q_l;
+    orc_parallel(q_row, &p, nrows, nthreads);
+    return 0;
+}
+
+/* orc_quant_attention: the float-mask (or no-mask) form, no window. */
 int orc_quant_attention(const uint16_t *q, const uint32_t *k_packed,
                         const uint16_t *k_scales, const uint16_t *k_biases,
                         const uint32_t *v_packed, const uint16_t *v_scales,
@@ -523,44 +600,10 @@ int orc_quant_attention(const uint16_t *q, const uint32_t *k_packed,
                         uint32_t group_size, double scale, const uint32_t *sel,
                         uint32_t nsel, double *out, int nthreads)
 {
-    if (batch == 0 || n_q_heads == 0 || n_kv_heads == 0 ||
-        n_q_heads % n_kv_heads || dim == 0 || kv_seq_len == 0 ||
-        kv_capacity < kv_seq_len || q_l == 0)
-        return -1;
-    if (bits != 4 && bits != 8)
-        return -1;
-    if (group_size == 0 || dim % group_size || dim % (32u / bits))
-        return -1;
-    if (mask && mask_stride < kv_seq_len)
-        return -1;
-    if (sel)
-        for (uint32_t r = 0; r < nsel; ++r)
-            if (sel[2 * r] >= batch * n_q_heads || sel[2 * r + 1] >= q_l)
-                return -1;
-    orc_q_problem p = {q,
-                       k_packed,
-                       k_scales,
-                       k_biases,
-                       v_packed,
-                       v_scales,
-                       v_biases,
-                       sinks,
-                       mask,
-                       mask_head_stride,
-                       mask_stride,
-                       batch,
-                       n_q_heads,
-                       n_kv_heads,
-                       dim,
-                       kv_seq_len,
-                       kv_capacity,
-                       q_l,
-                       bits,
-                       group_size,
-                       scale,
-                       sel,
-                       out};
-    uint32_t nrows = sel ? nsel : batch * n_q_heads * q_l;
-    orc_parallel(q_row, &p, nrows, nthreads);
-    return 0;
+    return orc_quant_attention_ex(q, k_packed, k_scales, k_biases, v_packed,
+                                  v_scales, v_biases, sinks, mask, NULL,
+                                  mask_head_stride, mask_stride, 0u, batch,
+                                  n_q_heads, n_kv_heads, dim, kv_seq_len,
+                                  kv_capacity, q_l, bits, group_size, scale, sel,
+                                  nsel, out, nthreads);
 }

@@ -51,6 +51,14 @@ MUTATIONS = [
      "return (double)p->mask[(size_t)i * p->kv_seq_len + j];", 0),
     ("key_transposed", "size_t krow = ((size_t)hk * p->kv_capacity + j) * D;",
      "size_t krow = ((size_t)j * p->n_kv_heads + hk) * D;", 0),
+    ("window_off_by_one", "(uint64_t)t + p->window <= (uint64_t)p->kv_seq_len - 1u",
+     "(uint64_t)t + p->window < (uint64_t)p->kv_seq_len - 1u", 0),
+    ("window_from_start", "(uint64_t)t + p->window <= (uint64_t)p->kv_seq_len - 1u",
+     "(uint64_t)t >= p->window", 0),
+    ("bool_inverted", "return p->mask_bool[cell] != 0u ? 0.0 : ORC_MASKED;",
+     "return p->mask_bool[cell] == 0u ? 0.0 : ORC_MASKED;", 0),
+    ("bool_low_bit_only", "return p->mask_bool[cell] != 0u ? 0.0 : ORC_MASKED;",
+     "return (p->mask_bool[cell] & 1u) ? 0.0 : ORC_MASKED;", 0),
 ]
 
 

@@ -2,7 +2,9 @@
 
 Source: "ffai/flash_quantized_sdpa.rs" (metaltile-std 0.1.0) -- layout doc,
 base kernel macro (dequant x = scale_g * code + bias_g, GQA q_idx/repeat,
-sink initialisation, final o / l), float-mask macro (additive bias).
+sink initialisation, final o / l), float-mask macro (additive bias),
+bool-mask macro (a zero u32 drops the token) and the sliding-window gate
+(token t kept iff t + window > tokens - 1).
 """
 
 import os
@@ -15,19 +17,19 @@ from tree_masked_decode_amd import inputs
 
 
 def qcase(seed=0, B=2, nQ=4, nKV=2, dim=64, L=40, cap=None, q_l=1, bits=4, G=32,
-          sinks=False, mask=None):
+          sinks=False, mask=None, window=0):
     return inputs.quant_case(dict(batch=B, n_q_heads=nQ, n_kv_heads=nKV, dim=dim,
                                   kv_seq_len=L, kv_capacity=cap or L, q_l=q_l,
                                   bits=bits, group_size=G, sinks=sinks,
-                                  mask=mask), seed=seed)
+                                  mask=mask, window_size=window), seed=seed)
 
 
 def qrun(c, **kw):
     args = dict(n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
                 bits=c["bits"], group_size=c["group_size"], scale=c["scale"],
-                sinks=c["sinks"], mask=c["mask"],
+                sinks=c["sinks"], mask=c["mask"], mask_bool=c.get("mask_bool"),
                 mask_head_stride=c["mask_head_stride"],
-                mask_stride=c["mask_stride"])
+                mask_stride=c["mask_stride"], window_size=c.get("window_size", 0))
     args.update(kw)
     return oracle.quant_attention(c["q"], c["k_packed"], c["k_scales"],
                                   c["k_biases"], c["v_packed"], c["v_scales"],
@@ -113,11 +115,21 @@ def _brute_quant(c):
     rep = nQ // c["n_kv_heads"]
     L = c["kv_seq_len"]
     out = np.zeros((BnQ, q_l, dim))
+    W = c.get("window_size", 0)
+    keep = np.ones((q_l, L), dtype=bool)
+    if W:
+        keep &= (np.arange(L) + W > L - 1)[None, :]
     for qi in range(BnQ):
         kv = qi // rep
         z = c["scale"] * (c["q"][qi].astype(np.float64) @ K[kv, :L].T)
         if c["mask"] is not None:
             z = z + c["mask"].reshape(BnQ, q_l, -1)[qi, :, :L].astype(np.float64)
+        k = keep.copy()
+        if c.get("mask_bool") is not None:
+            k &= c["mask_bool"].reshape(BnQ, q_l, -1)[qi, :, :L] != 0
+        elif c["mask"] is None and q_l > 1:
+            k &= np.arange(L)[None, :] <= L - q_l + np.arange(q_l)[:, None]
+        z = np.where(k, z, -np.inf)
         cols = [z]
         vals = [V[kv, :L]]
         if c["sinks"] is not None:
@@ -125,8 +137,11 @@ def _brute_quant(c):
             vals.append(np.zeros((1, dim)))
         z = np.concatenate(cols, axis=1)
         Vx = np.concatenate(vals, axis=0)
-        w = np.exp(z - z.max(axis=1, keepdims=True))
-        out[qi] = (w @ Vx) / w.sum(axis=1, keepdims=True)
+        zmax = z.max(axis=1, keepdims=True)
+        live = np.isfinite(zmax[:, 0])
+        w = np.exp(z - np.where(np.isfinite(zmax), zmax, 0.0))
+        o = (w @ Vx) / np.where(live, w.sum(axis=1), 1.0)[:, None]
+        out[qi] = np.where(live[:, None], o, 0.0)   # no visible key: zeros
     return out
 
 
@@ -226,3 +241,86 @@ def test_quant_rows_selection_matches_full():
     sel = qrun(c, rows=rows)
     for r, (qi, i) in enumerate(rows):
         assert np.array_equal(sel[r], full[qi, i])
+
+
+# ---- bool mask and sliding window ----
+
+@pytest.mark.parametrize("bits,G,sinks,q_l,window", [
+    (4, 32, False, 1, 0), (4, 64, True, 2, 0), (8, 32, True, 1, 0),
+    (8, 16, False, 3, 0), (4, 32, True, 1, 21), (8, 64, False, 2, 7)])
+def test_bool_mask_matches_brute_force(bits, G, sinks, q_l, window):
+    c = qcase(11, B=2, nQ=4, nKV=2, dim=64, L=57, q_l=q_l, bits=bits, G=G,
+              sinks=sinks, mask="bool", window=window)
+    assert c["mask_bool"].dtype == np.uint32 and (c["mask_bool"] == 0).any()
+    np.testing.assert_allclose(qrun(c), _brute_quant(c), rtol=0, atol=1e-12)
+
+
+def test_bool_mask_only_zero_versus_nonzero_matters():
+    c = qcase(12, B=1, nQ=2, nKV=1, dim=32, L=33, q_l=2, bits=4, G=32,
+              sinks=True, mask="bool")
+    d = dict(c)
+    d["mask_bool"] = np.where(c["mask_bool"] != 0, np.uint32(1), np.uint32(0))
+    assert np.array_equal(qrun(c), qrun(d))
+
+
+def test_bool_mask_all_visible_equals_no_mask_at_q_l_1():
+    # q_l = 1: the implicit rule (no mask) attends every token
+    c = qcase(13, B=2, nQ=4, nKV=2, dim=64, L=40, bits=8, G=64, sinks=True,
+              mask="bool")
+    c["mask_bool"][:] = np.uint32(7)
+    assert np.array_equal(qrun(c), qrun(c, mask_bool=None))
+
+
+def test_bool_mask_equals_float_mask_of_zero_and_sentinel():
+    c = qcase(14, B=1, nQ=2, nKV=1, dim=32, L=29, q_l=2, bits=4, G=16,
+              mask="bool")
+    f = np.where(c["mask_bool"] != 0, 0.0, -65504.0).astype(np.float16)
+    assert np.array_equal(qrun(c), qrun(c, mask_bool=None, mask=f))
+
+
+def test_bool_mask_row_with_nothing_visible():
+    # R2: no visible key gives zeros; with a sink (value zero) also zeros
+    c = qcase(15, B=1, nQ=2, nKV=1, dim=32, L=20, bits=4, G=32, mask="bool")
+    c["mask_bool"][1] = 0
+    got = qrun(c)
+    assert np.array_equal(got[1], np.zeros_like(got[1]))
+    assert np.abs(got[0]).max() > 0
+    got_s = qrun(c, sinks=np.array([0.5, -0.25], dtype=np.float32))
+    assert np.array_equal(got_s[1], np.zeros_like(got_s[1]))
+
+
+def test_window_of_one_token_is_last_value_row():
+    # one visible token: softmax weight 1, so out = dequantised V[L - 1]
+    c = qcase(16, B=1, nQ=2, nKV=1, dim=64, L=23, bits=4, G=32, window=1)
+    got = qrun(c)
+    pf, G = 8, 32
+    w = c["v_packed"][0, 22]
+    sc = c["v_scales"][0, 22].astype(np.float64)
+    bi = c["v_biases"][0, 22].astype(np.float64)
+    expect = np.array([sc[d // G] * ((int(w[d // pf]) >> ((d % pf) * 4)) & 15) + bi[d // G]
+                       for d in range(64)])
+    for h in range(2):
+        assert np.array_equal(got[h, 0], expect)
+
+
+def test_window_equals_problem_cut_to_last_tokens():
+    # keeping the last W tokens is the same as a problem of W tokens that
+    # start at L - W (q_l = 1, no mask, with sinks)
+    L, W = 45, 13
+    c = qcase(17, B=2, nQ=4, nKV=2, dim=64, L=L, bits=8, G=32, sinks=True, window=W)
+    cut = dict(c)
+    for name in ("k_packed", "k_scales", "k_biases", "v_packed", "v_scales", "v_biases"):
+        cut[name] = np.ascontiguousarray(c[name][:, L - W:L])
+    cut["kv_seq_len"] = W
+    cut["window_size"] = 0
+    cut["mask_stride"] = W
+    np.testing.assert_allclose(qrun(c), qrun(cut), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(qrun(c), _brute_quant(c), rtol=0, atol=1e-12)
+
+
+def test_window_not_shorter_than_sequence_is_no_window():
+    c = qcase(18, B=1, nQ=2, nKV=1, dim=32, L=30, bits=4, G=32, sinks=True,
+              mask="alibi")
+    for W in (30, 31, 1000):
+        assert np.array_equal(qrun(c, window_size=W), qrun(c))
+    assert not np.array_equal(qrun(c, window_size=29), qrun(c))

@@ -51,6 +51,16 @@ QUANT_WORKLOADS = {
     "quant_4bit": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
                        kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=4,
                        group_size=64, sinks=True, mask="alibi", nwg=None),
+    # the bool-mask variant of the same decode: one u32 visibility word per
+    # (query, token), 75% visible
+    "quant_4bit_bool": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
+                            kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=4,
+                            group_size=64, sinks=True, mask="bool", nwg=None),
+    # sliding-window decode: only the last 4096 of 16384 tokens are attended
+    "quant_4bit_window": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
+                              kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=4,
+                              group_size=64, sinks=True, mask="alibi",
+                              window_size=4096, nwg=None),
 }
 
 
@@ -155,12 +165,26 @@ def alibi_bias(n_q_heads: int, batch: int, tokens: int, q_l: int = 1) -> np.ndar
     return out
 
 
+def bool_mask(rows: int, q_l: int, tokens: int, rng, density: float) -> np.ndarray:
+    """u32 visibility cells [rows, q_l, tokens]: each cell is visible with
+    probability `density`, and a visible cell holds an arbitrary non-zero
+    word (1, 0xFFFFFFFF, 0x80000000 or a random one), since only zero versus
+    non-zero is meaningful."""
+    vis = rng.random((rows, q_l, tokens)) < density
+    words = rng.integers(1, 1 << 32, size=(rows, q_l, tokens), dtype=np.uint64)
+    pick = rng.integers(0, 4, size=(rows, q_l, tokens))
+    words = np.where(pick == 0, 1, np.where(pick == 1, 0xFFFFFFFF,
+                                            np.where(pick == 2, 0x80000000, words)))
+    return np.where(vis, words, 0).astype(np.uint32)
+
+
 def quant_case(workload="quant_4bit", seed: int = 0, **overrides) -> dict:
     """Draw one affine-quantized problem (layouts of the quantized SDPA page).
 
     Returns q [B*nQ, q_l, dim] f16, k_packed/v_packed [B*nKV, cap, dim/pf]
     u32, k/v scales and biases [B*nKV, cap, dim/G] f16, sinks [nQ] f32 or
-    None, mask f16 [B*nQ, q_l, tokens] or None, and the shape parameters.
+    None, mask f16 [B*nQ, q_l, tokens] or None, mask_bool u32 [B*nQ, q_l,
+    tokens] or None (mask="bool"), window_size, and the shape parameters.
     """
     cfg = dict(QUANT_WORKLOADS[workload]) if isinstance(workload, str) else dict(workload)
     cfg.update(overrides)
@@ -190,12 +214,17 @@ def quant_case(workload="quant_4bit", seed: int = 0, **overrides) -> dict:
         if cfg.get("mask_stride") is None:
             cfg["mask_stride"] = L
         cfg["mask_head_stride"] = q_l * cfg["mask_stride"]
-    elif mode is None:
+    elif mode is None or mode == "bool":
         mask = None
         cfg["mask_stride"] = L
         cfg["mask_head_stride"] = 0
     else:
         mask = mode  # caller-supplied f16 array
-    cfg.update(q=q, sinks=sinks, mask=mask,
+    mask_bool = None
+    if mode == "bool":
+        mask_bool = bool_mask(B * nQ, q_l, L, rng, cfg.get("bool_density", 0.75))
+        cfg["mask_head_stride"] = q_l * L
+    cfg.setdefault("window_size", 0)
+    cfg.update(q=q, sinks=sinks, mask=mask, mask_bool=mask_bool,
                scale=float(cfg.get("scale") or 1.0 / math.sqrt(dim)), **out)
     return cfg
