@@ -75,10 +75,15 @@ def fp_alg(c):
 def quant_alg(c):
     B, nQ, nKV, dim = c["batch"], c["n_q_heads"], c["n_kv_heads"], c["dim"]
     L, q_l, bits, G = c["kv_seq_len"], c["q_l"], c["bits"], c["group_size"]
+    W = c.get("window_size", 0)
+    if W:
+        L = min(W, L)   # a sliding window reads only its last W tokens
     packed = 2 * B * nKV * L * dim * bits // 8
     sb = 4 * B * nKV * L * (dim // G) * 2
     qb = B * nQ * q_l * dim * 2
     mask = 0 if c["mask"] is None else B * nQ * q_l * L * 2
+    if c.get("mask_bool") is not None:
+        mask = B * nQ * q_l * L * 4
     sinks = 0 if c["sinks"] is None else nQ * 4
     out = B * nQ * q_l * dim * 2
     flops = 4 * (B * nQ * q_l) * L * dim
@@ -169,14 +174,18 @@ def cpu_baseline(name, c, alg, quant):
         nrows = c["q"].shape[0] * c["q"].shape[1]
         rows = [(r // c["q_l"], r % c["q_l"]) for r in range(0, nrows, max(1, nrows // 32))]
         mask = None if c["mask"] is None else np.ascontiguousarray(c["mask"]).ravel()
+        mb = c.get("mask_bool")
+        mb = None if mb is None else np.ascontiguousarray(mb).ravel()
         t = time.perf_counter()
         oracle.quant_attention(c["q"], c["k_packed"], c["k_scales"], c["k_biases"],
                                c["v_packed"], c["v_scales"], c["v_biases"],
                                n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
                                bits=c["bits"], group_size=c["group_size"],
                                scale=c["scale"], sinks=c["sinks"], mask=mask,
-                               mask_head_stride=c["mask_head_stride"],
-                               mask_stride=c["mask_stride"], rows=rows, nthreads=threads)
+                               mask_bool=mb, mask_head_stride=c["mask_head_stride"],
+                               mask_stride=c["mask_stride"],
+                               window_size=c.get("window_size", 0), rows=rows,
+                               nthreads=threads)
         dt = time.perf_counter() - t
     else:
         H, q_l = c["n_heads"], c["q_l"]
@@ -237,9 +246,15 @@ def main():
         base = {n: to_dev(c[n]) for n in names}
         base["sinks"] = None if c["sinks"] is None else to_dev(c["sinks"])
         base["mask"] = None if c["mask"] is None else to_dev(np.ascontiguousarray(c["mask"]).ravel())
+        mask_kind = 0 if c["mask"] is None else 1
+        if c.get("mask_bool") is not None:
+            base["mask"] = to_dev(np.ascontiguousarray(c["mask_bool"]).ravel().view(np.int32))
+            mask_kind = 2
+        window = c.get("window_size", 0)
         B, nQ, nKV, dim = c["batch"], c["n_q_heads"], c["n_kv_heads"], c["dim"]
         L, q_l = c["kv_seq_len"], c["q_l"]
-        nwg = args.nwg or ta.quant_pick_nwg(B, nQ, nKV, dim, L, q_l)
+        span = min(window, L) if window else L
+        nwg = args.nwg or ta.quant_pick_nwg(B, nQ, nKV, dim, span, q_l)
         nrows, D = B * nQ * q_l, dim
         out_dtype = torch.float16
     else:
@@ -269,14 +284,21 @@ def main():
     for cp in copies:
         if quant:
             kvb = (ctypes.c_size_t * 6)(*[nb(cp[n]) for n in names[1:]])
-            fargs = (vp(cp["q"]), 1, nb(cp["q"]), vp(cp["k_packed"]), vp(cp["k_scales"]),
-                     vp(cp["k_biases"]), vp(cp["v_packed"]), vp(cp["v_scales"]),
-                     vp(cp["v_biases"]), kvb, vp(cp["sinks"]), nb(cp["sinks"]),
-                     vp(cp["mask"]), nb(cp["mask"]), c["mask_head_stride"],
-                     c["mask_stride"], vp(P), nb(P), vp(O), nb(O), B, nQ, nKV, dim,
-                     L, c["kv_capacity"], q_l, c["bits"], c["group_size"], c["scale"],
-                     nwg, ctypes.c_void_p(sptr))
-            calls.append((lib.tree_attn_quant_forward, fargs))
+            head = (vp(cp["q"]), 1, nb(cp["q"]), vp(cp["k_packed"]), vp(cp["k_scales"]),
+                    vp(cp["k_biases"]), vp(cp["v_packed"]), vp(cp["v_scales"]),
+                    vp(cp["v_biases"]), kvb, vp(cp["sinks"]), nb(cp["sinks"]),
+                    vp(cp["mask"]))
+            tail = (vp(P), nb(P), vp(O), nb(O), B, nQ, nKV, dim, L, c["kv_capacity"],
+                    q_l, c["bits"], c["group_size"], c["scale"], nwg,
+                    ctypes.c_void_p(sptr))
+            if mask_kind == 2 or window:
+                fargs = head + (mask_kind, nb(cp["mask"]), c["mask_head_stride"],
+                                c["mask_stride"], window) + tail
+                calls.append((lib.tree_attn_quant_forward_ex, fargs))
+            else:
+                fargs = head + (nb(cp["mask"]), c["mask_head_stride"],
+                                c["mask_stride"]) + tail
+                calls.append((lib.tree_attn_quant_forward, fargs))
         else:
             fargs = (vp(cp["q"]), nb(cp["q"]), vp(cp["k"]), vp(cp["v"]),
                      1 if kind == "f16" else 0, nb(cp["k"]), vp(cp["mask"]), nb(cp["mask"]),

@@ -67,6 +67,11 @@ extern "C" {
 #define TA_MASKED (-65504.0f)
 #define TA_ATTENDED 0.0f
 
+/* Mask kinds of tree_attn_quant_forward_ex. */
+#define TA_MASK_NONE 0 /* no mask buffer: the implicit causal rule */
+#define TA_MASK_F16 1  /* additive fp16 bias ([FQS] float-mask macro) */
+#define TA_MASK_BOOL 2 /* u32 visibility words ([FQS] bool-mask macro) */
+
 /*
  * Bytes of the split-KV partial-result scratch for `nwg` splits:
  *   n_heads * q_l * nwg * (head_dim + 2) * 4, saturating at SIZE_MAX.
@@ -204,6 +209,42 @@ TA_API int tree_attn_quant_forward(
     uint32_t batch, uint32_t n_q_heads, uint32_t n_kv_heads, uint32_t dim,
     uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l, uint32_t bits,
     uint32_t group_size, float scale, uint32_t nwg, void *stream);
+
+/*
+ * tree_attn_quant_forward with the other mask kind and the sliding window of
+ * [FQS] (bool-mask macro; the causal / sliding-window gate of the base,
+ * bool- and float-mask macros).  Arguments as tree_attn_quant_forward, plus:
+ *
+ *   mask_kind    TA_MASK_NONE (mask must be NULL), TA_MASK_F16 (mask is the
+ *                fp16 additive bias described above) or TA_MASK_BOOL (mask
+ *                is DEVICE u32, same cell layout: a zero word drops token t
+ *                for that row, any other value keeps it with no bias).
+ *                The buffer must hold the last cell, (batch*n_q_heads - 1)
+ *                * mask_head_stride + (q_l - 1) * mask_stride + kv_seq_len
+ *                - 1, in elements of 2 (F16) or 4 (BOOL) bytes, and be
+ *                aligned to its element size.
+ *   window_size  0 keeps every token; W > 0 keeps token t only if
+ *                t + W > kv_seq_len - 1 (the last W tokens), for every row,
+ *                on top of the mask.  W >= kv_seq_len keeps every token.
+ *                Tokens before the window are not read at all, and a split
+ *                count from tree_attn_quant_pick_nwg(..., min(W, kv_seq_len),
+ *                ...) sizes the splits to the window.
+ *
+ * Errors as tree_attn_quant_forward, and TA_EINVAL for an unknown mask_kind
+ * or a mask pointer that does not match it (NULL iff TA_MASK_NONE).
+ * tree_attn_quant_forward(...) is this call with mask_kind = mask ?
+ * TA_MASK_F16 : TA_MASK_NONE and window_size = 0.
+ */
+TA_API int tree_attn_quant_forward_ex(
+    const void *q, int q_dtype, size_t q_bytes, const uint32_t *k_packed,
+    const void *k_scales, const void *k_biases, const uint32_t *v_packed,
+    const void *v_scales, const void *v_biases, const size_t kv_bytes[6],
+    const float *sinks, size_t sinks_bytes, const void *mask, int mask_kind,
+    size_t mask_bytes, uint64_t mask_head_stride, uint32_t mask_stride,
+    uint32_t window_size, float *partials, size_t partials_bytes, void *out,
+    size_t out_bytes, uint32_t batch, uint32_t n_q_heads, uint32_t n_kv_heads,
+    uint32_t dim, uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
+    uint32_t bits, uint32_t group_size, float scale, uint32_t nwg, void *stream);
 
 /*
  * Build the explicit tree mask on the device ([TA] header: chains, fixed

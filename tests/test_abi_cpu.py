@@ -224,6 +224,42 @@ def test_quant_validation(lib, kw, code, word):
     assert word in L.last_error()
 
 
+def qfx(lib, mask_kind=1, window=0, **kw):
+    p = dict(q=FAKE, q_dtype=1, q_bytes=BIG, kp=FAKE, ks=FAKE, kb=FAKE, vp=FAKE,
+             vs=FAKE, vb=FAKE, kv_bytes=[BIG] * 6, sinks=FAKE, sinks_bytes=BIG,
+             mask=FAKE, mask_bytes=BIG, mhs=16384, mask_stride=16384,
+             partials=FAKE, partials_bytes=BIG, out=FAKE, out_bytes=BIG,
+             batch=4, nq=32, nkv=8, dim=128, L=16384, cap=16384, q_l=1, bits=4,
+             G=64, scale=0.088, nwg=8)
+    p.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    kvb = (ctypes.c_size_t * 6)(*p["kv_bytes"])
+    return lib.tree_attn_quant_forward_ex(
+        vp(p["q"]), p["q_dtype"], p["q_bytes"], vp(p["kp"]), vp(p["ks"]),
+        vp(p["kb"]), vp(p["vp"]), vp(p["vs"]), vp(p["vb"]), kvb, vp(p["sinks"]),
+        p["sinks_bytes"], vp(p["mask"]), mask_kind, p["mask_bytes"], p["mhs"],
+        p["mask_stride"], window, vp(p["partials"]), p["partials_bytes"],
+        vp(p["out"]), p["out_bytes"], p["batch"], p["nq"], p["nkv"], p["dim"],
+        p["L"], p["cap"], p["q_l"], p["bits"], p["G"], p["scale"], p["nwg"], None)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(mask_kind=3), L.TA_EINVAL, "mask_kind"),
+    (dict(mask_kind=-1), L.TA_EINVAL, "mask_kind"),
+    (dict(mask_kind=2, mask=None), L.TA_EINVAL, "NULL exactly"),
+    (dict(mask_kind=0), L.TA_EINVAL, "NULL exactly"),
+    (dict(mask_kind=2, mask_bytes=(127 * 16384 + 16384) * 4 - 1), L.TA_ESIZE, "mask"),
+    (dict(mask_kind=1, mask_bytes=(127 * 16384 + 16384) * 2 - 1), L.TA_ESIZE, "mask"),
+    (dict(mask_kind=2, mask=FAKE + 2), L.TA_EINVAL, "aligned"),
+    (dict(mask_kind=2, mask_stride=100), L.TA_EINVAL, "mask_stride"),
+    (dict(mask_kind=2, window=5, bits=3), L.TA_EUNSUPPORTED, "bits"),
+])
+def test_quant_ex_validation(lib, kw, code, word):
+    assert qfx(lib, **kw) == code
+    assert word in L.last_error()
+
+
 def mk(lib, parents, q_l=None, L_=16, stride=16, mask=FAKE, nbytes=BIG):
     arr = (ctypes.c_int32 * max(1, len(parents)))(*parents)
     q_l = len(parents) if q_l is None else q_l

@@ -1,7 +1,8 @@
 """GPU parity of the affine-quantized K/V path against the oracle.
 
 "ffai/flash_quantized_sdpa.rs" (metaltile-std 0.1.0): 4/8-bit codes with
-per-group f16 scales and biases, optional sinks, optional additive f16 mask.
+per-group f16 scales and biases, optional sinks, optional additive f16 mask
+or u32 visibility mask (bool-mask macro), optional sliding window.
 Output is f16: each element must be within 2e-3 of the exact result plus
 half an fp16 ulp of it (the rounding the f16 output type itself imposes).
 """
@@ -27,10 +28,11 @@ def ta():
     return ta
 
 
-def qcase(seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, cap=None):
+def qcase(seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, cap=None, window=0):
     return inputs.quant_case(dict(batch=B, n_q_heads=nQ, n_kv_heads=nKV, dim=dim,
                                   kv_seq_len=L, kv_capacity=cap or (L + 5 + (L + 5) % 2), q_l=q_l,
-                                  bits=bits, group_size=G, sinks=sinks, mask=mask),
+                                  bits=bits, group_size=G, sinks=sinks, mask=mask,
+                                  window_size=window),
                              seed=seed)
 
 
@@ -40,13 +42,16 @@ def gpu_run(ta, c, nwg=None):
                                 "v_scales", "v_biases")}
     sinks = None if c["sinks"] is None else dev(c["sinks"])
     mask = None if c["mask"] is None else dev(np.ascontiguousarray(c["mask"]).ravel())
+    mb = c.get("mask_bool")
+    mb = None if mb is None else dev(np.ascontiguousarray(mb).ravel().view(np.int32))
     out = ta.quant_verify(t["q"], t["k_packed"], t["k_scales"], t["k_biases"],
                           t["v_packed"], t["v_scales"], t["v_biases"],
                           n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
                           bits=c["bits"], group_size=c["group_size"], scale=c["scale"],
-                          nwg=nwg, sinks=sinks, mask=mask,
+                          nwg=nwg, sinks=sinks, mask=mask, mask_bool=mb,
                           mask_head_stride=c["mask_head_stride"],
-                          mask_stride=c["mask_stride"])
+                          mask_stride=c["mask_stride"],
+                          window_size=c.get("window_size", 0))
     torch.cuda.synchronize()
     return host(out)
 
@@ -58,7 +63,9 @@ def ref_run(c, rows=None):
         kv_seq_len=c["kv_seq_len"], bits=c["bits"], group_size=c["group_size"],
         scale=c["scale"], sinks=c["sinks"],
         mask=None if c["mask"] is None else np.ascontiguousarray(c["mask"]).ravel(),
-        mask_head_stride=c["mask_head_stride"], mask_stride=c["mask_stride"], rows=rows)
+        mask_bool=None if c.get("mask_bool") is None else np.ascontiguousarray(c["mask_bool"]).ravel(),
+        mask_head_stride=c["mask_head_stride"], mask_stride=c["mask_stride"],
+        window_size=c.get("window_size", 0), rows=rows)
 
 
 SMALL = [
@@ -139,3 +146,86 @@ def test_quant_deterministic(ta):
     a = gpu_run(ta, c)
     b = gpu_run(ta, c)
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+# ---- u32 visibility mask and sliding window ----
+
+GATED = [
+    # seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, window, nwg
+    (20, 1, 4, 1, 128, 100, 1, 4, 64, False, "bool", 0, 1),
+    (21, 2, 8, 2, 128, 333, 1, 4, 64, True, "bool", 0, 3),
+    (22, 1, 4, 4, 64, 257, 1, 8, 32, True, "bool", 0, 2),
+    (23, 2, 6, 2, 256, 190, 1, 4, 128, False, "bool", 0, None),
+    (24, 1, 2, 1, 512, 97, 1, 8, 32, True, "bool", 0, 2),
+    (25, 3, 4, 1, 128, 77, 5, 4, 32, True, "bool", 0, 2),      # 20 rows: 2 row tiles
+    (26, 1, 2, 1, 64, 101, 2, 8, 64, False, "bool", 0, 9),     # splits past the tiles
+    (27, 1, 4, 1, 128, 500, 1, 4, 64, True, "alibi", 1, None),  # one token
+    (28, 1, 4, 1, 128, 500, 1, 4, 64, False, None, 31, 2),     # window inside one tile
+    (29, 1, 4, 1, 128, 500, 1, 8, 64, True, "bool", 33, 3),    # window crosses a tile edge
+    (30, 2, 4, 2, 64, 1000, 1, 4, 32, True, "alibi", 320, 4),  # window on tile edges
+    (31, 1, 2, 1, 256, 333, 3, 4, 64, False, "bool", 100, 2),
+    (32, 1, 4, 1, 128, 300, 1, 4, 64, True, "alibi", 299, 5),  # one token short of all
+    (33, 1, 4, 1, 128, 300, 1, 4, 64, True, None, 300, 5),     # window == L: no window
+    (34, 1, 4, 1, 128, 300, 1, 4, 64, True, "bool", 5000, 5),  # window > L
+    (35, 1, 2, 1, 512, 161, 2, 4, 128, True, None, 70, 3),
+]
+
+
+@pytest.mark.parametrize("seed,B,nQ,nKV,dim,L,q_l,bits,G,sinks,mask,window,nwg", GATED)
+def test_quant_gated_parity(ta, seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask,
+                            window, nwg):
+    note("quant gated seed=%d dim=%d L=%d q_l=%d bits=%d G=%d sinks=%s mask=%s W=%d nwg=%s"
+         % (seed, dim, L, q_l, bits, G, sinks, mask, window, nwg))
+    c = qcase(seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, window=window)
+    assert_close(gpu_run(ta, c, nwg), ref_run(c), TOL, "gated %d" % seed, f16_out=True)
+
+
+def test_quant_workload_bool(ta):
+    note("workload quant_4bit_bool (full)")
+    c = inputs.quant_case("quant_4bit_bool")
+    assert_close(gpu_run(ta, c), ref_run(c), TOL, "quant_4bit_bool", f16_out=True)
+
+
+def test_quant_workload_window(ta):
+    note("workload quant_4bit_window (full)")
+    c = inputs.quant_case("quant_4bit_window")
+    assert_close(gpu_run(ta, c), ref_run(c), TOL, "quant_4bit_window", f16_out=True)
+
+
+def test_quant_bool_edge_rows_and_tail_cells(ta):
+    note("quant bool mask: empty rows, high-bit words, garbage past kv_seq_len")
+    L, stride = 203, 256
+    c = qcase(36, 1, 4, 1, 128, L, 2, 4, 64, True, "bool")
+    mb = np.zeros((4, 2, stride), dtype=np.uint32)
+    mb[:, :, :L] = c["mask_bool"]
+    mb[:, :, L:] = 0xFFFFFFFF          # never read
+    mb[1, 0, :] = 0                    # nothing visible: zeros (the sink value is 0)
+    mb[2, 1, :L] = 0x80000000          # only the top bit set: visible
+    c["mask_bool"] = mb
+    c["mask_stride"] = stride
+    c["mask_head_stride"] = 2 * stride
+    got = gpu_run(ta, c, 3)
+    assert np.all(got[1, 0] == 0.0)
+    assert_close(got, ref_run(c), TOL, "bool edges", f16_out=True)
+
+
+def test_quant_ex_entry_matches_plain_entry(ta):
+    note("quant: forward_ex(F16, no window) is the plain entry, byte for byte")
+    import torch
+    c = qcase(37, 2, 8, 2, 128, 700, 1, 4, 64, True, "alibi")
+    t = {k: dev(c[k]) for k in ("q", "k_packed", "k_scales", "k_biases", "v_packed",
+                                "v_scales", "v_biases")}
+    mask = dev(np.ascontiguousarray(c["mask"]).ravel())
+    sinks = dev(c["sinks"])
+    args = (t["q"], t["k_packed"], t["k_scales"], t["k_biases"], t["v_packed"],
+            t["v_scales"], t["v_biases"])
+    kw = dict(n_kv_heads=2, kv_seq_len=700, bits=4, group_size=64, scale=c["scale"],
+              nwg=1, sinks=sinks, mask=mask, mask_head_stride=c["mask_head_stride"],
+              mask_stride=c["mask_stride"])
+    o1 = torch.empty((16, 1, 128), dtype=torch.float16, device="cuda")
+    o2 = torch.empty_like(o1)
+    ta.tree_attn_quant_forward(*args, out=o1, **kw)
+    ta.tree_attn_quant_forward_ex(*args, out=o2, mask_kind=ta.TA_MASK_F16,
+                                  window_size=0, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))

@@ -20,11 +20,15 @@ MASKED = -65504.0   # mask cell that excludes a key ("ops/tree_attention.rs")
 ATTENDED = 0.0
 TA_F32 = 0
 TA_F16 = 1
+TA_MASK_NONE = 0
+TA_MASK_F16 = 1
+TA_MASK_BOOL = 2
 
 __all__ = [
     "MASKED", "ATTENDED", "TreeAttnError", "partials_bytes", "pick_nwg",
     "quant_pick_nwg", "tree_attn_forward", "tree_attn_reduce",
-    "tree_attn_quant_forward", "build_tree_mask", "verify", "quant_verify",
+    "tree_attn_quant_forward", "tree_attn_quant_forward_ex", "build_tree_mask",
+    "verify", "quant_verify",
 ]
 
 
@@ -198,29 +202,77 @@ def tree_attn_quant_forward(q, k_packed, k_scales, k_biases, v_packed,
     _check(rc)
 
 
+def tree_attn_quant_forward_ex(q, k_packed, k_scales, k_biases, v_packed,
+                               v_scales, v_biases, *, n_kv_heads, kv_seq_len,
+                               bits, group_size, scale, nwg, sinks=None,
+                               mask=None, mask_kind=None, mask_head_stride=0,
+                               mask_stride=None, window_size=0, out=None,
+                               partials=None, stream=None):
+    """Quantized forward with a mask kind (TA_MASK_NONE / TA_MASK_F16 /
+    TA_MASK_BOOL; default: F16 for an f16 tensor, BOOL for a 4-byte integer
+    tensor) and a sliding window (0 = none)."""
+    bufs = (q, k_packed, k_scales, k_biases, v_packed, v_scales, v_biases,
+            sinks, mask, out, partials)
+    for t in bufs:
+        _dense(t, "buffer")
+    if mask_kind is None:
+        mask_kind = (TA_MASK_NONE if mask is None else
+                     TA_MASK_F16 if mask.is_floating_point() else TA_MASK_BOOL)
+    BnQ, q_l, dim = q.shape
+    BnKV, cap, _ = k_packed.shape
+    batch = BnKV // n_kv_heads
+    nq = BnQ // batch
+    kvb = (ctypes.c_size_t * 6)(*[_nbytes(t) for t in (
+        k_packed, k_scales, k_biases, v_packed, v_scales, v_biases)])
+    rc = _api().tree_attn_quant_forward_ex(
+        _ptr(q), TA_F16 if q.element_size() == 2 and q.is_floating_point() else -1,
+        _nbytes(q), _ptr(k_packed), _ptr(k_scales), _ptr(k_biases),
+        _ptr(v_packed), _ptr(v_scales), _ptr(v_biases), kvb, _ptr(sinks),
+        _nbytes(sinks), _ptr(mask), int(mask_kind), _nbytes(mask),
+        int(mask_head_stride), int(mask_stride or kv_seq_len), int(window_size),
+        _ptr(partials), _nbytes(partials), _ptr(out), _nbytes(out), batch, nq,
+        n_kv_heads, dim, kv_seq_len, cap, q_l, bits, group_size, float(scale), nwg,
+        _stream(stream))
+    _check(rc)
+
+
 def quant_verify(q, k_packed, k_scales, k_biases, v_packed, v_scales,
                  v_biases, *, n_kv_heads, kv_seq_len, bits, group_size, scale,
-                 nwg=None, sinks=None, mask=None, mask_head_stride=0,
-                 mask_stride=None, out=None, partials=None, stream=None):
-    """Quantized forward plus merge; returns ``out`` [B*nQ, q_l, dim] f16."""
+                 nwg=None, sinks=None, mask=None, mask_bool=None,
+                 mask_head_stride=0, mask_stride=None, window_size=0, out=None,
+                 partials=None, stream=None):
+    """Quantized forward plus merge; returns ``out`` [B*nQ, q_l, dim] f16.
+    ``mask`` is an f16 additive bias, ``mask_bool`` u32 visibility words
+    (at most one); ``window_size`` > 0 keeps the last window_size tokens."""
     import torch
     BnQ, q_l, dim = q.shape
     BnKV = k_packed.shape[0]
     batch = BnKV // n_kv_heads
+    if mask is not None and mask_bool is not None:
+        raise ValueError("quant_verify: give at most one of mask and mask_bool")
     if nwg is None:
-        nwg = quant_pick_nwg(batch, BnQ // batch, n_kv_heads, dim, kv_seq_len, q_l)
+        span = min(window_size, kv_seq_len) if window_size else kv_seq_len
+        nwg = quant_pick_nwg(batch, BnQ // batch, n_kv_heads, dim, span, q_l)
     if out is None:
         out = torch.empty((BnQ, q_l, dim), dtype=torch.float16, device=q.device)
     if nwg > 1 and partials is None:
         partials = torch.empty(partials_bytes(BnQ, dim, q_l, nwg) // 4,
                                dtype=torch.float32, device=q.device)
-    tree_attn_quant_forward(
-        q, k_packed, k_scales, k_biases, v_packed, v_scales, v_biases,
-        n_kv_heads=n_kv_heads, kv_seq_len=kv_seq_len, bits=bits,
-        group_size=group_size, scale=scale, nwg=nwg, sinks=sinks, mask=mask,
-        mask_head_stride=mask_head_stride, mask_stride=mask_stride,
-        out=out if nwg == 1 else None, partials=partials if nwg > 1 else None,
-        stream=stream)
+    common = dict(n_kv_heads=n_kv_heads, kv_seq_len=kv_seq_len, bits=bits,
+                  group_size=group_size, scale=scale, nwg=nwg, sinks=sinks,
+                  mask_head_stride=mask_head_stride, mask_stride=mask_stride,
+                  out=out if nwg == 1 else None,
+                  partials=partials if nwg > 1 else None, stream=stream)
+    if mask_bool is None and not window_size:
+        tree_attn_quant_forward(q, k_packed, k_scales, k_biases, v_packed,
+                                v_scales, v_biases, mask=mask, **common)
+    else:
+        m = mask_bool if mask_bool is not None else mask
+        kind = (TA_MASK_BOOL if mask_bool is not None else
+                TA_MASK_F16 if mask is not None else TA_MASK_NONE)
+        tree_attn_quant_forward_ex(q, k_packed, k_scales, k_biases, v_packed,
+                                   v_scales, v_biases, mask=m, mask_kind=kind,
+                                   window_size=window_size, **common)
     if nwg > 1:
         tree_attn_reduce(partials, out, nrows=BnQ * q_l, head_dim=dim, nwg=nwg,
                          stream=stream)

@@ -26,6 +26,9 @@ TA_EUNSUPPORTED = -4
 TA_EHIP = -5
 TA_F32 = 0
 TA_F16 = 1
+TA_MASK_NONE = 0
+TA_MASK_F16 = 1
+TA_MASK_BOOL = 2
 
 EXPORTS = (
     "tree_attn_partials_bytes",
@@ -34,6 +37,7 @@ EXPORTS = (
     "tree_attn_forward",
     "tree_attn_reduce",
     "tree_attn_quant_forward",
+    "tree_attn_quant_forward_ex",
     "build_tree_mask",
     "tree_attn_last_error",
 )
@@ -77,6 +81,10 @@ def load():
             P, I, Z, P, P, P, P, P, P, ctypes.POINTER(Z), P, Z, P, Z,
             ctypes.c_uint64, U, P, Z, P, Z, U, U, U, U, U, U, U, U, U, F, U, P]
         lib.tree_attn_quant_forward.restype = I
+        lib.tree_attn_quant_forward_ex.argtypes = [
+            P, I, Z, P, P, P, P, P, P, ctypes.POINTER(Z), P, Z, P, I, Z,
+            ctypes.c_uint64, U, U, P, Z, P, Z, U, U, U, U, U, U, U, U, U, F, U, P]
+        lib.tree_attn_quant_forward_ex.restype = I
         lib.build_tree_mask.argtypes = [P, U, U, U, P, Z, P]
         lib.build_tree_mask.restype = I
         lib.tree_attn_last_error.argtypes = []

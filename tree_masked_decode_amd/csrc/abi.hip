@@ -302,17 +302,22 @@ int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
   return hip_status(ta::launch_reduce(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-int tree_attn_quant_forward(
-    const void *q, int q_dtype, size_t q_bytes, const uint32_t *k_packed,
+static int quant_forward(
+    const char *fn, const void *q, int q_dtype, size_t q_bytes, const uint32_t *k_packed,
     const void *k_scales, const void *k_biases, const uint32_t *v_packed,
     const void *v_scales, const void *v_biases, const size_t kv_bytes[6],
-    const float *sinks, size_t sinks_bytes, const void *mask,
+    const float *sinks, size_t sinks_bytes, const void *mask, int mask_kind,
     size_t mask_bytes, uint64_t mask_head_stride, uint32_t mask_stride,
-    float *partials, size_t partials_bytes, void *out, size_t out_bytes,
-    uint32_t batch, uint32_t n_q_heads, uint32_t n_kv_heads, uint32_t dim,
-    uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l, uint32_t bits,
-    uint32_t group_size, float scale, uint32_t nwg, void *stream) {
-  const char *fn = "tree_attn_quant_forward";
+    uint32_t window_size, float *partials, size_t partials_bytes, void *out,
+    size_t out_bytes, uint32_t batch, uint32_t n_q_heads, uint32_t n_kv_heads,
+    uint32_t dim, uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
+    uint32_t bits, uint32_t group_size, float scale, uint32_t nwg, void *stream) {
+  if (mask_kind != TA_MASK_NONE && mask_kind != TA_MASK_F16 && mask_kind != TA_MASK_BOOL)
+    return fail(TA_EINVAL, "%s: mask_kind must be TA_MASK_NONE, TA_MASK_F16 or TA_MASK_BOOL",
+                fn);
+  if ((mask_kind == TA_MASK_NONE) != (mask == nullptr))
+    return fail(TA_EINVAL, "%s: mask must be NULL exactly when mask_kind is TA_MASK_NONE", fn);
+  const uint64_t cell_bytes = mask_kind == TA_MASK_BOOL ? 4 : 2;
   if (q_dtype != TA_F16)
     return fail(TA_EUNSUPPORTED, "%s: queries/scales/biases/out dtype must be TA_F16", fn);
   if (bits != 4 && bits != 8)
@@ -355,7 +360,7 @@ int tree_attn_quant_forward(
   for (const void *p : ptrs)
     if (!aligned16(p)) return fail(TA_EINVAL, "%s: device pointers must be 16-byte aligned", fn);
   if ((out && !aligned16(out)) || (partials && !aligned16(partials)) ||
-      (mask && ((uintptr_t)mask & 1u)) || (sinks && ((uintptr_t)sinks & 3u)))
+      (mask && ((uintptr_t)mask & (cell_bytes - 1))) || (sinks && ((uintptr_t)sinks & 3u)))
     return fail(TA_EINVAL, "%s: device pointers must be 16-byte aligned", fn);
 
   const uint64_t BnQ = (uint64_t)batch * n_q_heads, BnKV = (uint64_t)batch * n_kv_heads;
@@ -370,7 +375,7 @@ int tree_attn_quant_forward(
     // last cell: (BnQ-1)*mask_head_stride + (q_l-1)*mask_stride + (kv_seq_len-1)
     uint64_t t1, t2, t3;
     if (!mul_ok(BnQ - 1, mask_head_stride, t1) || !mul_ok(q_l - 1, mask_stride, t2) ||
-        !add_ok(t1, t2, t3) || !add_ok(t3, kv_seq_len, t3) || !mul_ok(t3, 2, req_mask))
+        !add_ok(t1, t2, t3) || !add_ok(t3, kv_seq_len, t3) || !mul_ok(t3, cell_bytes, req_mask))
       return fail(TA_EOVERFLOW, "%s: mask extent overflows", fn);
   }
   bool of = false;
@@ -411,7 +416,8 @@ int tree_attn_quant_forward(
   a.vs = static_cast<const ta::half_t *>(v_scales);
   a.vb = static_cast<const ta::half_t *>(v_biases);
   a.sinks = sinks;
-  a.mask = static_cast<const ta::half_t *>(mask);
+  a.mask = mask_kind == TA_MASK_F16 ? static_cast<const ta::half_t *>(mask) : nullptr;
+  a.mbool = mask_kind == TA_MASK_BOOL ? static_cast<const uint32_t *>(mask) : nullptr;
   a.out = static_cast<ta::half_t *>(out);
   a.mask_head_stride = mask ? mask_head_stride : 0;
   a.mask_stride = mask ? mask_stride : kv_seq_len;
@@ -426,6 +432,10 @@ int tree_attn_quant_forward(
   a.rows = (uint32_t)rows;
   a.row_tiles = ceil_div(a.rows, ta::kQuantRowsPerWG);
   a.n_tiles = ceil_div(kv_seq_len, ta::quant_tile_keys(dim));
+  // window: the last window_size tokens ("ffai/flash_quantized_sdpa.rs",
+  // token t is kept iff t + window_size > kv_seq_len - 1); 0 or a window
+  // at least as long as the sequence keeps every token
+  a.key_lo = (window_size > 0 && window_size < kv_seq_len) ? kv_seq_len - window_size : 0;
   uint64_t units = BnKV * nwg;
   uint64_t blocks = (uint64_t)ta::kXcds * ((units + ta::kXcds - 1) / ta::kXcds) * a.row_tiles;
   if (blocks > 0x7fffffffull)
@@ -441,6 +451,42 @@ int tree_attn_quant_forward(
   return hip_status(ta::launch_quant_forward(a, dim, bits, group_size,
                                              static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int tree_attn_quant_forward(
+    const void *q, int q_dtype, size_t q_bytes, const uint32_t *k_packed,
+    const void *k_scales, const void *k_biases, const uint32_t *v_packed,
+    const void *v_scales, const void *v_biases, const size_t kv_bytes[6],
+    const float *sinks, size_t sinks_bytes, const void *mask,
+    size_t mask_bytes, uint64_t mask_head_stride, uint32_t mask_stride,
+    float *partials, size_t partials_bytes, void *out, size_t out_bytes,
+    uint32_t batch, uint32_t n_q_heads, uint32_t n_kv_heads, uint32_t dim,
+    uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l, uint32_t bits,
+    uint32_t group_size, float scale, uint32_t nwg, void *stream) {
+  return quant_forward("tree_attn_quant_forward", q, q_dtype, q_bytes, k_packed, k_scales,
+                       k_biases, v_packed, v_scales, v_biases, kv_bytes, sinks, sinks_bytes,
+                       mask, mask ? TA_MASK_F16 : TA_MASK_NONE, mask_bytes, mask_head_stride,
+                       mask_stride, 0u, partials, partials_bytes, out, out_bytes, batch,
+                       n_q_heads, n_kv_heads, dim, kv_seq_len, kv_capacity, q_l, bits,
+                       group_size, scale, nwg, stream);
+}
+
+int tree_attn_quant_forward_ex(
+    const void *q, int q_dtype, size_t q_bytes, const uint32_t *k_packed,
+    const void *k_scales, const void *k_biases, const uint32_t *v_packed,
+    const void *v_scales, const void *v_biases, const size_t kv_bytes[6],
+    const float *sinks, size_t sinks_bytes, const void *mask, int mask_kind,
+    size_t mask_bytes, uint64_t mask_head_stride, uint32_t mask_stride,
+    uint32_t window_size, float *partials, size_t partials_bytes, void *out,
+    size_t out_bytes, uint32_t batch, uint32_t n_q_heads, uint32_t n_kv_heads,
+    uint32_t dim, uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
+    uint32_t bits, uint32_t group_size, float scale, uint32_t nwg, void *stream) {
+  return quant_forward("tree_attn_quant_forward_ex", q, q_dtype, q_bytes, k_packed,
+                       k_scales, k_biases, v_packed, v_scales, v_biases, kv_bytes, sinks,
+                       sinks_bytes, mask, mask_kind, mask_bytes, mask_head_stride, mask_stride,
+                       window_size, partials, partials_bytes, out, out_bytes, batch, n_q_heads,
+                       n_kv_heads, dim, kv_seq_len, kv_capacity, q_l, bits, group_size, scale,
+                       nwg, stream);
 }
 
 int build_tree_mask(const int32_t *parents, uint32_t q_l, uint32_t kv_seq_len,

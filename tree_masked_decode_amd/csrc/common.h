@@ -53,12 +53,14 @@ struct QuantArgs {
   const half_t *ks, *kb, *vs, *vb;  // [BnKV, cap, dim/G]
   const float *sinks;         // [nQ] or nullptr
   const half_t *mask;         // f16 additive or nullptr
+  const uint32_t *mbool;      // u32 visibility words or nullptr (never both)
   float *part_o, *part_sm;
   half_t *out;                // [BnQ, q_l, dim]
   uint64_t mask_head_stride;
   uint32_t mask_stride;
   uint32_t batch, nq, nkv, repeat, kv_seq_len, kv_capacity, q_l;
   uint32_t nwg, rows, row_tiles, n_tiles, units;
+  uint32_t key_lo;            // first token the sliding window keeps (0: all)
   float qscale;               // scale * log2(e)
 };
 

@@ -130,15 +130,18 @@ struct QShape {
   static_assert(KT % 1024 == 0, "K tile copies");
 };
 
-// Mask modes: none (implicit causal), 16-byte copies (row starts and
-// kv_seq_len multiples of 8 cells), 4-byte copies (multiples of 2), or
-// per-lane register loads (any alignment).
-enum { kMaskNone = 0, kMaskB128 = 1, kMaskB32 = 2, kMaskReg = 3 };
+// Mask modes: none (implicit causal); an fp16 additive mask in 16-byte
+// copies (row starts and kv_seq_len multiples of 8 cells), 4-byte copies
+// (multiples of 2) or per-lane register loads (any alignment); or a u32
+// visibility mask ("ffai/flash_quantized_sdpa.rs", bool-mask macro) in
+// 4-byte copies, two rows of 32 cells each.
+enum { kMaskNone = 0, kMaskB128 = 1, kMaskB32 = 2, kMaskReg = 3, kMaskBool = 4 };
 template <int DIM, int BITS, int G, int MM> struct QStage {
   using S = QShape<DIM, BITS, G>;
-  static constexpr int MASK_I = MM == kMaskB128 ? 1 : MM == kMaskB32 ? 4 : 0;
-  static constexpr int HAS_M = (MM == kMaskB128 || MM == kMaskB32) ? 1 : 0;
-  static constexpr int BYTES = 2 * S::KT + 4 * S::SBP + HAS_M * S::MB;
+  static constexpr int MASK_I = MM == kMaskB128 ? 1 : MM == kMaskB32 ? 4 : MM == kMaskBool ? 8 : 0;
+  static constexpr int M_BYTES = MM == kMaskBool ? 2 * S::MB
+                                 : (MM == kMaskB128 || MM == kMaskB32) ? S::MB : 0;
+  static constexpr int BYTES = 2 * S::KT + 4 * S::SBP + M_BYTES;
   static constexpr int PER_TILE = 2 * S::KT_I + S::SB_I + MASK_I;
   static constexpr int NS = (3 * BYTES + S::VL <= 48 * 1024) ? 3 : 2;
   static constexpr int LDS = NS * BYTES + S::VL;
@@ -208,11 +211,16 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   const uint32_t *VP = a.vp + kvrow0 * S::WPK;
   const half_t *KS = a.ks + kvrow0 * NG, *KB = a.kb + kvrow0 * NG;
   const half_t *VS = a.vs + kvrow0 * NG, *VB = a.vb + kvrow0 * NG;
-  const half_t *mrow = IMPLICIT ? nullptr
-                                : a.mask + (size_t)qidx * a.mask_head_stride +
-                                      (size_t)node * a.mask_stride;
+  const half_t *mrow = (MM == kMaskReg) ? a.mask + (size_t)qidx * a.mask_head_stride +
+                                                (size_t)node * a.mask_stride
+                                          : nullptr;
   const int64_t causal_last = (int64_t)a.kv_seq_len - (int64_t)a.q_l + (int64_t)node;
   const uint32_t L = a.kv_seq_len;
+  // sliding window ("ffai/flash_quantized_sdpa.rs" causal / sliding-window
+  // gate): tokens below key_lo are never attended; the splits cover the
+  // tiles from the one that holds key_lo
+  const uint32_t klo = a.key_lo;
+  const uint32_t tile_lo = klo / BN;
 
   // ---- per-tile registers ----
   struct Tile {
@@ -225,7 +233,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   // ---- copies of tile t into stage (t - t0) % NS ----
   // Keys past kv_seq_len re-read row L - 1 (or the word that holds it), so
   // that nothing outside the buffers is read; they are excluded below.
-  const uint32_t t_first = [&] { uint32_t x0, x1; split_range(a.n_tiles, a.nwg, split, x0, x1); return x0; }();
+  uint32_t t0, t1;
+  split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
+  t0 += tile_lo;
+  t1 += tile_lo;
+  const uint32_t t_first = t0;
   auto stage_off = [&](uint32_t t) -> uint32_t { return ((t - t_first) % NS) * ST::BYTES; };
   // mask row of the workgroup's row r (rows past the end reuse row 0)
   auto mask_row = [&](uint32_t r) -> const half_t * {
@@ -249,6 +261,17 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   }
   const half_t *mrow_l = nullptr;
   if (MM == kMaskB128) mrow_l = mask_row(lane / 4u) + 8u * (lane % 4u);
+  // bool mask: copy i moves rows 2i, 2i + 1 (lane / 32), cell lane % 32
+  const uint32_t *mb_l[MM == kMaskBool ? 8 : 1];
+  if (MM == kMaskBool) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t g2 = rt * 16u + 2u * i + lane / 32u;
+      if (g2 >= a.rows) g2 = rt * 16u;   // rows past the end reuse row 0
+      const uint32_t q2 = kv * a.repeat + g2 % a.repeat;
+      mb_l[i] = a.mbool + (size_t)q2 * a.mask_head_stride + (size_t)(g2 / a.repeat) * a.mask_stride;
+    }
+  }
   auto issue = [&](uint32_t t) {
     const uint32_t key0 = t * BN;
     const uint32_t sb = lds0 + stage_off(t);
@@ -299,6 +322,12 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
         if (key >= L) key = L - 2u;
         dma_b32(mask_row(4u * i + lane / 16u) + key, sb + 2u * S::KT + 4u * S::SBP + 256u * i);
       }
+    } else if (MM == kMaskBool) {
+      // past kv_seq_len: re-read cell L - 1 of the row (never used)
+      const uint32_t cell = min(key0 + lane % 32u, L - 1u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma_b32(mb_l[i] + cell, sb + 2u * S::KT + 4u * S::SBP + 256u * i);
     }
   };
   // wait until tile t has landed; `after` later tiles may stay in flight
@@ -318,6 +347,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     for (int arr = 0; arr < 4; ++arr)
       SBl[arr] = reinterpret_cast<const uint32_t *>(st + 2 * S::KT + arr * S::SBP);
     const half_t *Ml = reinterpret_cast<const half_t *>(st + 2 * S::KT + 4 * S::SBP);
+    const uint32_t *Mb = reinterpret_cast<const uint32_t *>(st + 2 * S::KT + 4 * S::SBP);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint32_t kr = 16u * kb + n;   // key within the tile
@@ -341,13 +371,16 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       for (int j = 0; j < 4; ++j) {
         const uint32_t kk = key0 + k4 + j;
         float mv;
+        const bool in = valid && kk < L && kk >= klo;
         if (IMPLICIT) {
-          mv = (valid && kk < L && (int64_t)kk <= causal_last) ? 0.0f : kMasked;
+          mv = (in && (int64_t)kk <= causal_last) ? 0.0f : kMasked;
         } else if (MM == kMaskReg) {
-          mv = (valid && kk < L) ? (float)mrow[kk] : kMasked;
+          mv = in ? (float)mrow[kk] : kMasked;
+        } else if (MM == kMaskBool) {
+          mv = (in && Mb[n * BN + k4 + j] != 0u) ? 0.0f : kMasked;
         } else {
           const float x = (float)Ml[n * BN + k4 + j];  // always in the stage
-          mv = (valid && kk < L) ? x : kMasked;
+          mv = in ? x : kMasked;
         }
         T.m[kb][j] = mv;
       }
@@ -487,8 +520,6 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   };
 
   // ---- main loop: tile t from LDS while tiles t + 1 .. t + NS - 1 land ----
-  uint32_t t0, t1;
-  split_range(a.n_tiles, a.nwg, split, t0, t1);
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
     if (t0 + i < t1) issue(t0 + i);
@@ -564,6 +595,7 @@ hipError_t launch_qm(const QuantArgs &a, hipStream_t s) {
 
 template <int DIM, int BITS, int G>
 hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
+  if (a.mbool != nullptr) return launch_qm<DIM, BITS, G, kMaskBool>(a, s);
   if (a.mask == nullptr) return launch_qm<DIM, BITS, G, kMaskNone>(a, s);
   const uint64_t all = a.mask_head_stride | a.mask_stride | a.kv_seq_len |
                        (uint64_t)((uintptr_t)a.mask / sizeof(half_t));
