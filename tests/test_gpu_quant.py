@@ -192,9 +192,10 @@ def test_quant_workload_window(ta):
     assert_close(gpu_run(ta, c), ref_run(c), TOL, "quant_4bit_window", f16_out=True)
 
 
-def test_quant_bool_edge_rows_and_tail_cells(ta):
-    note("quant bool mask: empty rows, high-bit words, garbage past kv_seq_len")
-    L, stride = 203, 256
+@pytest.mark.parametrize("L", [203, 204])   # 4-byte and 16-byte mask copies
+def test_quant_bool_edge_rows_and_tail_cells(ta, L):
+    note("quant bool mask: empty rows, high-bit words, garbage past kv_seq_len, L=%d" % L)
+    stride = 256
     c = qcase(36, 1, 4, 1, 128, L, 2, 4, 64, True, "bool")
     mb = np.zeros((4, 2, stride), dtype=np.uint32)
     mb[:, :, :L] = c["mask_bool"]

@@ -144,7 +144,7 @@ uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
   const uint64_t kv = 2ull * batch * n_kv_heads * kv_seq_len * dim / 2;
   const uint64_t part = (uint64_t)batch * n_q_heads * q_l * (dim + 2) * 4;
   return pick_splits(batch * n_kv_heads, ceil_div(rows, ta::kQuantRowsPerWG),
-                     ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, 8u, 8u, kv, part);
+                     ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, 8u, 2u, kv, part);
 }
 
 int tree_attn_forward(const float *q, size_t q_bytes, const void *k,

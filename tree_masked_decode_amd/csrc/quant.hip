@@ -134,18 +134,24 @@ struct QShape {
 // copies (row starts and kv_seq_len multiples of 8 cells), 4-byte copies
 // (multiples of 2) or per-lane register loads (any alignment); or a u32
 // visibility mask ("ffai/flash_quantized_sdpa.rs", bool-mask macro) in
-// 4-byte copies, two rows of 32 cells each.
-enum { kMaskNone = 0, kMaskB128 = 1, kMaskB32 = 2, kMaskReg = 3, kMaskBool = 4 };
+// 16-byte copies of eight rows (row starts and kv_seq_len multiples of 4
+// cells) or 4-byte copies of two rows (any layout).
+enum { kMaskNone = 0, kMaskB128 = 1, kMaskB32 = 2, kMaskReg = 3, kMaskBool = 4,
+       kMaskBoolB128 = 5 };
 template <int DIM, int BITS, int G, int MM> struct QStage {
   using S = QShape<DIM, BITS, G>;
-  static constexpr int MASK_I = MM == kMaskB128 ? 1 : MM == kMaskB32 ? 4 : MM == kMaskBool ? 8 : 0;
-  static constexpr int M_BYTES = MM == kMaskBool ? 2 * S::MB
+  static constexpr int MASK_I = MM == kMaskB128 ? 1 : MM == kMaskB32 ? 4
+                               : MM == kMaskBool ? 8 : MM == kMaskBoolB128 ? 2 : 0;
+  static constexpr int M_BYTES = (MM == kMaskBool || MM == kMaskBoolB128) ? 2 * S::MB
                                  : (MM == kMaskB128 || MM == kMaskB32) ? S::MB : 0;
   static constexpr int BYTES = 2 * S::KT + 4 * S::SBP + M_BYTES;
   static constexpr int PER_TILE = 2 * S::KT_I + S::SB_I + MASK_I;
-  static constexpr int NS = (3 * BYTES + S::VL <= 48 * 1024) ? 3 : 2;
+  // Eight one-wavefront workgroups share a CU at dim <= 128 (two per SIMD),
+  // so a workgroup keeps within 20 KB of LDS there; wider heads run fewer.
+  static constexpr int BUDGET = DIM <= 128 ? 20 * 1024 : 48 * 1024;
+  static constexpr int NS = (3 * BYTES + S::VL <= BUDGET) ? 3 : 2;
   static constexpr int LDS = NS * BYTES + S::VL;
-  static_assert(PER_TILE <= 63, "vmcnt range");
+  static_assert(PER_TILE * (NS - 1) <= 63, "vmcnt range");
 };
 
 // Word index of (group g, step-in-group sub, part) for lane group gp.
@@ -262,11 +268,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   const half_t *mrow_l = nullptr;
   if (MM == kMaskB128) mrow_l = mask_row(lane / 4u) + 8u * (lane % 4u);
   // bool mask: copy i moves rows 2i, 2i + 1 (lane / 32), cell lane % 32
-  const uint32_t *mb_l[MM == kMaskBool ? 8 : 1];
-  if (MM == kMaskBool) {
+  // (4-byte copies) or rows 8i .. 8i + 7 (lane / 8), cells 4 (lane % 8) ..
+  // + 3 (16-byte copies)
+  constexpr int MB_N = MM == kMaskBool ? 8 : MM == kMaskBoolB128 ? 2 : 1;
+  const uint32_t *mb_l[MB_N];
+  if (MM == kMaskBool || MM == kMaskBoolB128) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t g2 = rt * 16u + 2u * i + lane / 32u;
+    for (int i = 0; i < MB_N; ++i) {
+      uint32_t g2 = rt * 16u + (MM == kMaskBool ? 2u * i + lane / 32u : 8u * i + lane / 8u);
       if (g2 >= a.rows) g2 = rt * 16u;   // rows past the end reuse row 0
       const uint32_t q2 = kv * a.repeat + g2 % a.repeat;
       mb_l[i] = a.mbool + (size_t)q2 * a.mask_head_stride + (size_t)(g2 / a.repeat) * a.mask_stride;
@@ -328,12 +337,22 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         dma_b32(mb_l[i] + cell, sb + 2u * S::KT + 4u * S::SBP + 256u * i);
+    } else if (MM == kMaskBoolB128) {
+      // past kv_seq_len (a multiple of 4): re-read cells L - 4 .. L - 1
+      uint32_t cell = key0 + 4u * (lane % 8u);
+      if (cell >= L) cell = L - 4u;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma_b128(mb_l[i] + cell, sb + 2u * S::KT + 4u * S::SBP + 1024u * i);
     }
   };
-  // wait until tile t has landed; `after` later tiles may stay in flight
+  // wait until tile t has landed; `after` later tiles (0 .. NS - 1) may
+  // stay in flight
   auto wait_tile = [&](uint32_t after) {
-    if (NS >= 3 && after >= 1)
-      wait_vm<(NS >= 3 ? ST::PER_TILE : 0)>();
+    if (NS >= 3 && after >= 2)
+      wait_vm<(NS >= 3 ? 2 * ST::PER_TILE : 0)>();
+    else if (after >= 1)
+      wait_vm<ST::PER_TILE>();
     else
       wait_vm<0>();
   };
@@ -376,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
           mv = (in && (int64_t)kk <= causal_last) ? 0.0f : kMasked;
         } else if (MM == kMaskReg) {
           mv = in ? (float)mrow[kk] : kMasked;
-        } else if (MM == kMaskBool) {
+        } else if (MM == kMaskBool || MM == kMaskBoolB128) {
           mv = (in && Mb[n * BN + k4 + j] != 0u) ? 0.0f : kMasked;
         } else {
           const float x = (float)Ml[n * BN + k4 + j];  // always in the stage
@@ -519,18 +538,20 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     }
   };
 
-  // ---- main loop: tile t from LDS while tiles t + 1 .. t + NS - 1 land ----
+  // ---- main loop: tile t from LDS while tiles t + 1 .. t + NS land ----
+  // A tile's stage is copied whole into registers (load_tile), so the copies
+  // of tile t + NS go into tile t's own stage as soon as those reads have
+  // returned: NS tiles stay in flight behind the arithmetic.
 #pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
+  for (int i = 0; i < NS; ++i)
     if (t0 + i < t1) issue(t0 + i);
   Tile cur;
   for (uint32_t t = t0; t < t1; ++t) {
-    wait_tile(min(t1 - 1u - t, (uint32_t)(NS - 2)));
-    // the stage of tile t - 1 was read by the previous iteration; its reads
-    // have returned before the copies into it start
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (t + NS - 1 < t1) issue(t + NS - 1);
+    wait_tile(min(t1 - 1u - t, (uint32_t)(NS - 1)));
     load_tile(t, cur);
+    // the reads of tile t's stage have returned before copies refill it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t + NS < t1) issue(t + NS);
     int live = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -595,7 +616,12 @@ hipError_t launch_qm(const QuantArgs &a, hipStream_t s) {
 
 template <int DIM, int BITS, int G>
 hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
-  if (a.mbool != nullptr) return launch_qm<DIM, BITS, G, kMaskBool>(a, s);
+  if (a.mbool != nullptr) {
+    const uint64_t words = a.mask_head_stride | a.mask_stride | a.kv_seq_len |
+                           (uint64_t)((uintptr_t)a.mbool / sizeof(uint32_t));
+    if (words % 4 == 0) return launch_qm<DIM, BITS, G, kMaskBoolB128>(a, s);
+    return launch_qm<DIM, BITS, G, kMaskBool>(a, s);
+  }
   if (a.mask == nullptr) return launch_qm<DIM, BITS, G, kMaskNone>(a, s);
   const uint64_t all = a.mask_head_stride | a.mask_stride | a.kv_seq_len |
                        (uint64_t)((uintptr_t)a.mask / sizeof(half_t));
