@@ -74,6 +74,10 @@ def _load():
                                           U, U, U, ctypes.c_double, P, U, P,
                                           ctypes.c_int]
             lib.orc_attention.restype = ctypes.c_int
+            lib.orc_attention_ex.argtypes = [P, P, P, ctypes.c_int, P, U, U, U, U,
+                                             U, U, U, ctypes.c_double, U, P, U, P,
+                                             ctypes.c_int]
+            lib.orc_attention_ex.restype = ctypes.c_int
             lib.orc_attention_partials.argtypes = [P, P, P, ctypes.c_int, P, U,
                                                    U, U, U, U, U, U,
                                                    ctypes.c_double, P, U, P, P,
@@ -137,11 +141,13 @@ def tree_mask(parents, kv_seq_len: int, mask_stride: int | None = None):
 
 
 def attention(q, k, v, mask, *, n_kv_heads, kv_seq_len, scale, mask_stride=None,
-              rows=None, nthreads=None):
+              window_start=0, rows=None, nthreads=None):
     """fp-path attention in double ("tree_attention.metal", impl; reading R1/R2).
 
     q: [n_heads, q_l, D] float32.  k, v: [n_kv_heads, kv_capacity, D], float32
-    or float16.  mask: [q_l, mask_stride] float32 or None (implicit causal).
+    or float16.  mask: [q_l, mask_stride] float32 or None (implicit causal;
+    with window_start, row i sees keys window_start .. kv_seq_len - q_l + i,
+    the "tree_attention.metal" header's implicit causal / sliding-window rule).
     Returns [q_l, n_heads, D] float64, or [len(rows), D] when ``rows`` is a
     list of (node i, head h) pairs.
     """
@@ -166,9 +172,10 @@ def attention(q, k, v, mask, *, n_kv_heads, kv_seq_len, scale, mask_stride=None,
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.uint32).reshape(-1, 2))
         nsel = sel.shape[0]
         out = np.empty((nsel, D), dtype=np.float64)
-    rc = _load().orc_attention(_ptr(q), _ptr(k), _ptr(v), kv_f16, _ptr(mask), H,
-                               Hk, D, kv_seq_len, cap, q_l, stride, float(scale),
-                               _ptr(sel), nsel, _ptr(out), _threads(nthreads))
+    rc = _load().orc_attention_ex(_ptr(q), _ptr(k), _ptr(v), kv_f16, _ptr(mask), H,
+                                  Hk, D, kv_seq_len, cap, q_l, stride, float(scale),
+                                  int(window_start), _ptr(sel), nsel, _ptr(out),
+                                  _threads(nthreads))
     if rc != 0:
         raise OracleError("invalid attention problem")
     return out

@@ -34,6 +34,10 @@
  *   R8  With no mask buffer the implicit causal rule applies: row i sees
  *       key j iff j <= kv_seq_len - q_l + i.  ([TA] header, flash_attn_vec
  *       implicit mask.)
+ *   R8W The implicit rule with a sliding-window start: row i sees key j iff
+ *       window_start <= j <= kv_seq_len - q_l + i, one window_start for
+ *       every row, as the [TA] header states the byte-identity contract
+ *       (0.0f for k_pos in [window_start, abs_pos]).  window_start = 0 is R8.
  *   R12 A sink is one extra virtual key per query head with raw logit
  *       sinks[h] (no scale, no mask) and a zero value.  ([FQS] base macro,
  *       accumulator initialisation.)
@@ -133,6 +137,7 @@ typedef struct {
     uint32_t n_heads, n_kv_heads, head_dim, kv_seq_len, kv_capacity, q_l,
         mask_stride;
     double scale;
+    uint32_t window_start; /* R8W; implicit rule only */
 } orc_fp_problem;
 
 static double kv_elem(const void *base, int is_f16, size_t idx)
@@ -148,7 +153,7 @@ static double fp_mask_cell(const orc_fp_problem *p, uint32_t i, uint32_t j)
     if (p->mask)
         return (double)p->mask[(size_t)i * p->mask_stride + j];
     int64_t last = (int64_t)p->kv_seq_len - (int64_t)p->q_l + (int64_t)i;
-    return ((int64_t)j <= last) ? 0.0 : ORC_MASKED;
+    return (j >= p->window_start && (int64_t)j <= last) ? 0.0 : ORC_MASKED;
 }
 
 /* Logit of key j for (node i, head h); returns 0 if the key is excluded. */
@@ -289,19 +294,21 @@ static void fp_full_row(void *vctx, uint32_t r)
  * layout of [OPS].  Otherwise sel holds nsel (i, h) pairs.
  * Returns 0, or -1 on an invalid problem.
  */
-int orc_attention(const float *q, const void *k, const void *v, int kv_f16,
-                  const float *mask, uint32_t n_heads, uint32_t n_kv_heads,
-                  uint32_t head_dim, uint32_t kv_seq_len, uint32_t kv_capacity,
-                  uint32_t q_l, uint32_t mask_stride, double scale,
-                  const uint32_t *sel, uint32_t nsel, double *out,
-                  int nthreads)
+int orc_attention_ex(const float *q, const void *k, const void *v, int kv_f16,
+                     const float *mask, uint32_t n_heads, uint32_t n_kv_heads,
+                     uint32_t head_dim, uint32_t kv_seq_len, uint32_t kv_capacity,
+                     uint32_t q_l, uint32_t mask_stride, double scale,
+                     uint32_t window_start, const uint32_t *sel, uint32_t nsel,
+                     double *out, int nthreads)
 {
     orc_fp_problem p = {q,          k,          v,        kv_f16,
                         mask,       n_heads,    n_kv_heads, head_dim,
                         kv_seq_len, kv_capacity, q_l,      mask_stride,
-                        scale};
+                        scale,      window_start};
     if (!fp_problem_ok(&p))
         return -1;
+    if (mask && window_start)
+        return -1; /* a mask buffer encodes all visibility ([TA] header) */
     if (sel)
         for (uint32_t r = 0; r < nsel; ++r)
             if (sel[2 * r] >= q_l || sel[2 * r + 1] >= n_heads)
@@ -310,6 +317,19 @@ int orc_attention(const float *q, const void *k, const void *v, int kv_f16,
     uint32_t nrows = sel ? nsel : n_heads * q_l;
     orc_parallel(fp_full_row, &c, nrows, nthreads);
     return 0;
+}
+
+/* orc_attention: orc_attention_ex with window_start = 0. */
+int orc_attention(const float *q, const void *k, const void *v, int kv_f16,
+                  const float *mask, uint32_t n_heads, uint32_t n_kv_heads,
+                  uint32_t head_dim, uint32_t kv_seq_len, uint32_t kv_capacity,
+                  uint32_t q_l, uint32_t mask_stride, double scale,
+                  const uint32_t *sel, uint32_t nsel, double *out,
+                  int nthreads)
+{
+    return orc_attention_ex(q, k, v, kv_f16, mask, n_heads, n_kv_heads, head_dim,
+                            kv_seq_len, kv_capacity, q_l, mask_stride, scale, 0u,
+                            sel, nsel, out, nthreads);
 }
 
 /* ---- split-KV partials and their log-sum-exp combine --------------------- */

@@ -277,3 +277,51 @@ def test_merge_of_hand_partials():
     z = oracle.lse_combine(np.zeros((1, 2, 2)), np.zeros((1, 2)),
                            np.full((1, 2), -np.inf))
     assert np.all(z == 0.0)
+
+
+# ---- implicit causal rule with a sliding-window start (R8W) ----
+
+def windowed(q_l, L, ws, stride=None):
+    """The explicit mask the "tree_attention.metal" header pairs with the
+    implicit rule: 0 on [window_start, abs_pos], -65504 elsewhere."""
+    stride = stride or L
+    i = np.arange(q_l)[:, None]
+    j = np.arange(stride)[None, :]
+    return np.where((j >= ws) & (j <= L - q_l + i), 0.0, MASKED).astype(np.float32)
+
+
+@pytest.mark.parametrize("L,q_l,ws,kvd", [(37, 5, 0, "f32"), (37, 5, 10, "f16"),
+                                          (64, 3, 31, "f32"), (100, 8, 92, "f16")])
+def test_window_start_matches_brute_force(L, q_l, ws, kvd):
+    c = small(21, H=4, Hk=2, D=128, L=L, q_l=q_l, kv_dtype=kvd)
+    got = run(c, None, window_start=ws)
+    ref = brute(c["q"], c["k"], c["v"], windowed(q_l, L, ws), 2, L, c["scale"])
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_window_start_equals_explicit_window_mask_exactly():
+    c = small(22, H=4, Hk=1, D=128, L=50, q_l=4)
+    for ws in (0, 1, 17, 46):
+        assert np.array_equal(run(c, None, window_start=ws),
+                              run(c, windowed(4, 50, ws)))
+
+
+def test_window_start_zero_is_plain_implicit():
+    c = small(23, H=2, Hk=2, D=128, L=33, q_l=6)
+    assert np.array_equal(run(c, None, window_start=0), run(c, None))
+
+
+def test_window_start_at_last_row_position_is_one_value():
+    # the last node sees exactly one key when window_start = abs_pos = L - 1
+    L, q_l = 40, 3
+    c = small(24, H=2, Hk=1, D=128, L=L, q_l=q_l)
+    got = run(c, None, window_start=L - 1)
+    np.testing.assert_array_equal(got[q_l - 1, 0], c["v"][0, L - 1].astype(np.float64))
+    # earlier nodes' abs_pos < window_start: nothing visible, zeros (R2)
+    assert np.array_equal(got[: q_l - 1], np.zeros_like(got[: q_l - 1]))
+
+
+def test_window_start_with_mask_is_rejected():
+    c = small(25, H=2, Hk=1, D=128, L=20, q_l=2)
+    with pytest.raises(oracle.OracleError):
+        run(c, causal(2, 20), window_start=3)

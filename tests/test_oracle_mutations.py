@@ -27,8 +27,8 @@ MUTATIONS = [
      "if (m < ORC_MASKED)\n        return 0;\n    uint32_t D", 0),
     ("gqa_modulo", "uint32_t hk = h / (p->n_heads / p->n_kv_heads); /* GQA",
      "uint32_t hk = h % p->n_kv_heads; /* GQA", 0),
-    ("causal_off_by_one", "return ((int64_t)j <= last) ? 0.0 : ORC_MASKED;",
-     "return ((int64_t)j < last) ? 0.0 : ORC_MASKED;", 0),
+    ("causal_off_by_one", "(int64_t)j <= last) ? 0.0 : ORC_MASKED;",
+     "(int64_t)j < last) ? 0.0 : ORC_MASKED;", 0),
     ("head_major_output", "i = r / p->n_heads; /* out row",
      "i = r % p->q_l; h = r / p->q_l; if (0) /* out row", 0),
     ("no_normalisation", "o[d] = (s > 0.0) ? o[d] / s : 0.0; /* R2 */",
@@ -55,6 +55,10 @@ MUTATIONS = [
      "(uint64_t)t + p->window < (uint64_t)p->kv_seq_len - 1u", 0),
     ("window_from_start", "(uint64_t)t + p->window <= (uint64_t)p->kv_seq_len - 1u",
      "(uint64_t)t >= p->window", 0),
+    ("window_start_exclusive", "return (j >= p->window_start && (int64_t)j <= last)",
+     "return (j > p->window_start && (int64_t)j <= last)", 0),
+    ("window_start_ignored", "return (j >= p->window_start && (int64_t)j <= last)",
+     "return ((int64_t)j <= last)", 0),
     ("bool_inverted", "return p->mask_bool[cell] != 0u ? 0.0 : ORC_MASKED;",
      "return p->mask_bool[cell] == 0u ? 0.0 : ORC_MASKED;", 0),
     ("bool_low_bit_only", "return p->mask_bool[cell] != 0u ? 0.0 : ORC_MASKED;",
