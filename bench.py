@@ -64,9 +64,13 @@ def fp_alg(c):
     H, Hk, D = c["n_heads"], c["n_kv_heads"], c["head_dim"]
     L, q_l = c["kv_seq_len"], c["q_l"]
     esz = 2 if c["kv_dtype"] == "f16" else 4
+    ws = c.get("window_start")
+    mask = q_l * L * 4
+    if ws is not None:   # decode: no mask buffer, keys from window_start on
+        L -= ws
+        mask = 0
     kv = 2 * Hk * L * D * esz
     qb = H * q_l * D * 4
-    mask = q_l * L * 4
     out = q_l * H * D * 4
     flops = 4 * (q_l * H) * L * D
     return dict(bytes=kv + qb + mask + out, kv_bytes=kv, flops=flops)
@@ -192,11 +196,13 @@ def cpu_baseline(name, c, alg, quant):
         nrows = H * q_l
         step = max(1, nrows // 64)
         rows = [(r // H, r % H) for r in range(0, nrows, step)]
-        mask = oracle.tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"])
+        ws = c.get("window_start")
+        mask = (None if ws is not None else
+                oracle.tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"]))
         t = time.perf_counter()
         oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
-                         kv_seq_len=c["kv_seq_len"], scale=c["scale"], rows=rows,
-                         nthreads=threads)
+                         kv_seq_len=c["kv_seq_len"], scale=c["scale"],
+                         window_start=ws or 0, rows=rows, nthreads=threads)
         dt = time.perf_counter() - t
     us_call = dt * 1e6 * nrows / len(rows)
     return {"value": round(alg["bytes"] / (us_call * 1e-6) / 1e9, 4), "unit": "GB/s",
@@ -259,10 +265,12 @@ def main():
         out_dtype = torch.float16
     else:
         base = {"q": to_dev(c["q"]), "k": to_dev(c["k"]), "v": to_dev(c["v"])}
-        base["mask"] = ta.build_tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"])
+        ws = c.get("window_start")
+        base["mask"] = (None if ws is not None else
+                        ta.build_tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"]))
         H, Hk, D = c["n_heads"], c["n_kv_heads"], c["head_dim"]
         L, q_l = c["kv_seq_len"], c["q_l"]
-        nwg = args.nwg or c.get("nwg") or ta.pick_nwg(H, Hk, D, L, q_l,
+        nwg = args.nwg or c.get("nwg") or ta.pick_nwg(H, Hk, D, L - (ws or 0), q_l,
                                                        1 if kind == "f16" else 0)
         nrows = H * q_l
         out_dtype = torch.float32
@@ -299,6 +307,12 @@ def main():
                 fargs = head + (nb(cp["mask"]), c["mask_head_stride"],
                                 c["mask_stride"]) + tail
                 calls.append((lib.tree_attn_quant_forward, fargs))
+        elif ws is not None:
+            fargs = (vp(cp["q"]), nb(cp["q"]), vp(cp["k"]), vp(cp["v"]),
+                     1 if kind == "f16" else 0, nb(cp["k"]), vp(P), nb(P), vp(O), nb(O),
+                     H, Hk, D, L, c["kv_capacity"], q_l, ws, c["scale"], nwg,
+                     ctypes.c_void_p(sptr))
+            calls.append((lib.tree_attn_decode, fargs))
         else:
             fargs = (vp(cp["q"]), nb(cp["q"]), vp(cp["k"]), vp(cp["v"]),
                      1 if kind == "f16" else 0, nb(cp["k"]), vp(cp["mask"]), nb(cp["mask"]),

@@ -147,6 +147,34 @@ TA_API int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
                       void *stream);
 
 /*
+ * Causal (sliding-window) decode without a mask buffer: the implicit rule
+ * of [TA] header, which flash_attn_vec computes from abs_pos = kv_seq_len -
+ * q_l + i.  Node i (query position abs_pos) sees key j iff
+ *   window_start <= j <= abs_pos,
+ * with one window_start for every row (the header's byte-identity contract
+ * pairs it with an explicit mask that is 0.0f on [window_start, abs_pos]).
+ * A node whose abs_pos < window_start sees nothing and yields zeros.
+ * Arguments and results as tree_attn_forward with mask == NULL, plus:
+ *
+ *   window_start  first key any row may see; 0 gives the plain causal rule
+ *                 (the same call as tree_attn_forward with mask == NULL).
+ *                 Must be < kv_seq_len (TA_EINVAL otherwise).  Keys below
+ *                 the 32-key (16 at head_dim 512 with fp32 K/V) tile that
+ *                 holds window_start are not read, and a split count from
+ *                 tree_attn_pick_nwg(..., kv_seq_len - window_start, ...)
+ *                 sizes the splits to the window.  The result equals
+ *                 tree_attn_forward with the explicit window mask to
+ *                 rounding, and bit for bit when window_start lies in the
+ *                 first tile (both calls then split the same keys).
+ */
+TA_API int tree_attn_decode(const float *q, size_t q_bytes, const void *k,
+                     const void *v, int kv_dtype, size_t kv_bytes, float *partials,
+                     size_t partials_bytes, float *out, size_t out_bytes,
+                     uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                     uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
+                     uint32_t window_start, float scale, uint32_t nwg, void *stream);
+
+/*
  * Log-sum-exp merge of split partial results (the reduce pass that [TA]
  * header and [OPS] tree_attention() run after the main kernel).  For each
  * row r, over the splits w with S_w > 0:

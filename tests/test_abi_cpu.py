@@ -260,6 +260,21 @@ def test_quant_ex_validation(lib, kw, code, word):
     assert word in L.last_error()
 
 
+@no_gpu_only
+@pytest.mark.parametrize("ws,L_,code,word", [
+    (16384, 16384, L.TA_EINVAL, "window_start"),
+    (20000, 16384, L.TA_EINVAL, "window_start"),
+    (5, 16384, L.TA_EUNSUPPORTED, "head_dim"),
+])
+def test_decode_validation(lib, ws, L_, code, word):
+    vp = ctypes.c_void_p
+    hd = 96 if code == L.TA_EUNSUPPORTED else 128
+    rc = lib.tree_attn_decode(vp(FAKE), BIG, vp(FAKE), vp(FAKE), 1, BIG, vp(FAKE), BIG,
+                              vp(FAKE), BIG, 8, 2, hd, L_, L_, 4, ws, 0.1, 2, None)
+    assert rc == code
+    assert word in L.last_error()
+
+
 def mk(lib, parents, q_l=None, L_=16, stride=16, mask=FAKE, nbytes=BIG):
     arr = (ctypes.c_int32 * max(1, len(parents)))(*parents)
     q_l = len(parents) if q_l is None else q_l

@@ -276,3 +276,70 @@ def test_reduce_alone_on_oracle_partials(ta):
         T.tree_attn_reduce(part, out, nrows=nrows, head_dim=D, nwg=nw)
         torch.cuda.synchronize()
         assert_close(host(out), oracle.lse_combine(o_un, s, mx), tol, "reduce")
+
+
+# --------------------------------------------------------------------------
+# causal decode with a sliding-window start (tree_attn_decode)
+# --------------------------------------------------------------------------
+DECODE = [
+    # seed, H, Hk, D, L, q_l, kv dtype, window_start, nwg
+    (40, 4, 2, 128, 333, 5, "f32", 0, 3),
+    (41, 4, 2, 128, 333, 5, "f32", 5, 3),
+    (42, 8, 2, 256, 517, 9, "f16", 31, 4),
+    (43, 8, 2, 256, 517, 9, "f16", 32, 4),      # window starts on a tile edge
+    (44, 8, 2, 256, 517, 9, "f16", 33, None),
+    (45, 8, 1, 512, 700, 3, "f16", 300, 2),
+    (46, 4, 4, 128, 1000, 1, "f16", 999, 1),     # the last key only
+    (47, 4, 2, 512, 257, 4, "f32", 100, 2),      # fp32, 16-key tiles
+    (48, 6, 2, 128, 2000, 16, "f16", 1990, 5),   # early nodes see nothing
+    (49, 24, 4, 256, 4096, 16, "f16", 1000, None),
+]
+
+
+def run_decode(ta, c, ws, nwg=None):
+    import torch
+    q, k, v, _ = gpu_case(c, None)
+    out = ta.decode(q, k, v, kv_seq_len=c["kv_seq_len"], scale=c["scale"],
+                    window_start=ws, nwg=nwg)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("seed,H,Hk,D,L,q_l,kvd,ws,nwg", DECODE)
+def test_decode_window_parity(ta, seed, H, Hk, D, L, q_l, kvd, ws, nwg):
+    note("decode seed=%d H=%d Hk=%d D=%d L=%d q_l=%d %s ws=%d nwg=%s"
+         % (seed, H, Hk, D, L, q_l, kvd, ws, nwg))
+    c = small_case(seed, H, Hk, D, L, q_l, kvd, tree="chain")
+    got = run_decode(ta, c, ws, nwg)
+    ref = oracle.attention(c["q"], c["k"], c["v"], None, n_kv_heads=Hk, kv_seq_len=L,
+                           scale=c["scale"], window_start=ws)
+    assert_close(got, ref, TOL[kvd], "decode %d" % seed)
+    abs_pos = L - q_l + np.arange(q_l)
+    assert np.all(got[abs_pos < ws] == 0.0)
+
+
+@pytest.mark.parametrize("kvd,D,ws,nwg", [("f32", 128, 3, 3), ("f16", 256, 17, 4),
+                                          ("f16", 512, 31, 2), ("f16", 128, 0, 5)])
+def test_decode_window_in_first_tile_byte_identical_to_explicit(ta, kvd, D, ws, nwg):
+    note("decode byte identity %s D=%d ws=%d nwg=%d" % (kvd, D, ws, nwg))
+    L, q_l = 517, 9
+    c = small_case(50, 8, 2, D, L, q_l, kvd, tree="chain")
+    i = np.arange(q_l)[:, None]
+    j = np.arange(L)[None, :]
+    mask = np.where((j >= ws) & (j <= L - q_l + i), 0.0, -65504.0).astype(np.float32)
+    a = run_verify(ta, c, mask, nwg=nwg)
+    b = run_decode(ta, c, ws, nwg)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_workload_decode_window_128k(ta):
+    note("workload decode_window_128k (sampled rows)")
+    c = inputs.fp_case("decode_window_128k")
+    L, H, ws = c["kv_seq_len"], c["n_heads"], c["window_start"]
+    got = run_decode(ta, c, ws)
+    assert np.all(np.isfinite(got))
+    rows = sample_rows(c["q_l"], H, 16)
+    ref = oracle.attention(c["q"], c["k"], c["v"], None, n_kv_heads=c["n_kv_heads"],
+                           kv_seq_len=L, scale=c["scale"], window_start=ws, rows=rows)
+    sel = np.stack([got[i, h] for i, h in rows])
+    assert_close(sel, ref, TOL["f16"], "decode_window_128k")

@@ -28,7 +28,7 @@ __all__ = [
     "MASKED", "ATTENDED", "TreeAttnError", "partials_bytes", "pick_nwg",
     "quant_pick_nwg", "tree_attn_forward", "tree_attn_reduce",
     "tree_attn_quant_forward", "tree_attn_quant_forward_ex", "build_tree_mask",
-    "verify", "quant_verify",
+    "tree_attn_decode", "verify", "decode", "quant_verify",
 ]
 
 
@@ -147,6 +147,46 @@ def build_tree_mask(parents, kv_seq_len, mask_stride=None, *, out=None,
                                 kv_seq_len, stride, _ptr(out), _nbytes(out),
                                 _stream(stream))
     _check(rc)
+    return out
+
+
+def tree_attn_decode(q, k, v, *, kv_seq_len, scale, nwg, window_start=0,
+                     out=None, partials=None, stream=None):
+    """Causal decode with a sliding-window start (no mask buffer).  q [H,
+    q_l, D] f32; k, v [Hk, cap, D] f32/f16.  nwg == 1 writes ``out`` ([q_l,
+    H, D] f32); nwg > 1 writes ``partials``."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (partials, "partials")):
+        _dense(t, n)
+    H, q_l, D = q.shape
+    Hk, cap, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != k.dtype or Dk != D:
+        raise ValueError("k and v must share shape and dtype, head_dim must match q")
+    rc = _api().tree_attn_decode(
+        _ptr(q), _nbytes(q), _ptr(k), _ptr(v), _kv_dtype(k), _nbytes(k),
+        _ptr(partials), _nbytes(partials), _ptr(out), _nbytes(out), H, Hk, D,
+        kv_seq_len, cap, q_l, int(window_start), float(scale), nwg, _stream(stream))
+    _check(rc)
+
+
+def decode(q, k, v, *, kv_seq_len, scale, window_start=0, nwg=None, out=None,
+           partials=None, stream=None):
+    """Causal (sliding-window) decode plus the merge; returns ``out``
+    [q_l, H, D] f32."""
+    import torch
+    H, q_l, D = q.shape
+    if nwg is None:
+        nwg = pick_nwg(H, k.shape[0], D, kv_seq_len - window_start, q_l, _kv_dtype(k))
+    if out is None:
+        out = torch.empty((q_l, H, D), dtype=torch.float32, device=q.device)
+    if nwg > 1 and partials is None:
+        partials = torch.empty(partials_bytes(H, D, q_l, nwg) // 4,
+                               dtype=torch.float32, device=q.device)
+    tree_attn_decode(q, k, v, kv_seq_len=kv_seq_len, scale=scale, nwg=nwg,
+                     window_start=window_start, out=out if nwg == 1 else None,
+                     partials=partials if nwg > 1 else None, stream=stream)
+    if nwg > 1:
+        tree_attn_reduce(partials, out, nrows=H * q_l, head_dim=D, nwg=nwg,
+                         stream=stream)
     return out
 
 

@@ -35,6 +35,7 @@ EXPORTS = (
     "tree_attn_pick_nwg",
     "tree_attn_quant_pick_nwg",
     "tree_attn_forward",
+    "tree_attn_decode",
     "tree_attn_reduce",
     "tree_attn_quant_forward",
     "tree_attn_quant_forward_ex",
@@ -75,6 +76,9 @@ def load():
         lib.tree_attn_forward.argtypes = [P, Z, P, P, I, Z, P, Z, P, Z, P, Z,
                                           U, U, U, U, U, U, U, F, U, P]
         lib.tree_attn_forward.restype = I
+        lib.tree_attn_decode.argtypes = [P, Z, P, P, I, Z, P, Z, P, Z,
+                                         U, U, U, U, U, U, U, F, U, P]
+        lib.tree_attn_decode.restype = I
         lib.tree_attn_reduce.argtypes = [P, Z, P, I, Z, U, U, U, P]
         lib.tree_attn_reduce.restype = I
         lib.tree_attn_quant_forward.argtypes = [

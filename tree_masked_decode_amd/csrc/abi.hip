@@ -147,15 +147,17 @@ uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
                      ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, 8u, 2u, kv, part);
 }
 
-int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
+static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void *k,
                       const void *v, int kv_dtype, size_t kv_bytes,
                       const float *mask, size_t mask_bytes, float *partials,
                       size_t partials_bytes, float *out, size_t out_bytes,
                       uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
                       uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
-                      uint32_t mask_stride, float scale, uint32_t nwg,
-                      void *stream) {
-  const char *fn = "tree_attn_forward";
+                      uint32_t mask_stride, uint32_t window_start, float scale,
+                      uint32_t nwg, void *stream) {
+  if (window_start >= kv_seq_len && kv_seq_len > 0)
+    return fail(TA_EINVAL, "%s: window_start (%u) must be < kv_seq_len (%u)", fn,
+                window_start, kv_seq_len);
   // --- parameter contract ("ops/tree_attention.rs", validate_params) ---
   if (head_dim != 128 && head_dim != 256 && head_dim != 512)
     return fail(TA_EUNSUPPORTED, "%s: head_dim must be 128, 256, or 512, got %u",
@@ -240,6 +242,7 @@ int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
   a.mask_stride = mask ? mask_stride : kv_seq_len;
   a.nwg = nwg;
   a.rows = (uint32_t)rows;
+  a.key_lo = mask ? 0u : window_start;
   a.qscale = scale * ta::kLog2e;
   a.scale = scale;
   const bool f16 = kv_dtype == TA_F16;
@@ -262,6 +265,32 @@ int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
   hipError_t e = f16 ? ta::launch_forward_f16(a, head_dim, s)
                      : ta::launch_forward_f32(a, head_dim, s);
   return hip_status(e, fn);
+}
+
+int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
+                      const void *v, int kv_dtype, size_t kv_bytes,
+                      const float *mask, size_t mask_bytes, float *partials,
+                      size_t partials_bytes, float *out, size_t out_bytes,
+                      uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                      uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
+                      uint32_t mask_stride, float scale, uint32_t nwg,
+                      void *stream) {
+  return fp_forward("tree_attn_forward", q, q_bytes, k, v, kv_dtype, kv_bytes, mask,
+                    mask_bytes, partials, partials_bytes, out, out_bytes, n_heads,
+                    n_kv_heads, head_dim, kv_seq_len, kv_capacity, q_l, mask_stride, 0u,
+                    scale, nwg, stream);
+}
+
+int tree_attn_decode(const float *q, size_t q_bytes, const void *k, const void *v,
+                     int kv_dtype, size_t kv_bytes, float *partials,
+                     size_t partials_bytes, float *out, size_t out_bytes,
+                     uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
+                     uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
+                     uint32_t window_start, float scale, uint32_t nwg, void *stream) {
+  return fp_forward("tree_attn_decode", q, q_bytes, k, v, kv_dtype, kv_bytes, nullptr, 0,
+                    partials, partials_bytes, out, out_bytes, n_heads, n_kv_heads,
+                    head_dim, kv_seq_len, kv_capacity, q_l, kv_seq_len, window_start, scale,
+                    nwg, stream);
 }
 
 int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,

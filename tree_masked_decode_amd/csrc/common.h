@@ -40,6 +40,7 @@ struct FwdArgs {
   uint32_t row_tiles;  // ceil(rows / rows per workgroup)
   uint32_t n_tiles;    // ceil(kv_seq_len / BN)
   uint32_t units;      // n_kv_heads * nwg
+  uint32_t key_lo;     // implicit rule only: first key any row sees (window start)
   float qscale;        // scale * log2(e): logits in base-2 units (fp32 kernel)
   float scale;         // softmax scale: logits in natural units (fp16 kernel)
 };

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
             const uint32_t key = key0 + 16u * kb + 4u * gp + j;
             bool in;
             if (IMPLICIT)
-              in = key < L && (int64_t)key <= causal_last[rb];
+              in = key < L && key >= a.key_lo && (int64_t)key <= causal_last[rb];
             else if (GENERAL)
               in = x[j] > kMasked && key < L;
             else
@@ -375,8 +375,13 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   };
 
   // ---- main loop ----
+  // the splits cover the tiles from the one that holds key_lo (the
+  // implicit rule's window start; 0 otherwise)
+  const uint32_t tile_lo = a.key_lo / BN;
   uint32_t t0, t1;
-  split_range(a.n_tiles, a.nwg, split, t0, t1);
+  split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
+  t0 += tile_lo;
+  t1 += tile_lo;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (t0 + s < t1) {
@@ -406,6 +411,8 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   // needs no per-cell key checks.
   uint32_t fast = L / BN;
   if (IMPLICIT) fast = min(fast, (uint32_t)(((int64_t)L - a.q_l + node0 + 1) / BN));
+  // a window start inside the first tile: that split checks every cell
+  if (IMPLICIT && a.key_lo % BN != 0 && t0 == tile_lo) fast = t0;
   fast = min(max(fast, t0), t1);
   uint32_t t = t0;
   while (t < fast) {

@@ -32,15 +32,16 @@ constexpr size_t f32_lds_bytes() {
 }
 
 // Mask cell of (node i, key j), or "excluded".  IMPLICIT computes the
-// causal rule of the "tree_attention.metal" header (j <= L - q_l + i); the
-// explicit form reads the caller's [q_l, mask_stride] buffer.  Both feed the
-// same arithmetic below, so an explicit chain mask reproduces the implicit
-// result bit for bit.
+// causal / sliding-window rule of the "tree_attention.metal" header
+// (key_lo <= j <= L - q_l + i); the explicit form reads the caller's
+// [q_l, mask_stride] buffer.  Both feed the same arithmetic below, so an
+// explicit mask of the same rule reproduces the implicit result bit for bit
+// whenever both cover the same tiles.
 template <bool IMPLICIT>
 __device__ inline float mask_cell(const FwdArgs &a, uint32_t i, uint32_t j) {
   if (IMPLICIT) {
     int64_t last = (int64_t)a.kv_seq_len - (int64_t)a.q_l + (int64_t)i;
-    return ((int64_t)j <= last) ? 0.0f : kMasked;
+    return (j >= a.key_lo && (int64_t)j <= last) ? 0.0f : kMasked;
   }
   return a.mask[(size_t)i * a.mask_stride + j];
 }
@@ -84,8 +85,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
   for (int k = 0; k < S::EPT; ++k) acc[k] = 0.0f;
 
+  // the splits cover the tiles from the one that holds key_lo
+  const uint32_t tile_lo = a.key_lo / S::BN;
   uint32_t t0, t1;
-  split_range(a.n_tiles, a.nwg, split, t0, t1);
+  split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
+  t0 += tile_lo;
+  t1 += tile_lo;
   const size_t kvbase = (size_t)hk * a.kv_capacity * D;
   const float *K = static_cast<const float *>(a.k) + kvbase;
   const float *V = static_cast<const float *>(a.v) + kvbase;

@@ -45,6 +45,12 @@ WORKLOADS = {
                               kv_seq_len=131072, kv_capacity=131072, q_l=8,
                               tree="chain", mask_stride=131072, kv_dtype="f16",
                               kv_std=1.0, nwg=None),
+    # causal decode without a mask buffer over the last 32768 of 131072 keys
+    # (implicit rule with a sliding-window start), long-context shape
+    "decode_window_128k": dict(n_heads=32, n_kv_heads=8, head_dim=512,
+                               kv_seq_len=131072, kv_capacity=131072, q_l=8,
+                               tree="chain", mask_stride=131072, kv_dtype="f16",
+                               kv_std=1.0, nwg=None, window_start=98304),
 }
 
 QUANT_WORKLOADS = {
