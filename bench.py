@@ -123,6 +123,7 @@ def measured_traffic(workload, kind):
 
 
 COPY_BYTES = 256 << 20     # the --copy-calibration copy: reads and writes this much
+CALIB_COPIES = 5           # ... this many times, right before the warm-up calls
 
 
 def record_traffic(workload, fetch_csv, write_csv):
@@ -140,18 +141,32 @@ def record_traffic(workload, fetch_csv, write_csv):
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
             acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
         return acc
+
+    def is_copy(k):
+        return "copy" in k.lower() or "elementwise" in k.lower()
+
+    def is_fwd(k):
+        return "fwd_" in k or "quant_kernel" in k
 
     out = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         acc = per_kernel(path, name)
-        copy = [v for (k, _), v in acc.items() if "copy" in k.lower() or "elementwise" in k.lower()]
-        fwd = [v for (k, _), v in acc.items() if "fwd_" in k or "quant_kernel" in k]
-        if not copy or not fwd:
-            raise SystemExit("record-traffic: no copy or forward dispatches in %s" % path)
-        copy_kib = max(copy)  # the 256 MiB copies (other copies are small)
+        fwd_ids = [d for (k, d) in acc if is_fwd(k)]
+        if not fwd_ids:
+            raise SystemExit("record-traffic: no forward dispatches in %s" % path)
+        first = min(fwd_ids)
+        # the calibration copies are the CALIB_COPIES copy dispatches right
+        # before the first forward (the input rotation copies come earlier
+        # and can be larger)
+        copies = sorted((d, v) for (k, d), v in acc.items() if is_copy(k) and d < first)
+        copy = [v for _, v in copies[-CALIB_COPIES:]]
+        fwd = [v for (k, _), v in acc.items() if is_fwd(k)]
+        if len(copy) < CALIB_COPIES:
+            raise SystemExit("record-traffic: no calibration copies in %s" % path)
+        copy_kib = statistics.median(copy)
         scale = COPY_BYTES / (copy_kib * 1024.0)
         out[name] = {"kib_per_launch": statistics.fmean(fwd), "copy_kib": copy_kib,
                      "scale": scale, "dispatches": len(fwd)}
@@ -340,7 +355,7 @@ def main():
         # a plain device copy of known size, for scaling the PMC byte counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(5):
+        for _ in range(CALIB_COPIES):
             dst.copy_(src)
         torch.cuda.synchronize()
         print("copy calibration: 5 copies of %d bytes" % src.numel(), file=sys.stderr)
