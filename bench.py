@@ -275,7 +275,9 @@ def main():
         B, nQ, nKV, dim = c["batch"], c["n_q_heads"], c["n_kv_heads"], c["dim"]
         L, q_l = c["kv_seq_len"], c["q_l"]
         span = min(window, L) if window else L
-        nwg = args.nwg or ta.quant_pick_nwg(B, nQ, nKV, dim, span, q_l)
+        nwg = args.nwg or ta.quant_pick_nwg(B, nQ, nKV, dim, span, q_l, bits=c["bits"],
+                                            group_size=c["group_size"],
+                                            mask_kind=mask_kind)
         nrows, D = B * nQ * q_l, dim
         out_dtype = torch.float16
     else:

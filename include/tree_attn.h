@@ -98,11 +98,27 @@ TA_API uint32_t tree_attn_pick_nwg(uint32_t n_heads, uint32_t n_kv_heads,
                             uint32_t head_dim, uint32_t kv_seq_len,
                             uint32_t q_l, int kv_dtype, uint32_t num_cus);
 
-/* The same for tree_attn_quant_forward. */
+/* The same for tree_attn_quant_forward (4-bit codes with an fp16 mask
+ * assumed for the residency of a workgroup). */
 TA_API uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
                                   uint32_t n_kv_heads, uint32_t dim,
                                   uint32_t kv_seq_len, uint32_t q_l,
                                   uint32_t num_cus);
+
+/*
+ * The split count for tree_attn_quant_forward(_ex) with the kernel variant
+ * the call will run: bits, group_size and mask_kind (TA_MASK_*) set its
+ * registers and LDS, and so how many workgroups a CU holds at once.  That
+ * number comes from the HIP runtime's occupancy query for the variant on the
+ * current device; without a device it is estimated from the variant's LDS
+ * size.  With a sliding window pass min(window_size, kv_seq_len) as
+ * kv_seq_len.  Always >= 1.
+ */
+TA_API uint32_t tree_attn_quant_pick_nwg_ex(uint32_t batch, uint32_t n_q_heads,
+                                     uint32_t n_kv_heads, uint32_t dim,
+                                     uint32_t kv_seq_len, uint32_t q_l, uint32_t bits,
+                                     uint32_t group_size, int mask_kind,
+                                     uint32_t num_cus);
 
 /*
  * Tree-attention forward pass ([TA] tree_attention_impl; [OPS]

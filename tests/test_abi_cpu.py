@@ -72,6 +72,22 @@ def test_pick_nwg_properties(lib):
     assert lib.tree_attn_quant_pick_nwg(4, 32, 8, 128, 16384, 1, 0) >= 1
 
 
+@no_gpu_only
+def test_quant_pick_nwg_ex_follows_the_variant_footprint(lib):
+    # without a device: two wavefronts per SIMD at dim 128, and the LDS of the
+    # variant: 4-bit stages fit eight workgroups a CU, 8-bit ones six
+    f = lib.tree_attn_quant_pick_nwg_ex
+    assert f(4, 32, 8, 128, 16384, 1, 4, 64, 1, 0) == 64
+    assert f(4, 32, 8, 128, 16384, 1, 8, 64, 1, 0) == 48
+    assert f(4, 32, 8, 128, 16384, 1, 4, 64, 2, 0) == 64
+    # a short sequence caps the splits at two tiles each
+    assert f(4, 32, 8, 128, 4096, 1, 4, 64, 1, 0) == 64
+    assert f(4, 32, 8, 128, 512, 1, 4, 64, 1, 0) == 8
+    # degenerate shapes and unsupported variants still give a usable count
+    assert f(0, 32, 8, 128, 16384, 1, 4, 64, 1, 0) == 1
+    assert f(4, 32, 8, 96, 16384, 1, 4, 32, 1, 0) >= 1
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))

@@ -91,9 +91,16 @@ def pick_nwg(n_heads, n_kv_heads, head_dim, kv_seq_len, q_l, kv_dtype,
 
 
 def quant_pick_nwg(batch, n_q_heads, n_kv_heads, dim, kv_seq_len, q_l,
-                   num_cus=0) -> int:
-    return int(_api().tree_attn_quant_pick_nwg(batch, n_q_heads, n_kv_heads,
-                                               dim, kv_seq_len, q_l, num_cus))
+                   num_cus=0, bits=None, group_size=None, mask_kind=None) -> int:
+    """Split count for the quantized forward; with bits, group_size and
+    mask_kind it accounts for how many workgroups of that variant fit a CU
+    (tree_attn_quant_pick_nwg_ex)."""
+    if bits is None:
+        return int(_api().tree_attn_quant_pick_nwg(batch, n_q_heads, n_kv_heads,
+                                                   dim, kv_seq_len, q_l, num_cus))
+    return int(_api().tree_attn_quant_pick_nwg_ex(
+        batch, n_q_heads, n_kv_heads, dim, kv_seq_len, q_l, bits, group_size,
+        TA_MASK_F16 if mask_kind is None else mask_kind, num_cus))
 
 
 def tree_attn_forward(q, k, v, mask, *, kv_seq_len, scale, nwg, out=None,
@@ -292,7 +299,10 @@ def quant_verify(q, k_packed, k_scales, k_biases, v_packed, v_scales,
         raise ValueError("quant_verify: give at most one of mask and mask_bool")
     if nwg is None:
         span = min(window_size, kv_seq_len) if window_size else kv_seq_len
-        nwg = quant_pick_nwg(batch, BnQ // batch, n_kv_heads, dim, span, q_l)
+        kind = (TA_MASK_BOOL if mask_bool is not None else
+                TA_MASK_F16 if mask is not None else TA_MASK_NONE)
+        nwg = quant_pick_nwg(batch, BnQ // batch, n_kv_heads, dim, span, q_l,
+                             bits=bits, group_size=group_size, mask_kind=kind)
     if out is None:
         out = torch.empty((BnQ, q_l, dim), dtype=torch.float16, device=q.device)
     if nwg > 1 and partials is None:

@@ -34,6 +34,7 @@ EXPORTS = (
     "tree_attn_partials_bytes",
     "tree_attn_pick_nwg",
     "tree_attn_quant_pick_nwg",
+    "tree_attn_quant_pick_nwg_ex",
     "tree_attn_forward",
     "tree_attn_decode",
     "tree_attn_reduce",
@@ -73,6 +74,8 @@ def load():
         lib.tree_attn_pick_nwg.restype = U
         lib.tree_attn_quant_pick_nwg.argtypes = [U, U, U, U, U, U, U]
         lib.tree_attn_quant_pick_nwg.restype = U
+        lib.tree_attn_quant_pick_nwg_ex.argtypes = [U, U, U, U, U, U, U, U, I, U]
+        lib.tree_attn_quant_pick_nwg_ex.restype = U
         lib.tree_attn_forward.argtypes = [P, Z, P, P, I, Z, P, Z, P, Z, P, Z,
                                           U, U, U, U, U, U, U, F, U, P]
         lib.tree_attn_forward.restype = I

@@ -267,6 +267,24 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
   return hip_status(e, fn);
 }
 
+uint32_t tree_attn_quant_pick_nwg_ex(uint32_t batch, uint32_t n_q_heads,
+                                     uint32_t n_kv_heads, uint32_t dim,
+                                     uint32_t kv_seq_len, uint32_t q_l, uint32_t bits,
+                                     uint32_t group_size, int mask_kind,
+                                     uint32_t num_cus) {
+  if (batch == 0 || n_q_heads == 0 || n_kv_heads == 0 || kv_seq_len == 0 ||
+      q_l == 0 || n_q_heads % n_kv_heads != 0)
+    return 1;
+  uint32_t per_cu = ta::quant_wgs_per_cu(dim, bits, group_size, mask_kind);
+  if (per_cu == 0) per_cu = 8u;   // not a supported variant: the plain estimate
+  uint32_t rows = q_l * (n_q_heads / n_kv_heads);
+  const uint64_t kv = 2ull * batch * n_kv_heads * kv_seq_len * dim * (bits ? bits : 4) / 8;
+  const uint64_t part = (uint64_t)batch * n_q_heads * q_l * (dim + 2) * 4;
+  return pick_splits(batch * n_kv_heads, ceil_div(rows, ta::kQuantRowsPerWG),
+                     ceil_div(kv_seq_len, ta::quant_tile_keys(dim)), num_cus, per_cu, 2u, kv,
+                     part);
+}
+
 int tree_attn_forward(const float *q, size_t q_bytes, const void *k,
                       const void *v, int kv_dtype, size_t kv_bytes,
                       const float *mask, size_t mask_bytes, float *partials,

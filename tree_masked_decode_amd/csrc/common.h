@@ -101,6 +101,9 @@ uint32_t f16_tile_keys(uint32_t head_dim);
 uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows);
 uint32_t f32_tile_keys(uint32_t head_dim);
 uint32_t quant_tile_keys(uint32_t dim);
+// Resident workgroups per CU of the quantized kernel variant (0: no such
+// variant); mask_kind 0 none, 1 fp16, 2 u32.
+uint32_t quant_wgs_per_cu(uint32_t dim, uint32_t bits, uint32_t group, int mask_kind);
 
 // Asynchronous global -> LDS copies: every lane moves 16 (or 4) bytes from its
 // own global address to lds + 16 * lane (4 * lane), `lds` being the

@@ -647,9 +647,63 @@ hipError_t launch_qb(const QuantArgs &a, uint32_t bits, uint32_t G, hipStream_t 
   return bits == 4 ? launch_qg<DIM, 4>(a, G, s) : launch_qg<DIM, 8>(a, G, s);
 }
 
+// Workgroups of one variant a CU holds: the runtime's occupancy answer for
+// the kernel with its LDS, or, with no device to ask, the plan's budgets
+// (two wavefronts per SIMD up to dim 128, one above; 160 KB of LDS).
+template <int DIM, int BITS, int G, int MM>
+uint32_t wgs_per_cu() {
+  using ST = QStage<DIM, BITS, G, MM>;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_kernel<DIM, BITS, G, MM>, kThreads,
+                                                   ST::LDS) == hipSuccess &&
+      n > 0)
+    return (uint32_t)n;
+  (void)hipGetLastError();
+  const uint32_t by_regs = DIM <= 128 ? 8u : 4u;
+  const uint32_t by_lds = (160u * 1024u) / (uint32_t)ST::LDS;
+  return by_regs < by_lds ? by_regs : by_lds;
+}
+
+template <int DIM, int BITS, int G>
+uint32_t wgs_per_cu_m(int mask_kind) {
+  // the fp16 mask's copy modes share one footprint (the register-load mode
+  // is smaller); both u32 copy modes share one too
+  if (mask_kind == 2) return wgs_per_cu<DIM, BITS, G, kMaskBoolB128>();
+  if (mask_kind == 1) return wgs_per_cu<DIM, BITS, G, kMaskB128>();
+  return wgs_per_cu<DIM, BITS, G, kMaskNone>();
+}
+
+template <int DIM, int BITS>
+uint32_t wgs_per_cu_g(uint32_t G, int mask_kind) {
+  switch (G) {
+    case 32: return wgs_per_cu_m<DIM, BITS, 32>(mask_kind);
+    case 64: return wgs_per_cu_m<DIM, BITS, 64>(mask_kind);
+    case 128:
+      if constexpr (DIM >= 128) return wgs_per_cu_m<DIM, BITS, 128>(mask_kind);
+      return 0;
+    default: return 0;
+  }
+}
+
+template <int DIM>
+uint32_t wgs_per_cu_b(uint32_t bits, uint32_t G, int mask_kind) {
+  return bits == 4 ? wgs_per_cu_g<DIM, 4>(G, mask_kind)
+                   : bits == 8 ? wgs_per_cu_g<DIM, 8>(G, mask_kind) : 0;
+}
+
 }  // namespace
 
 uint32_t quant_tile_keys(uint32_t) { return (uint32_t)BN; }
+
+uint32_t quant_wgs_per_cu(uint32_t dim, uint32_t bits, uint32_t group, int mask_kind) {
+  switch (dim) {
+    case 64: return wgs_per_cu_b<64>(bits, group, mask_kind);
+    case 128: return wgs_per_cu_b<128>(bits, group, mask_kind);
+    case 256: return wgs_per_cu_b<256>(bits, group, mask_kind);
+    case 512: return wgs_per_cu_b<512>(bits, group, mask_kind);
+    default: return 0;
+  }
+}
 
 hipError_t launch_quant_forward(const QuantArgs &a, uint32_t dim, uint32_t bits,
                                 uint32_t group, hipStream_t s) {

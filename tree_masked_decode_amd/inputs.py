@@ -62,6 +62,10 @@ QUANT_WORKLOADS = {
     "quant_4bit_bool": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
                             kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=4,
                             group_size=64, sinks=True, mask="bool", nwg=None),
+    # the same decode with 8-bit codes (4 per word)
+    "quant_8bit": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
+                       kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=8,
+                       group_size=64, sinks=True, mask="alibi", nwg=None),
     # sliding-window decode: only the last 4096 of 16384 tokens are attended
     "quant_4bit_window": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
                               kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=4,
