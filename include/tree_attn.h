@@ -238,8 +238,8 @@ TA_API int tree_attn_reduce(const float *partials, size_t partials_bytes, void *
  *   out        DEVICE f16 [batch*n_q_heads, q_l, dim], written iff nwg == 1
  *
  * q_dtype must be TA_F16 (scales, biases, mask and out share it); bits is
- * 4 or 8; dim is 64, 128, 256 or 512; group_size is 32, 64 or 128 and
- * divides dim; kv_capacity >= kv_seq_len > 0 (and even when group_size ==
+ * 4 or 8; dim is 64, 96, 128, 256 or 512 ([FQS] instantiations); group_size
+ * is 32, 64 or 128 and divides dim (so 32 at dim 96); kv_capacity >= kv_seq_len > 0 (and even when group_size ==
  * dim); mask_stride >= kv_seq_len when a mask is given.  With nwg > 1 follow with tree_attn_reduce(out_dtype =
  * TA_F16, nrows = batch*n_q_heads*q_l, head_dim = dim).
  */

@@ -218,7 +218,8 @@ def qf(lib, **kw):
 @pytest.mark.parametrize("kw,code,word", [
     (dict(q_dtype=0), L.TA_EUNSUPPORTED, "dtype"),
     (dict(bits=3), L.TA_EUNSUPPORTED, "bits"),
-    (dict(dim=96), L.TA_EUNSUPPORTED, "dim"),
+    (dict(dim=80), L.TA_EUNSUPPORTED, "dim"),
+    (dict(dim=96), L.TA_EINVAL, "divisible"),      # dim 96 needs group_size 32
     (dict(G=48), L.TA_EUNSUPPORTED, "group_size"),
     (dict(dim=64, G=128), L.TA_EINVAL, "divisible"),
     (dict(nq=30), L.TA_EINVAL, "divisible"),

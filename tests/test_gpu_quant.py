@@ -82,6 +82,9 @@ SMALL = [
     (9, 1, 2, 1, 128, 40, 1, 4, 64, False, None, 9),       # more splits than tiles
     (10, 1, 2, 1, 64, 101, 1, 4, 64, True, "alibi", 2),   # one group per token
     (11, 2, 4, 2, 64, 99, 2, 8, 64, False, None, 3),
+    (12, 1, 4, 1, 96, 333, 1, 4, 32, True, "alibi", 3),    # 1.5 KB K/V tiles
+    (13, 2, 4, 2, 96, 190, 2, 8, 32, False, None, 2),
+    (14, 3, 8, 2, 96, 1000, 1, 4, 32, True, None, None),
 ]
 
 
@@ -168,6 +171,8 @@ GATED = [
     (33, 1, 4, 1, 128, 300, 1, 4, 64, True, None, 300, 5),     # window == L: no window
     (34, 1, 4, 1, 128, 300, 1, 4, 64, True, "bool", 5000, 5),  # window > L
     (35, 1, 2, 1, 512, 161, 2, 4, 128, True, None, 70, 3),
+    (38, 1, 4, 2, 96, 300, 1, 4, 32, True, "bool", 0, 2),
+    (39, 1, 4, 1, 96, 500, 1, 8, 32, False, "alibi", 77, 3),
 ]
 
 

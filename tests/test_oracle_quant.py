@@ -145,11 +145,11 @@ def _brute_quant(c):
     return out
 
 
-@pytest.mark.parametrize("bits,G,sinks,alibi", [
-    (4, 32, False, False), (4, 64, True, True), (8, 32, True, False),
-    (8, 16, False, True)])
-def test_matches_brute_force(bits, G, sinks, alibi):
-    c = qcase(3, B=2, nQ=4, nKV=2, dim=64, L=57, bits=bits, G=G, sinks=sinks,
+@pytest.mark.parametrize("bits,G,sinks,alibi,dim", [
+    (4, 32, False, False, 64), (4, 64, True, True, 64), (8, 32, True, False, 64),
+    (8, 16, False, True, 64), (4, 32, True, True, 96), (8, 32, False, False, 96)])
+def test_matches_brute_force(bits, G, sinks, alibi, dim):
+    c = qcase(3, B=2, nQ=4, nKV=2, dim=dim, L=57, bits=bits, G=G, sinks=sinks,
               mask="alibi" if alibi else None)
     np.testing.assert_allclose(qrun(c), _brute_quant(c), rtol=0, atol=1e-12)
 

@@ -369,8 +369,8 @@ static int quant_forward(
     return fail(TA_EUNSUPPORTED, "%s: queries/scales/biases/out dtype must be TA_F16", fn);
   if (bits != 4 && bits != 8)
     return fail(TA_EUNSUPPORTED, "%s: bits must be 4 or 8, got %u", fn, bits);
-  if (dim != 64 && dim != 128 && dim != 256 && dim != 512)
-    return fail(TA_EUNSUPPORTED, "%s: dim must be 64, 128, 256 or 512, got %u", fn, dim);
+  if (dim != 64 && dim != 96 && dim != 128 && dim != 256 && dim != 512)
+    return fail(TA_EUNSUPPORTED, "%s: dim must be 64, 96, 128, 256 or 512, got %u", fn, dim);
   if (group_size != 32 && group_size != 64 && group_size != 128)
     return fail(TA_EUNSUPPORTED, "%s: group_size must be 32, 64 or 128, got %u", fn,
                 group_size);

@@ -111,14 +111,18 @@ struct QShape {
   static constexpr int GW = G * BITS / 32;     // words per group
   static constexpr int STEPS = DIM / 32;       // score MFMA steps
   static constexpr int DB = DIM / 16;          // PV output blocks
-  static constexpr int VCH = BN * WPK / 4 / kThreads;  // V 16-byte chunks/lane
+  static constexpr int VTOT = BN * WPK / 4;            // V 16-byte chunks of a tile
+  static constexpr int VCH = (VTOT + kThreads - 1) / kThreads;  // ... per lane
   static constexpr int RS = BN + 4;            // LDS row stride (words)
   static constexpr int SBW = 4 * NG / 2;       // u32 words of 4 keys' scales
   static_assert(VCH >= 1, "tile too small");
   static_assert(RUN * 4 == GW, "lane runs must tile a group");
   // LDS stage: K words, V words, K scales, K biases, V scales, V biases, mask
   static constexpr int KT = BN * WPK * 4;              // bytes of a K (or V) tile
-  static constexpr int KT_I = KT / 1024;               // 16-byte-per-lane copies
+  static constexpr int KT_I = (KT + 1023) / 1024;      // 16-byte-per-lane copies
+  // bytes of the last copy when a tile is not a whole number of copies
+  // (dim 96 at 4 bits: 1.5 KB); its lanes past that leave it alone
+  static constexpr int KT_TAIL = KT % 1024;
   static constexpr int SBB = BN * NG * 2;              // bytes of one scale/bias slice
   // the four slices back to back (4 SBB = 256 NG bytes) move in SB_I
   // 4-byte-per-lane copies; lane l of copy i takes byte 256 i + 4 l of that
@@ -127,7 +131,7 @@ struct QShape {
   static constexpr int SBP = SBB;
   static constexpr int MB = 16 * BN * 2;               // mask cells of 16 rows
   static constexpr int VL = WPK * RS * 4;              // V transpose area
-  static_assert(KT % 1024 == 0, "K tile copies");
+  static_assert(WPK % 4 == 0, "token rows of whole 16-byte chunks");
 };
 
 // Mask modes: none (implicit causal); an fp16 additive mask in 16-byte
@@ -288,8 +292,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       const size_t kvo = (size_t)key0 * (4u * S::WPK);
 #pragma unroll
       for (int i = 0; i < S::KT_I; ++i) {
-        dma_b128(kp_l + kvo + 1024u * i, sb + 1024u * i);
-        dma_b128(vp_l + kvo + 1024u * i, sb + S::KT + 1024u * i);
+        if (S::KT_TAIL == 0 || i + 1 < S::KT_I || 16u * lane < (uint32_t)S::KT_TAIL) {
+          dma_b128(kp_l + kvo + 1024u * i, sb + 1024u * i);
+          dma_b128(vp_l + kvo + 1024u * i, sb + S::KT + 1024u * i);
+        }
       }
       const size_t so = (size_t)key0 * (2u * NG);
 #pragma unroll
@@ -299,11 +305,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 #pragma unroll
       for (int i = 0; i < S::KT_I; ++i) {
         const uint32_t o = 1024u * i + 16u * lane;
-        uint32_t key = key0 + o / (4u * S::WPK);
-        if (key >= L) key = L - 1u;
-        const size_t go = (size_t)key * (4u * S::WPK) + o % (4u * S::WPK);
-        dma_b128(reinterpret_cast<const char *>(KP) + go, sb + 1024u * i);
-        dma_b128(reinterpret_cast<const char *>(VP) + go, sb + S::KT + 1024u * i);
+        if (S::KT_TAIL == 0 || o < (uint32_t)S::KT) {
+          uint32_t key = key0 + o / (4u * S::WPK);
+          if (key >= L) key = L - 1u;
+          const size_t go = (size_t)key * (4u * S::WPK) + o % (4u * S::WPK);
+          dma_b128(reinterpret_cast<const char *>(KP) + go, sb + 1024u * i);
+          dma_b128(reinterpret_cast<const char *>(VP) + go, sb + S::KT + 1024u * i);
+        }
       }
 #pragma unroll
       for (int i = 0; i < S::SB_I; ++i) {
@@ -408,7 +416,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     for (int u = 0; u < S::VCH; ++u) {
       const uint32_t c = lane + kThreads * u;
       const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
-      T.vw[u] = *reinterpret_cast<const u32x4 *>(Vl + key * S::WPK + 4 * q4);
+      T.vw[u] = (S::VTOT % kThreads == 0 || c < (uint32_t)S::VTOT)
+                    ? *reinterpret_cast<const u32x4 *>(Vl + key * S::WPK + 4 * q4)
+                    : u32x4{0u, 0u, 0u, 0u};
     }
   };
   // V words -> LDS [word][position]; position of key (16h + 4g4 + j) is
@@ -417,6 +427,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 #pragma unroll
     for (int u = 0; u < S::VCH; ++u) {
       const uint32_t c = lane + kThreads * u;
+      if (S::VTOT % kThreads != 0 && c >= (uint32_t)S::VTOT) continue;
       const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
       const uint32_t pos = 8u * ((key & 15u) >> 2) + 4u * (key >> 4) + (key & 3u);
 #pragma unroll
@@ -634,9 +645,11 @@ template <int DIM, int BITS>
 hipError_t launch_qg(const QuantArgs &a, uint32_t G, hipStream_t s) {
   switch (G) {
     case 32: return launch_q<DIM, BITS, 32>(a, s);
-    case 64: return launch_q<DIM, BITS, 64>(a, s);
+    case 64:
+      if constexpr (DIM % 64 == 0) return launch_q<DIM, BITS, 64>(a, s);
+      return hipErrorInvalidValue;
     case 128:
-      if constexpr (DIM >= 128) return launch_q<DIM, BITS, 128>(a, s);
+      if constexpr (DIM % 128 == 0) return launch_q<DIM, BITS, 128>(a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -677,9 +690,11 @@ template <int DIM, int BITS>
 uint32_t wgs_per_cu_g(uint32_t G, int mask_kind) {
   switch (G) {
     case 32: return wgs_per_cu_m<DIM, BITS, 32>(mask_kind);
-    case 64: return wgs_per_cu_m<DIM, BITS, 64>(mask_kind);
+    case 64:
+      if constexpr (DIM % 64 == 0) return wgs_per_cu_m<DIM, BITS, 64>(mask_kind);
+      return 0;
     case 128:
-      if constexpr (DIM >= 128) return wgs_per_cu_m<DIM, BITS, 128>(mask_kind);
+      if constexpr (DIM % 128 == 0) return wgs_per_cu_m<DIM, BITS, 128>(mask_kind);
       return 0;
     default: return 0;
   }
@@ -698,6 +713,7 @@ uint32_t quant_tile_keys(uint32_t) { return (uint32_t)BN; }
 uint32_t quant_wgs_per_cu(uint32_t dim, uint32_t bits, uint32_t group, int mask_kind) {
   switch (dim) {
     case 64: return wgs_per_cu_b<64>(bits, group, mask_kind);
+    case 96: return wgs_per_cu_b<96>(bits, group, mask_kind);
     case 128: return wgs_per_cu_b<128>(bits, group, mask_kind);
     case 256: return wgs_per_cu_b<256>(bits, group, mask_kind);
     case 512: return wgs_per_cu_b<512>(bits, group, mask_kind);
@@ -709,6 +725,7 @@ hipError_t launch_quant_forward(const QuantArgs &a, uint32_t dim, uint32_t bits,
                                 uint32_t group, hipStream_t s) {
   switch (dim) {
     case 64: return launch_qb<64>(a, bits, group, s);
+    case 96: return launch_qb<96>(a, bits, group, s);
     case 128: return launch_qb<128>(a, bits, group, s);
     case 256: return launch_qb<256>(a, bits, group, s);
     case 512: return launch_qb<512>(a, bits, group, s);
