@@ -107,6 +107,7 @@ FWD_SOURCES = {"f16": ["tree_masked_decode_amd/csrc/fwd_f16.hip",
                "f32": ["tree_masked_decode_amd/csrc/fwd_f32.hip",
                        "tree_masked_decode_amd/csrc/common.h"],
                "quant": ["tree_masked_decode_amd/csrc/quant.hip",
+                         "tree_masked_decode_amd/csrc/quant_impl.h",
                          "tree_masked_decode_amd/csrc/common.h"]}
 
 

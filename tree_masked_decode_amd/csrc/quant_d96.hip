@@ -1,0 +1,14 @@
+// quant_d96.hip -- the head-dim-96 variants of the quantized kernel.
+#include "quant_impl.h"
+
+namespace ta {
+
+hipError_t launch_quant_d96(const QuantArgs &a, uint32_t bits, uint32_t group, hipStream_t s) {
+  return launch_qb<96>(a, bits, group, s);
+}
+
+uint32_t quant_wgs_d96(uint32_t bits, uint32_t group, int mask_kind) {
+  return wgs_per_cu_b<96>(bits, group, mask_kind);
+}
+
+}  // namespace ta

@@ -1,0 +1,714 @@
+// quant_impl.h -- attention over an affine-quantized (4/8-bit) K/V cache:
+// the kernel templates.  Each quant_d<dim>.hip instantiates one head dim,
+// so that the variants compile in parallel; quant.hip dispatches.
+//
+// "ffai/flash_quantized_sdpa.rs" (metaltile-std 0.1.0): element d of a token
+// is scale_g * code + bias_g with the code taken little-end first from a
+// 32-bit word, a query head maps to kv stream q_idx / repeat, an optional
+// sink is a virtual key with raw logit sinks[h] and value 0, and an optional
+// additive f16 mask biases the logits.  That page runs one 32-lane group per
+// query over all tokens; here one wavefront takes up to 16 query rows that
+// share a kv stream (heads of the GQA group x tree nodes) over one KV split,
+// and the contractions run on v_mfma_f32_16x16x32_f16 with the codes as exact
+// fp16 integers.  The affine map is factored out of the contractions:
+//
+//   q.k_t = sum_g s_tg * (sum_{d in g} q_d c_td) + b_tg * (sum_{d in g} q_d)
+//   o_d   = sum_t (p_t s^v_tg) c^v_td + sum_t p_t b^v_tg,      g = group of d
+//
+// so K codes feed the score MFMA directly (one accumulator per group; Q is
+// used exactly as given in fp16 and the attention scale is applied to the
+// fp32 dot products), and the PV MFMA takes codes as A and p*scale_g as B
+// (one B operand per group, split into an fp16 hi/lo pair so the product
+// keeps fp32-like precision); the bias terms are short per-row dot products
+// on the VALU.
+//
+// Memory pipeline: every tile of 32 keys -- K words, V words, the four
+// scale/bias slices and the mask cells of the workgroup's rows -- is copied
+// global -> LDS with coalesced global_load_lds instructions into a ring of NS
+// stages, NS - 1 tiles ahead; the workgroup is one wavefront, so waits are
+// its own vmcnt counts and no barrier is needed.  The arithmetic then reads
+// the tile from LDS.
+//
+// Codes become fp16 by OR-ing them into the mantissa of 1024.0 (0x6400) and
+// subtracting 1024 (exact).  K codes are read straight into MFMA operands
+// (a 32-bit word holds 8 or 4 consecutive dims of one token, and the order of
+// the dims inside an MFMA step is free as long as Q uses the same order).
+// V must be transposed (the PV operand wants 8 tokens of one dim per lane),
+// so each wavefront bounces its V words through LDS as [word][token].
+#pragma once
+
+#include "common.h"
+
+namespace ta {
+
+namespace {
+
+constexpr int kThreads = 64;   // one wavefront per workgroup
+constexpr int BN = 32;         // keys per tile
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ inline uint32_t as_u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Two codes (already in bits 0..bits-1 of x0 / x1's lane slots) -> (c0, c1)
+// as exact fp16: OR into 1024.0's mantissa, then subtract 1024.
+__device__ inline uint32_t codes_to_h2(uint32_t packed_pair) {
+  half2_t h = as_h2(packed_pair | 0x64006400u);
+  const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
+  return as_u(h - k1024);
+}
+// The same from an unmasked word: (x & m) | 0x64006400 is one v_and_or_b32
+// when the nibble/byte mask m sits in a register (it is kept out of the
+// compiler's sight so that it is not folded back into a second literal).
+__device__ inline uint32_t masked_codes_to_h2(uint32_t x, uint32_t m) {
+  half2_t h = as_h2((x & m) | 0x64006400u);
+  const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
+  return as_u(h - k1024);
+}
+template <int BITS> __device__ inline uint32_t code_pair_mask() {
+  uint32_t m;
+  if (BITS == 4)
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(m));
+  else
+    asm volatile("v_mov_b32 %0, 0x00ff00ff" : "=v"(m));
+  return m;
+}
+
+// 8 slots of one MFMA step from the lane's words.  4-bit: one word, slots
+// [c0 c4 c1 c5 c2 c6 c3 c7].  8-bit: two words, slots [c0 c2 c1 c3] each.
+template <int BITS>
+__device__ inline half8_t word_codes(const uint32_t *w, uint32_t m) {
+  u32x4 r;
+  if (BITS == 4) {
+    r[0] = masked_codes_to_h2(w[0], m);
+    r[1] = masked_codes_to_h2(w[0] >> 4, m);
+    r[2] = masked_codes_to_h2(w[0] >> 8, m);
+    r[3] = masked_codes_to_h2(w[0] >> 12, m);
+  } else {
+    r[0] = masked_codes_to_h2(w[0], m);
+    r[1] = masked_codes_to_h2(w[0] >> 8, m);
+    r[2] = masked_codes_to_h2(w[1], m);
+    r[3] = masked_codes_to_h2(w[1] >> 8, m);
+  }
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// Dim index of slot j of a step whose first word is w0 (see word_codes).
+template <int BITS>
+__device__ inline uint32_t slot_dim(uint32_t w0, int j) {
+  if (BITS == 4) {
+    const int pi4[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    return 8u * w0 + pi4[j];
+  }
+  const int pi8[4] = {0, 2, 1, 3};
+  return 4u * (w0 + (uint32_t)(j >> 2)) + pi8[j & 3];
+}
+
+template <int DIM, int BITS, int G>
+struct QShape {
+  static constexpr int WPK = DIM * BITS / 32;  // 32-bit words per token row
+  static constexpr int NG = DIM / G;           // scale groups per token
+  static constexpr int WPS = BITS / 4;         // words per MFMA step per lane
+  static constexpr int SPG = G / 32;           // MFMA steps per group
+  static constexpr int RUN = SPG * WPS;        // lane's contiguous words per group
+  static constexpr int GW = G * BITS / 32;     // words per group
+  static constexpr int STEPS = DIM / 32;       // score MFMA steps
+  static constexpr int DB = DIM / 16;          // PV output blocks
+  static constexpr int VTOT = BN * WPK / 4;            // V 16-byte chunks of a tile
+  static constexpr int VCH = (VTOT + kThreads - 1) / kThreads;  // ... per lane
+  static constexpr int RS = BN + 4;            // LDS row stride (words)
+  static constexpr int SBW = 4 * NG / 2;       // u32 words of 4 keys' scales
+  static_assert(VCH >= 1, "tile too small");
+  static_assert(RUN * 4 == GW, "lane runs must tile a group");
+  // LDS stage: K words, V words, K scales, K biases, V scales, V biases, mask
+  static constexpr int KT = BN * WPK * 4;              // bytes of a K (or V) tile
+  static constexpr int KT_I = (KT + 1023) / 1024;      // 16-byte-per-lane copies
+  // bytes of the last copy when a tile is not a whole number of copies
+  // (dim 96 at 4 bits: 1.5 KB); its lanes past that leave it alone
+  static constexpr int KT_TAIL = KT % 1024;
+  static constexpr int SBB = BN * NG * 2;              // bytes of one scale/bias slice
+  // the four slices back to back (4 SBB = 256 NG bytes) move in SB_I
+  // 4-byte-per-lane copies; lane l of copy i takes byte 256 i + 4 l of that
+  // region, i.e. slice (256 i + 4 l) / SBB
+  static constexpr int SB_I = 4 * SBB / 256;
+  static constexpr int SBP = SBB;
+  static constexpr int MB = 16 * BN * 2;               // mask cells of 16 rows
+  static constexpr int VL = WPK * RS * 4;              // V transpose area
+  static_assert(WPK % 4 == 0, "token rows of whole 16-byte chunks");
+};
+
+// Mask modes: none (implicit causal); an fp16 additive mask in 16-byte
+// copies (row starts and kv_seq_len multiples of 8 cells), 4-byte copies
+// (multiples of 2) or per-lane register loads (any alignment); or a u32
+// visibility mask ("ffai/flash_quantized_sdpa.rs", bool-mask macro) in
+// 16-byte copies of eight rows (row starts and kv_seq_len multiples of 4
+// cells) or 4-byte copies of two rows (any layout).
+enum { kMaskNone = 0, kMaskB128 = 1, kMaskB32 = 2, kMaskReg = 3, kMaskBool = 4,
+       kMaskBoolB128 = 5 };
+template <int DIM, int BITS, int G, int MM> struct QStage {
+  using S = QShape<DIM, BITS, G>;
+  static constexpr int MASK_I = MM == kMaskB128 ? 1 : MM == kMaskB32 ? 4
+                               : MM == kMaskBool ? 8 : MM == kMaskBoolB128 ? 2 : 0;
+  static constexpr int M_BYTES = (MM == kMaskBool || MM == kMaskBoolB128) ? 2 * S::MB
+                                 : (MM == kMaskB128 || MM == kMaskB32) ? S::MB : 0;
+  static constexpr int BYTES = 2 * S::KT + 4 * S::SBP + M_BYTES;
+  static constexpr int PER_TILE = 2 * S::KT_I + S::SB_I + MASK_I;
+  // Eight one-wavefront workgroups share a CU at dim <= 128 (two per SIMD),
+  // so a workgroup keeps within 20 KB of LDS there; wider heads run fewer.
+  static constexpr int BUDGET = DIM <= 128 ? 20 * 1024 : 48 * 1024;
+  static constexpr int NS = (3 * BYTES + S::VL <= BUDGET) ? 3 : 2;
+  static constexpr int LDS = NS * BYTES + S::VL;
+  static_assert(PER_TILE * (NS - 1) <= 63, "vmcnt range");
+};
+
+// Word index of (group g, step-in-group sub, part) for lane group gp.
+template <int DIM, int BITS, int G>
+__device__ inline uint32_t step_word(int g, int sub, uint32_t gp) {
+  using S = QShape<DIM, BITS, G>;
+  return (uint32_t)(g * S::GW) + gp * S::RUN + (uint32_t)(sub * S::WPS);
+}
+
+template <int DIM, int BITS, int G, int MM>
+__global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
+  using S = QShape<DIM, BITS, G>;
+  using ST = QStage<DIM, BITS, G, MM>;
+  constexpr bool IMPLICIT = MM == kMaskNone;
+  constexpr int NG = S::NG, STEPS = S::STEPS, DB = S::DB, NS = ST::NS;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) char *)lds);
+  uint32_t *vlds = reinterpret_cast<uint32_t *>(lds + NS * ST::BYTES);
+
+  uint32_t unit, rt;
+  decode_block(blockIdx.x, a.row_tiles, unit, rt);
+  if (unit >= a.units) return;
+  const uint32_t kv = unit / a.nwg;          // kv stream: b * nkv + hk
+  const uint32_t split = unit % a.nwg;
+  const uint32_t lane = threadIdx.x;
+  const uint32_t n = lane & 15u, gp = lane >> 4;
+
+  const uint32_t gr = rt * 16u + n;          // row: node * repeat + head-in-group
+  const bool valid = gr < a.rows;
+  const uint32_t node = valid ? gr / a.repeat : 0u;
+  const uint32_t qidx = kv * a.repeat + (valid ? gr % a.repeat : 0u);
+
+  // ---- Q as given (fp16, exact), in the K operand's slot order; the
+  // attention scale is applied to the fp32 dot products afterwards ----
+  half8_t qf[STEPS];
+  float qsum[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) qsum[g] = 0.0f;
+  {
+    const half_t *qrow = a.q + ((size_t)qidx * a.q_l + node) * DIM;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int sub = 0; sub < S::SPG; ++sub) {
+        const uint32_t w0 = step_word<DIM, BITS, G>(g, sub, gp);
+        half8_t f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          f[j] = valid ? qrow[slot_dim<BITS>(w0, j)] : (half_t)0.0f;
+          qsum[g] += (float)f[j];
+        }
+        qf[g * S::SPG + sub] = f;
+      }
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    qsum[g] += __shfl_xor(qsum[g], 16);
+    qsum[g] += __shfl_xor(qsum[g], 32);
+  }
+
+  const size_t kvrow0 = (size_t)kv * a.kv_capacity;
+  const uint32_t *KP = a.kp + kvrow0 * S::WPK;
+  const uint32_t *VP = a.vp + kvrow0 * S::WPK;
+  const half_t *KS = a.ks + kvrow0 * NG, *KB = a.kb + kvrow0 * NG;
+  const half_t *VS = a.vs + kvrow0 * NG, *VB = a.vb + kvrow0 * NG;
+  const half_t *mrow = (MM == kMaskReg) ? a.mask + (size_t)qidx * a.mask_head_stride +
+                                                (size_t)node * a.mask_stride
+                                          : nullptr;
+  const int64_t causal_last = (int64_t)a.kv_seq_len - (int64_t)a.q_l + (int64_t)node;
+  const uint32_t L = a.kv_seq_len;
+  // sliding window ("ffai/flash_quantized_sdpa.rs" causal / sliding-window
+  // gate): tokens below key_lo are never attended; the splits cover the
+  // tiles from the one that holds key_lo
+  const uint32_t klo = a.key_lo;
+  const uint32_t tile_lo = klo / BN;
+
+  // ---- per-tile registers ----
+  struct Tile {
+    uint32_t kw[2][NG][S::RUN];   // K words: key 16kb+n, group g
+    uint32_t ksb[2][2][S::SBW];   // K scales/biases: keys 16kb+4gp..+3, all groups
+    uint32_t vsb[2][2][S::SBW];   // V scales/biases: keys F(gp, 4h..4h+3)
+    u32x4 vw[S::VCH];             // V words for the LDS transpose
+    float m[2][4];                // mask cells (row n, keys 16kb+4gp+j)
+  };
+  // ---- copies of tile t into stage (t - t0) % NS ----
+  // Keys past kv_seq_len re-read row L - 1 (or the word that holds it), so
+  // that nothing outside the buffers is read; they are excluded below.
+  uint32_t t0, t1;
+  split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
+  t0 += tile_lo;
+  t1 += tile_lo;
+  const uint32_t t_first = t0;
+  auto stage_off = [&](uint32_t t) -> uint32_t { return ((t - t_first) % NS) * ST::BYTES; };
+  // mask row of the workgroup's row r (rows past the end reuse row 0)
+  auto mask_row = [&](uint32_t r) -> const half_t * {
+    uint32_t g2 = rt * 16u + r;
+    if (g2 >= a.rows) g2 = rt * 16u;
+    const uint32_t q2 = kv * a.repeat + g2 % a.repeat;
+    return a.mask + (size_t)q2 * a.mask_head_stride + (size_t)(g2 / a.repeat) * a.mask_stride;
+  };
+  // Per-lane source pointers of the copies: a tile's K words, V words and
+  // each scale/bias slice are contiguous in memory, so every copy of a full
+  // tile is the lane's pointer plus a wave-uniform tile offset.  A tile that
+  // reaches past kv_seq_len takes the clamped path instead.
+  const char *kp_l = reinterpret_cast<const char *>(KP) + 16u * lane;
+  const char *vp_l = reinterpret_cast<const char *>(VP) + 16u * lane;
+  const half_t *sarr[4] = {KS, KB, VS, VB};
+  const char *sb_l[S::SB_I];
+#pragma unroll
+  for (int i = 0; i < S::SB_I; ++i) {
+    const uint32_t o = 256u * i + 4u * lane;
+    sb_l[i] = reinterpret_cast<const char *>(sarr[o / S::SBB]) + o % S::SBB;
+  }
+  const half_t *mrow_l = nullptr;
+  if (MM == kMaskB128) mrow_l = mask_row(lane / 4u) + 8u * (lane % 4u);
+  // bool mask: copy i moves rows 2i, 2i + 1 (lane / 32), cell lane % 32
+  // (4-byte copies) or rows 8i .. 8i + 7 (lane / 8), cells 4 (lane % 8) ..
+  // + 3 (16-byte copies)
+  constexpr int MB_N = MM == kMaskBool ? 8 : MM == kMaskBoolB128 ? 2 : 1;
+  const uint32_t *mb_l[MB_N];
+  if (MM == kMaskBool || MM == kMaskBoolB128) {
+#pragma unroll
+    for (int i = 0; i < MB_N; ++i) {
+      uint32_t g2 = rt * 16u + (MM == kMaskBool ? 2u * i + lane / 32u : 8u * i + lane / 8u);
+      if (g2 >= a.rows) g2 = rt * 16u;   // rows past the end reuse row 0
+      const uint32_t q2 = kv * a.repeat + g2 % a.repeat;
+      mb_l[i] = a.mbool + (size_t)q2 * a.mask_head_stride + (size_t)(g2 / a.repeat) * a.mask_stride;
+    }
+  }
+  auto issue = [&](uint32_t t) {
+    const uint32_t key0 = t * BN;
+    const uint32_t sb = lds0 + stage_off(t);
+    if (key0 + BN <= L) {
+      const size_t kvo = (size_t)key0 * (4u * S::WPK);
+#pragma unroll
+      for (int i = 0; i < S::KT_I; ++i) {
+        if (S::KT_TAIL == 0 || i + 1 < S::KT_I || 16u * lane < (uint32_t)S::KT_TAIL) {
+          dma_b128(kp_l + kvo + 1024u * i, sb + 1024u * i);
+          dma_b128(vp_l + kvo + 1024u * i, sb + S::KT + 1024u * i);
+        }
+      }
+      const size_t so = (size_t)key0 * (2u * NG);
+#pragma unroll
+      for (int i = 0; i < S::SB_I; ++i) dma_b32(sb_l[i] + so, sb + 2u * S::KT + 256u * i);
+    } else {
+      // keys past kv_seq_len re-read row L - 1 (or the word that holds it)
+#pragma unroll
+      for (int i = 0; i < S::KT_I; ++i) {
+        const uint32_t o = 1024u * i + 16u * lane;
+        if (S::KT_TAIL == 0 || o < (uint32_t)S::KT) {
+          uint32_t key = key0 + o / (4u * S::WPK);
+          if (key >= L) key = L - 1u;
+          const size_t go = (size_t)key * (4u * S::WPK) + o % (4u * S::WPK);
+          dma_b128(reinterpret_cast<const char *>(KP) + go, sb + 1024u * i);
+          dma_b128(reinterpret_cast<const char *>(VP) + go, sb + S::KT + 1024u * i);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < S::SB_I; ++i) {
+        const uint32_t o = 256u * i + 4u * lane;
+        const uint32_t h = (o % S::SBB) / 2u;               // first half of the word
+        uint32_t key = key0 + h / NG;
+        if (key >= L) key = NG == 1 ? ((L - 1u) & ~1u) : L - 1u;
+        dma_b32(sarr[o / S::SBB] + (size_t)key * NG + h % NG, sb + 2u * S::KT + 256u * i);
+      }
+    }
+    if (MM == kMaskB128) {
+      // lane: row lane / 4, cells 8 (lane % 4) .. + 7
+      if (key0 + BN <= L) {
+        dma_b128(mrow_l + key0, sb + 2u * S::KT + 4u * S::SBP);
+      } else {
+        uint32_t key = key0 + 8u * (lane % 4u);
+        if (key >= L) key = L - 8u;
+        dma_b128(mask_row(lane / 4u) + key, sb + 2u * S::KT + 4u * S::SBP);
+      }
+    } else if (MM == kMaskB32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // lane: row 4i + lane / 16, cells 2 (lane % 16), + 1
+        uint32_t key = key0 + 2u * (lane % 16u);
+        if (key >= L) key = L - 2u;
+        dma_b32(mask_row(4u * i + lane / 16u) + key, sb + 2u * S::KT + 4u * S::SBP + 256u * i);
+      }
+    } else if (MM == kMaskBool) {
+      // past kv_seq_len: re-read cell L - 1 of the row (never used)
+      const uint32_t cell = min(key0 + lane % 32u, L - 1u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma_b32(mb_l[i] + cell, sb + 2u * S::KT + 4u * S::SBP + 256u * i);
+    } else if (MM == kMaskBoolB128) {
+      // past kv_seq_len (a multiple of 4): re-read cells L - 4 .. L - 1
+      uint32_t cell = key0 + 4u * (lane % 8u);
+      if (cell >= L) cell = L - 4u;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma_b128(mb_l[i] + cell, sb + 2u * S::KT + 4u * S::SBP + 1024u * i);
+    }
+  };
+  // wait until tile t has landed; `after` later tiles (0 .. NS - 1) may
+  // stay in flight
+  auto wait_tile = [&](uint32_t after) {
+    if (NS >= 3 && after >= 2)
+      wait_vm<(NS >= 3 ? 2 * ST::PER_TILE : 0)>();
+    else if (after >= 1)
+      wait_vm<ST::PER_TILE>();
+    else
+      wait_vm<0>();
+  };
+  auto load_tile = [&](uint32_t t, Tile &T) {
+    const uint32_t key0 = t * BN;
+    const char *st = lds + stage_off(t);
+    const uint32_t *Kl = reinterpret_cast<const uint32_t *>(st);
+    const uint32_t *Vl = reinterpret_cast<const uint32_t *>(st + S::KT);
+    const uint32_t *SBl[4];
+#pragma unroll
+    for (int arr = 0; arr < 4; ++arr)
+      SBl[arr] = reinterpret_cast<const uint32_t *>(st + 2 * S::KT + arr * S::SBP);
+    const half_t *Ml = reinterpret_cast<const half_t *>(st + 2 * S::KT + 4 * S::SBP);
+    const uint32_t *Mb = reinterpret_cast<const uint32_t *>(st + 2 * S::KT + 4 * S::SBP);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t kr = 16u * kb + n;   // key within the tile
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int r = 0; r < S::RUN; ++r)
+          T.kw[kb][g][r] = Kl[kr * S::WPK + g * S::GW + gp * S::RUN + r];
+      // scales/biases of keys 16kb + 4gp + 0..3 (K side) and
+      // 16h + 4gp + 0..3 (V side, the keys of B-operand half h)
+      const uint32_t k4 = 16u * kb + 4u * gp;
+#pragma unroll
+      for (int w = 0; w < S::SBW; ++w) {
+        const uint32_t wi = (k4 * NG) / 2u + w;
+        T.ksb[kb][0][w] = SBl[0][wi];
+        T.ksb[kb][1][w] = SBl[1][wi];
+        T.vsb[kb][0][w] = SBl[2][wi];
+        T.vsb[kb][1][w] = SBl[3][wi];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kk = key0 + k4 + j;
+        float mv;
+        const bool in = valid && kk < L && kk >= klo;
+        if (IMPLICIT) {
+          mv = (in && (int64_t)kk <= causal_last) ? 0.0f : kMasked;
+        } else if (MM == kMaskReg) {
+          mv = in ? (float)mrow[kk] : kMasked;
+        } else if (MM == kMaskBool || MM == kMaskBoolB128) {
+          mv = (in && Mb[n * BN + k4 + j] != 0u) ? 0.0f : kMasked;
+        } else {
+          const float x = (float)Ml[n * BN + k4 + j];  // always in the stage
+          mv = in ? x : kMasked;
+        }
+        T.m[kb][j] = mv;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < S::VCH; ++u) {
+      const uint32_t c = lane + kThreads * u;
+      const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
+      T.vw[u] = (S::VTOT % kThreads == 0 || c < (uint32_t)S::VTOT)
+                    ? *reinterpret_cast<const u32x4 *>(Vl + key * S::WPK + 4 * q4)
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // V words -> LDS [word][position]; position of key (16h + 4g4 + j) is
+  // 8*g4 + 4h + j, so that lane group gp later reads its 8 keys contiguously.
+  auto store_v = [&](const Tile &T) {
+#pragma unroll
+    for (int u = 0; u < S::VCH; ++u) {
+      const uint32_t c = lane + kThreads * u;
+      if (S::VTOT % kThreads != 0 && c >= (uint32_t)S::VTOT) continue;
+      const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
+      const uint32_t pos = 8u * ((key & 15u) >> 2) + 4u * (key >> 4) + (key & 3u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vlds[(4 * q4 + e) * S::RS + pos] = T.vw[u][e];
+    }
+  };
+
+  // ---- online-softmax state of the lane's row ----
+  float Mrow = -INFINITY, Srow = 0.0f;
+  float pb[NG];                     // sum_t p_t * vbias_tg (lane's keys)
+#pragma unroll
+  for (int g = 0; g < NG; ++g) pb[g] = 0.0f;
+  floatx4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (a.sinks != nullptr && split == 0 && valid) {
+    // the sink: a virtual key with raw logit sinks[h] and value zero
+    Mrow = a.sinks[qidx % a.nq] * kLog2e;
+    Srow = (gp == 0) ? 1.0f : 0.0f;
+  }
+
+  const uint32_t vshift = (BITS == 4) ? 4u * (n & 7u) : 8u * (n & 3u);
+  const uint32_t vmask = (1u << BITS) - 1u;
+  const uint32_t cmask = code_pair_mask<BITS>();
+
+  auto compute = [&](const Tile &T) {
+    // scores, one accumulator per scale group
+    floatx4 sacc[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[g][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sub = 0; sub < S::SPG; ++sub) {
+          half8_t kf = word_codes<BITS>(&T.kw[kb][g][sub * S::WPS], cmask);
+          sacc[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[g * S::SPG + sub],
+                                                               sacc[g][kb], 0, 0, 0);
+        }
+      }
+    float s[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const half_t *ksc = reinterpret_cast<const half_t *>(T.ksb[kb][0]);
+      const half_t *kbi = reinterpret_cast<const half_t *>(T.ksb[kb][1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          x = fmaf((float)ksc[j * NG + g], sacc[g][kb][j], x);
+          x = fmaf((float)kbi[j * NG + g], qsum[g], x);
+        }
+        const float mv = T.m[kb][j];
+        x = (mv > kMasked) ? fmaf(x, a.qscale, mv * kLog2e) : -INFINITY;
+        s[kb][j] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(Mrow, tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(Mrow - m_use);
+    float p[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(s[0][j] - m_use);
+      p[4 + j] = __builtin_amdgcn_exp2f(s[1][j] - m_use);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) psum += p[j];
+    Srow = Srow * alpha + psum;
+    Mrow = m_new;
+    // B operands p * vscale_g as an fp16 pair hi + lo (the pair carries
+    // about 22 bits of the fp32 product, so the fp16 operand width does not
+    // limit the result), and the bias sums
+    half8_t pf[NG], pl[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const half_t *vsc = reinterpret_cast<const half_t *>(T.vsb[j >> 2][0]);
+        const half_t *vbi = reinterpret_cast<const half_t *>(T.vsb[j >> 2][1]);
+        const float w = p[j] * (float)vsc[(j & 3) * NG + g];
+        const half_t hi = (half_t)w;
+        pf[g][j] = hi;
+        pl[g][j] = (half_t)(w - (float)hi);
+        acc = fmaf(p[j], (float)vbi[(j & 3) * NG + g], acc);
+      }
+      pb[g] = pb[g] * alpha + acc;
+    }
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    // PV: A = V codes of dim 16db+n for the lane's 8 keys (from LDS)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint32_t w = (16u * db + n) * BITS / 32u;
+      const u32x4 lo = *reinterpret_cast<const u32x4 *>(&vlds[w * S::RS + 8u * gp]);
+      const u32x4 hi = *reinterpret_cast<const u32x4 *>(&vlds[w * S::RS + 8u * gp + 4u]);
+      uint32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = (lo[j] >> vshift) & vmask;
+        c[4 + j] = (hi[j] >> vshift) & vmask;
+      }
+      u32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = codes_to_h2(c[2 * e] | (c[2 * e + 1] << 16));
+      const int g = (16 * db) / G;
+      const half8_t vf = __builtin_bit_cast(half8_t, r);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[g], oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[g], oacc[db], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop: tile t from LDS while tiles t + 1 .. t + NS land ----
+  // A tile's stage is copied whole into registers (load_tile), so the copies
+  // of tile t + NS go into tile t's own stage as soon as those reads have
+  // returned: NS tiles stay in flight behind the arithmetic.
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (t0 + i < t1) issue(t0 + i);
+  Tile cur;
+  for (uint32_t t = t0; t < t1; ++t) {
+    wait_tile(min(t1 - 1u - t, (uint32_t)(NS - 1)));
+    load_tile(t, cur);
+    // the reads of tile t's stage have returned before copies refill it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t + NS < t1) issue(t + NS);
+    int live = 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) live |= (cur.m[kb][j] > kMasked);
+    if (__any(live)) {
+      __builtin_amdgcn_wave_barrier();
+      store_v(cur);
+      __builtin_amdgcn_wave_barrier();
+      compute(cur);
+    }
+  }
+
+  // ---- results ----
+  float stot = Srow + __shfl_xor(Srow, 16);
+  stot += __shfl_xor(stot, 32);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    pb[g] += __shfl_xor(pb[g], 16);
+    pb[g] += __shfl_xor(pb[g], 32);
+  }
+  if (!valid) return;
+  const size_t rid = (size_t)qidx * a.q_l + node;
+  // lane holds O[d = 16db + 4gp + j] of its row
+  if (a.nwg == 1) {
+    const float inv = (stot > 0.0f) ? 1.0f / stot : 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int g = (16 * db) / G;
+      floatx4 o = (oacc[db] + pb[g]) * inv;
+      half4_t h = {(half_t)o[0], (half_t)o[1], (half_t)o[2], (half_t)o[3]};
+      *reinterpret_cast<half4_t *>(a.out + rid * DIM + 16 * db + 4 * gp) = h;
+    }
+  } else {
+    const size_t nrows = (size_t)a.batch * a.nq * a.q_l;
+    const size_t prow = (size_t)split * nrows + rid;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int g = (16 * db) / G;
+      *reinterpret_cast<floatx4 *>(a.part_o + prow * DIM + 16 * db + 4 * gp) = oacc[db] + pb[g];
+    }
+    if (gp == 0) {
+      a.part_sm[prow * 2 + 0] = stot;
+      a.part_sm[prow * 2 + 1] = Mrow;
+    }
+  }
+}
+
+template <int DIM, int BITS, int G, int MM>
+hipError_t launch_qm(const QuantArgs &a, hipStream_t s) {
+  using ST = QStage<DIM, BITS, G, MM>;
+  static const bool attr_set = [] {
+    (void)hipFuncSetAttribute((const void *)quant_kernel<DIM, BITS, G, MM>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    return true;
+  }();
+  (void)attr_set;
+  dim3 grid(grid_size(a.units, a.row_tiles));
+  hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, MM>), grid, dim3(kThreads), ST::LDS, s, a);
+  return hipGetLastError();
+}
+
+template <int DIM, int BITS, int G>
+hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
+  if (a.mbool != nullptr) {
+    const uint64_t words = a.mask_head_stride | a.mask_stride | a.kv_seq_len |
+                           (uint64_t)((uintptr_t)a.mbool / sizeof(uint32_t));
+    if (words % 4 == 0) return launch_qm<DIM, BITS, G, kMaskBoolB128>(a, s);
+    return launch_qm<DIM, BITS, G, kMaskBool>(a, s);
+  }
+  if (a.mask == nullptr) return launch_qm<DIM, BITS, G, kMaskNone>(a, s);
+  const uint64_t all = a.mask_head_stride | a.mask_stride | a.kv_seq_len |
+                       (uint64_t)((uintptr_t)a.mask / sizeof(half_t));
+  if (all % 8 == 0) return launch_qm<DIM, BITS, G, kMaskB128>(a, s);
+  if (all % 2 == 0) return launch_qm<DIM, BITS, G, kMaskB32>(a, s);
+  return launch_qm<DIM, BITS, G, kMaskReg>(a, s);
+}
+
+template <int DIM, int BITS>
+hipError_t launch_qg(const QuantArgs &a, uint32_t G, hipStream_t s) {
+  switch (G) {
+    case 32: return launch_q<DIM, BITS, 32>(a, s);
+    case 64:
+      if constexpr (DIM % 64 == 0) return launch_q<DIM, BITS, 64>(a, s);
+      return hipErrorInvalidValue;
+    case 128:
+      if constexpr (DIM % 128 == 0) return launch_q<DIM, BITS, 128>(a, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DIM>
+hipError_t launch_qb(const QuantArgs &a, uint32_t bits, uint32_t G, hipStream_t s) {
+  return bits == 4 ? launch_qg<DIM, 4>(a, G, s) : launch_qg<DIM, 8>(a, G, s);
+}
+
+// Workgroups of one variant a CU holds: the runtime's occupancy answer for
+// the kernel with its LDS, or, with no device to ask, the plan's budgets
+// (two wavefronts per SIMD up to dim 128, one above; 160 KB of LDS).
+template <int DIM, int BITS, int G, int MM>
+uint32_t wgs_per_cu() {
+  using ST = QStage<DIM, BITS, G, MM>;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_kernel<DIM, BITS, G, MM>, kThreads,
+                                                   ST::LDS) == hipSuccess &&
+      n > 0)
+    return (uint32_t)n;
+  (void)hipGetLastError();
+  const uint32_t by_regs = DIM <= 128 ? 8u : 4u;
+  const uint32_t by_lds = (160u * 1024u) / (uint32_t)ST::LDS;
+  return by_regs < by_lds ? by_regs : by_lds;
+}
+
+template <int DIM, int BITS, int G>
+uint32_t wgs_per_cu_m(int mask_kind) {
+  // the fp16 mask's copy modes share one footprint (the register-load mode
+  // is smaller); both u32 copy modes share one too
+  if (mask_kind == 2) return wgs_per_cu<DIM, BITS, G, kMaskBoolB128>();
+  if (mask_kind == 1) return wgs_per_cu<DIM, BITS, G, kMaskB128>();
+  return wgs_per_cu<DIM, BITS, G, kMaskNone>();
+}
+
+template <int DIM, int BITS>
+uint32_t wgs_per_cu_g(uint32_t G, int mask_kind) {
+  switch (G) {
+    case 32: return wgs_per_cu_m<DIM, BITS, 32>(mask_kind);
+    case 64:
+      if constexpr (DIM % 64 == 0) return wgs_per_cu_m<DIM, BITS, 64>(mask_kind);
+      return 0;
+    case 128:
+      if constexpr (DIM % 128 == 0) return wgs_per_cu_m<DIM, BITS, 128>(mask_kind);
+      return 0;
+    default: return 0;
+  }
+}
+
+template <int DIM>
+uint32_t wgs_per_cu_b(uint32_t bits, uint32_t G, int mask_kind) {
+  return bits == 4 ? wgs_per_cu_g<DIM, 4>(G, mask_kind)
+                   : bits == 8 ? wgs_per_cu_g<DIM, 8>(G, mask_kind) : 0;
+}
+
+}  // namespace
+}  // namespace ta
