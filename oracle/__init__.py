@@ -90,7 +90,9 @@ def _load():
                                                 U, U, U, U, U, ctypes.c_double,
                                                 P, U, P, ctypes.c_int]
             lib.orc_quant_attention.restype = ctypes.c_int
-            lib.orc_quant_attention_ex.argtypes = [P, P, P, P, P, P, P, P, P, P,
+            lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
+            lib.orc_bf16_to_f64.restype = ctypes.c_double
+            lib.orc_quant_attention_ex.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, P,
                                                    ctypes.c_uint64, U, U, U, U,
                                                    U, U, U, U, U, U, U,
                                                    ctypes.c_double, P, U, P,
@@ -229,10 +231,16 @@ def lse_combine(o_un, s, m):
     return out
 
 
+def bf16_to_f64(bits):
+    """bfloat16 bit pattern -> float64, exactly (the oracle's decoder)."""
+    return _load().orc_bf16_to_f64(int(bits))
+
+
 def quant_attention(q, k_packed, k_scales, k_biases, v_packed, v_scales,
                     v_biases, *, n_kv_heads, kv_seq_len, bits, group_size, scale,
                     sinks=None, mask=None, mask_bool=None, mask_head_stride=0,
-                    mask_stride=None, window_size=0, rows=None, nthreads=None):
+                    mask_stride=None, window_size=0, elem="f16", rows=None,
+                    nthreads=None):
     """Affine-quantized K/V attention in double ("ffai/flash_quantized_sdpa.rs").
 
     q: [B*nQ, q_l, dim] float16.  k_packed: [B*nKV, cap, dim/(32/bits)] uint32.
@@ -243,23 +251,28 @@ def quant_attention(q, k_packed, k_scales, k_biases, v_packed, v_scales,
     None; at most one of mask and mask_bool.  window_size: W > 0 keeps only
     tokens t with t + W > kv_seq_len - 1 (the bool- and float-mask macros'
     sliding-window gate); 0 keeps all.
+    elem: the element type of q, the scales, biases and float mask -- "f16"
+    (float16 arrays), "bf16" (uint16 arrays of bfloat16 bit patterns) or
+    "f32" (float32 arrays).
     Returns [B*nQ, q_l, dim] float64 or [len(rows), dim] for (q_idx, i) rows.
     """
-    q = _c(q, np.float16)
+    code = {"f16": 0, "bf16": 1, "f32": 2}[elem]
+    et = {"f16": np.float16, "bf16": np.uint16, "f32": np.float32}[elem]
+    q = _c(q, et)
     BnQ, q_l, dim = q.shape
     k_packed = _c(k_packed, np.uint32)
     v_packed = _c(v_packed, np.uint32)
-    k_scales = _c(k_scales, np.float16)
-    k_biases = _c(k_biases, np.float16)
-    v_scales = _c(v_scales, np.float16)
-    v_biases = _c(v_biases, np.float16)
+    k_scales = _c(k_scales, et)
+    k_biases = _c(k_biases, et)
+    v_scales = _c(v_scales, et)
+    v_biases = _c(v_biases, et)
     BnKV, cap, _ = k_packed.shape
     batch = BnKV // n_kv_heads
     nq = BnQ // batch
     if sinks is not None:
         sinks = _c(sinks, np.float32)
     if mask is not None:
-        mask = _c(mask, np.float16)
+        mask = _c(mask, et)
     if mask_bool is not None:
         mask_bool = _c(mask_bool, np.uint32)
     stride = kv_seq_len if mask_stride is None else int(mask_stride)
@@ -270,9 +283,9 @@ def quant_attention(q, k_packed, k_scales, k_biases, v_packed, v_scales,
         sel = np.ascontiguousarray(np.asarray(rows, dtype=np.uint32).reshape(-1, 2))
         nsel = sel.shape[0]
         out = np.empty((nsel, dim), dtype=np.float64)
-    h = lambda a: None if a is None else a.view(np.uint16)
+    h = lambda a: a
     rc = _load().orc_quant_attention_ex(
-        _ptr(h(q)), _ptr(k_packed), _ptr(h(k_scales)), _ptr(h(k_biases)),
+        code, _ptr(h(q)), _ptr(k_packed), _ptr(h(k_scales)), _ptr(h(k_biases)),
         _ptr(v_packed), _ptr(h(v_scales)), _ptr(h(v_biases)), _ptr(sinks),
         _ptr(h(mask)), _ptr(mask_bool), int(mask_head_stride), stride,
         int(window_size), batch, nq, n_kv_heads, dim, kv_seq_len, cap, q_l, bits,

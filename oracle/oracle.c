@@ -83,6 +83,23 @@ double orc_f16_to_f64(uint16_t h)
     return sign ? -v : v;
 }
 
+/* bfloat16 -> double, exactly, from its bit fields: 1 sign bit, 8 exponent
+ * bits (bias 127), 7 mantissa bits, the upper half of an IEEE binary32. */
+double orc_bf16_to_f64(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xff;
+    int m = b & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -133);            /* subnormal: m/128 * 2^-126 */
+    else if (e == 255)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + m), e - 134); /* (1 + m/128) * 2^(e-127) */
+    return sign ? -v : v;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Tree topology -> explicit mask.                                          */
 /* [TA] header: chains, fixed trees and dynamic trees all become a          */
@@ -425,22 +442,25 @@ int orc_lse_combine(const double *o_un, const double *s, const double *m,
 
 /* ------------------------------------------------------------------------ */
 /* Affine-quantized K/V attention ([FQS]).                                  */
-/* q        [B*nQ, q_l, dim] f16 bits                                        */
+/* The element type T ([FQS] kernels are generic in T) of q, the scales,   */
+/* the biases and the float mask: elem 0 = f16, 1 = bf16, 2 = f32.          */
+/* q        [B*nQ, q_l, dim] T                                               */
 /* k_packed [B*nKV, kv_capacity, dim/pf] u32, pf = 32/bits                   */
-/* k_scales, k_biases [B*nKV, kv_capacity, dim/G] f16 bits; V the same       */
+/* k_scales, k_biases [B*nKV, kv_capacity, dim/G] T; V the same              */
 /* sinks    [nQ] f32 or NULL                                                 */
-/* mask     f16 bits, cell (q_idx, i, t) at                                  */
+/* mask     T, cell (q_idx, i, t) at                                         */
 /*          q_idx*mask_head_stride + i*mask_stride + t, or NULL (R-Q)        */
 /* out      [B*nQ, q_l, dim] in double                                       */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-    const uint16_t *q;
+    const void *q;
     const uint32_t *kp;
-    const uint16_t *ks, *kb;
+    const void *ks, *kb;
     const uint32_t *vp;
-    const uint16_t *vs, *vb;
+    const void *vs, *vb;
     const float *sinks;
-    const uint16_t *mask;
+    const void *mask;
+    int elem;                  /* 0 f16, 1 bf16, 2 f32 */
     const uint32_t *mask_bool; /* R-B; at most one of mask, mask_bool */
     uint32_t window;           /* R-W */
     uint64_t mask_head_stride;
@@ -451,10 +471,20 @@ typedef struct {
     double *out;
 } orc_q_problem;
 
+/* Element idx of a T array, exactly. */
+static double q_elem(const orc_q_problem *p, const void *base, size_t idx)
+{
+    if (p->elem == 1)
+        return orc_bf16_to_f64(((const uint16_t *)base)[idx]);
+    if (p->elem == 2)
+        return (double)((const float *)base)[idx];
+    return orc_f16_to_f64(((const uint16_t *)base)[idx]);
+}
+
 /* Dequantised element d of token t of kv stream kv ([FQS] base macro):
  * x = scale_g * code + bias_g with code = (word >> shift) & (2^bits - 1). */
-static double q_dequant(const uint32_t *packed, const uint16_t *scales,
-                        const uint16_t *biases, const orc_q_problem *p,
+static double q_dequant(const uint32_t *packed, const void *scales,
+                        const void *biases, const orc_q_problem *p,
                         uint32_t kv, uint32_t t, uint32_t d)
 {
     uint32_t pf = 32u / p->bits;
@@ -463,8 +493,8 @@ static double q_dequant(const uint32_t *packed, const uint16_t *scales,
     size_t tok = (size_t)kv * p->kv_capacity + t;
     uint32_t word = packed[tok * words + d / pf];
     uint32_t code = (word >> ((d % pf) * p->bits)) & ((1u << p->bits) - 1u);
-    double sc = orc_f16_to_f64(scales[tok * ngroups + d / p->group]);
-    double bi = orc_f16_to_f64(biases[tok * ngroups + d / p->group]);
+    double sc = q_elem(p, scales, tok * ngroups + d / p->group);
+    double bi = q_elem(p, biases, tok * ngroups + d / p->group);
     return sc * (double)code + bi;
 }
 
@@ -473,7 +503,7 @@ static double q_mask_cell(const orc_q_problem *p, uint32_t q_idx, uint32_t i,
 {
     size_t cell = (size_t)q_idx * p->mask_head_stride + (size_t)i * p->mask_stride + t;
     if (p->mask)
-        return orc_f16_to_f64(p->mask[cell]);
+        return q_elem(p, p->mask, cell);
     if (p->mask_bool)
         return p->mask_bool[cell] != 0u ? 0.0 : ORC_MASKED; /* R-B */
     int64_t last = (int64_t)p->kv_seq_len - (int64_t)p->q_l + (int64_t)i;
@@ -490,10 +520,10 @@ static int q_logit(const orc_q_problem *p, uint32_t q_idx, uint32_t i,
     if (m <= ORC_MASKED)
         return 0;
     uint32_t kv = q_idx / (p->nq / p->nkv); /* [FQS]: q_idx / repeat_count */
-    const uint16_t *qrow = p->q + ((size_t)q_idx * p->q_l + i) * p->dim;
+    size_t qrow = ((size_t)q_idx * p->q_l + i) * p->dim;
     double dot = 0.0;
     for (uint32_t d = 0; d < p->dim; ++d)
-        dot += orc_f16_to_f64(qrow[d]) *
+        dot += q_elem(p, p->q, qrow + d) *
                q_dequant(p->kp, p->ks, p->kb, p, kv, t, d);
     *logit = p->scale * dot + m;
     return 1;
@@ -548,11 +578,11 @@ static void q_row(void *vctx, uint32_t r)
  * (f16 bits) and mask_bool (u32) share the cell layout; at most one may be
  * given.  window: R-W.  Returns 0, or -1 on an invalid problem.
  */
-int orc_quant_attention_ex(const uint16_t *q, const uint32_t *k_packed,
-                           const uint16_t *k_scales, const uint16_t *k_biases,
-                           const uint32_t *v_packed, const uint16_t *v_scales,
-                           const uint16_t *v_biases, const float *sinks,
-                           const uint16_t *mask, const uint32_t *mask_bool,
+int orc_quant_attention_ex(int elem, const void *q, const uint32_t *k_packed,
+                           const void *k_scales, const void *k_biases,
+                           const uint32_t *v_packed, const void *v_scales,
+                           const void *v_biases, const float *sinks,
+                           const void *mask, const uint32_t *mask_bool,
                            uint64_t mask_head_stride, uint32_t mask_stride,
                            uint32_t window, uint32_t batch, uint32_t n_q_heads,
                            uint32_t n_kv_heads, uint32_t dim, uint32_t kv_seq_len,
@@ -569,6 +599,8 @@ int orc_quant_attention_ex(const uint16_t *q, const uint32_t *k_packed,
     if (group_size == 0 || dim % group_size || dim % (32u / bits))
         return -1;
     if (mask && mask_bool)
+        return -1;
+    if (elem < 0 || elem > 2)
         return -1;
     if ((mask || mask_bool) && mask_stride < kv_seq_len)
         return -1;
@@ -587,6 +619,7 @@ int orc_quant_attention_ex(const uint16_t *q, const uint32_t *k_packed,
     p.vb = v_biases;
     p.sinks = sinks;
     p.mask = mask;
+    p.elem = elem;
     p.mask_bool = mask_bool;
     p.window = window;
     p.mask_head_stride = mask_head_stride;
@@ -620,7 +653,7 @@ int orc_quant_attention(const uint16_t *q, const uint32_t *k_packed,
                         uint32_t group_size, double scale, const uint32_t *sel,
                         uint32_t nsel, double *out, int nthreads)
 {
-    return orc_quant_attention_ex(q, k_packed, k_scales, k_biases, v_packed,
+    return orc_quant_attention_ex(0, q, k_packed, k_scales, k_biases, v_packed,
                                   v_scales, v_biases, sinks, mask, NULL,
                                   mask_head_stride, mask_stride, 0u, batch,
                                   n_q_heads, n_kv_heads, dim, kv_seq_len,

@@ -39,8 +39,13 @@ MUTATIONS = [
      "v = ldexp((double)(1024 + m), e - 24);", 0),
     ("code_order_reversed", "uint32_t code = (word >> ((d % pf) * p->bits))",
      "uint32_t code = (word >> ((pf - 1 - d % pf) * p->bits))", 0),
-    ("group_index_modulo", "double sc = orc_f16_to_f64(scales[tok * ngroups + d / p->group]);",
-     "double sc = orc_f16_to_f64(scales[tok * ngroups + (d / p->group + 1) % ngroups]);", 0),
+    ("group_index_modulo", "double sc = q_elem(p, scales, tok * ngroups + d / p->group);",
+     "double sc = q_elem(p, scales, tok * ngroups + (d / p->group + 1) % ngroups);", 0),
+    ("bf16_exponent_bias", "v = ldexp((double)(128 + m), e - 134);",
+     "v = ldexp((double)(128 + m), e - 133);", 0),
+    ("bf16_mantissa_width", "int m = b & 0x7f;", "int m = b & 0x3f;", 0),
+    ("f32_read_as_f16", "        return (double)((const float *)base)[idx];",
+     "        return orc_f16_to_f64(((const uint16_t *)base)[idx]);", 0),
     ("bias_dropped", "return sc * (double)code + bi;", "return sc * (double)code;", 0),
     ("sink_scaled", "sink = (double)p->sinks[q_idx % p->nq]; /* R12 */",
      "sink = p->scale * (double)p->sinks[q_idx % p->nq]; /* R12 */", 0),

@@ -324,3 +324,82 @@ def test_window_not_shorter_than_sequence_is_no_window():
     for W in (30, 31, 1000):
         assert np.array_equal(qrun(c, window_size=W), qrun(c))
     assert not np.array_equal(qrun(c, window_size=29), qrun(c))
+
+
+# ---- element types bf16 and f32 (the page's kernels are generic in T) ----
+
+def test_bf16_decode_known_patterns():
+    # bfloat16 = the upper half of an IEEE binary32
+    known = {0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x4049: 3.140625,
+             0x3E80: 0.25, 0x0000: 0.0, 0x7F7F: 3.3895313892515355e38,
+             0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x42F6: 123.0}
+    for bits, val in known.items():
+        assert oracle.bf16_to_f64(bits) == val, hex(bits)
+    assert oracle.bf16_to_f64(0x7F80) == np.inf
+    assert np.isnan(oracle.bf16_to_f64(0x7FC0))
+
+
+def test_bf16_decode_exhaustive_against_f32_upper_half():
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):   # NaN patterns
+        ref = (bits << np.uint32(16)).view(np.float32).astype(np.float64)
+    got = np.array([oracle.bf16_to_f64(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def _as(c, elem):
+    """The same values re-expressed in another element type (exact)."""
+    d = dict(c)
+    for n in ("q", "k_scales", "k_biases", "v_scales", "v_biases", "mask"):
+        if d.get(n) is None:
+            continue
+        x = np.asarray(d[n], dtype=np.float32)
+        d[n] = inputs.to_bf16_bits(x) if elem == "bf16" else x.astype(np.float32)
+    d["elem"] = elem
+    return d
+
+
+def qrun_e(c, **kw):
+    return qrun(c, elem=c.get("elem", "f16"), **kw)
+
+
+@pytest.mark.parametrize("elem", ["bf16", "f32"])
+def test_element_types_agree_on_values_all_can_hold(elem):
+    # values with 8 significant bits and a modest exponent are exact in f16,
+    # bf16 and f32 alike: the three element types must give the same result
+    c = qcase(30, B=1, nQ=4, nKV=2, dim=64, L=41, q_l=2, bits=4, G=32,
+              sinks=True, mask="alibi")
+    for n in ("q", "k_scales", "k_biases", "v_scales", "v_biases", "mask"):
+        x = np.asarray(c[n], dtype=np.float32)
+        x = np.where(np.abs(x) < 2.0 ** -14, 0.0, x).astype(np.float32)  # f16 normals only
+        b = inputs.to_bf16_bits(x).astype(np.uint32) << np.uint32(16)
+        c[n] = b.view(np.float32).astype(np.float16)    # 8 significant bits
+    assert np.array_equal(qrun_e(_as(c, elem)), qrun_e(c))
+
+
+@pytest.mark.parametrize("elem,bits,G", [("bf16", 4, 32), ("bf16", 8, 64), ("f32", 4, 64),
+                                         ("f32", 8, 32)])
+def test_element_types_match_brute_force(elem, bits, G):
+    c = qcase(31, B=2, nQ=4, nKV=2, dim=64, L=53, q_l=2, bits=bits, G=G,
+              sinks=True, mask="alibi")
+    c = inputs.quant_case(dict(batch=2, n_q_heads=4, n_kv_heads=2, dim=64,
+                               kv_seq_len=53, kv_capacity=53, q_l=2, bits=bits,
+                               group_size=G, sinks=True, mask="alibi", elem=elem),
+                          seed=31)
+    ref = _brute_quant(_decoded(c))
+    np.testing.assert_allclose(qrun_e(c), ref, rtol=0, atol=1e-12)
+
+
+def _decoded(c):
+    """float64 copies of the T-typed arrays for the numpy brute force."""
+    d = dict(c)
+    for n in ("q", "k_scales", "k_biases", "v_scales", "v_biases", "mask"):
+        if d.get(n) is None:
+            continue
+        x = np.asarray(d[n])
+        if c["elem"] == "bf16":
+            x = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        d[n] = x.astype(np.float64)
+    return d

@@ -161,16 +161,38 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     return words
 
 
-def alibi_bias(n_q_heads: int, batch: int, tokens: int, q_l: int = 1) -> np.ndarray:
-    """Synthetic ALiBi-style additive bias, f16 [batch*nQ, q_l, tokens]:
-    slope_h = 2^(-8 (h+1) / nQ), bias = slope_h * (t - (tokens - q_l + i))."""
+def to_bf16_bits(x) -> np.ndarray:
+    """float -> bfloat16 bit patterns (uint16), rounded to nearest even."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def to_elem(x, elem: str) -> np.ndarray:
+    """Round values to the element type of the quantized path's Q, scales,
+    biases and float mask: "f16" (float16), "bf16" (uint16 bit patterns) or
+    "f32" (float32)."""
+    if elem == "f16":
+        return np.asarray(x).astype(np.float16)
+    if elem == "bf16":
+        return to_bf16_bits(np.asarray(x, dtype=np.float32))
+    return np.asarray(x).astype(np.float32)
+
+
+def alibi_bias(n_q_heads: int, batch: int, tokens: int, q_l: int = 1,
+               elem: str = "f16") -> np.ndarray:
+    """Synthetic ALiBi-style additive bias [batch*nQ, q_l, tokens] in the
+    element type: slope_h = 2^(-8 (h+1) / nQ), bias = slope_h * (t - (tokens
+    - q_l + i))."""
     h = np.arange(n_q_heads, dtype=np.float64)
     slope = 2.0 ** (-8.0 * (h + 1.0) / n_q_heads)
     t = np.arange(tokens, dtype=np.float64)
-    out = np.empty((batch * n_q_heads, q_l, tokens), dtype=np.float16)
+    out = None
     for i in range(q_l):
         pos = tokens - q_l + i
-        b = (slope[:, None] * (t[None, :] - pos)).astype(np.float16)
+        b = to_elem(slope[:, None] * (t[None, :] - pos), elem)
+        if out is None:
+            out = np.empty((batch * n_q_heads, q_l, tokens), dtype=b.dtype)
         out[:, i, :] = np.tile(b, (batch, 1))
     return out
 
@@ -201,26 +223,28 @@ def quant_case(workload="quant_4bit", seed: int = 0, **overrides) -> dict:
     B, nQ, nKV = cfg["batch"], cfg["n_q_heads"], cfg["n_kv_heads"]
     dim, L, cap = cfg["dim"], cfg["kv_seq_len"], cfg["kv_capacity"]
     q_l, bits, G = cfg["q_l"], cfg["bits"], cfg["group_size"]
+    elem = cfg.setdefault("elem", "f16")
     rng = np.random.default_rng(seed)
-    q = rng.standard_normal((B * nQ, q_l, dim), dtype=np.float32).astype(np.float16)
+    q = to_elem(rng.standard_normal((B * nQ, q_l, dim), dtype=np.float32), elem)
     pf = 32 // bits
     out = {}
     for name in ("k", "v"):
         packed = np.empty((B * nKV, cap, dim // pf), dtype=np.uint32)
-        scales = np.empty((B * nKV, cap, dim // G), dtype=np.float16)
-        biases = np.empty((B * nKV, cap, dim // G), dtype=np.float16)
+        edt = to_elem(np.zeros(1), elem).dtype
+        scales = np.empty((B * nKV, cap, dim // G), dtype=edt)
+        biases = np.empty((B * nKV, cap, dim // G), dtype=edt)
         for s in range(B * nKV):
             codes = rng.integers(0, 1 << bits, size=(cap, dim), dtype=np.uint32)
             packed[s] = pack_codes(codes, bits)
-            scales[s] = rng.uniform(0.01, 0.1, size=(cap, dim // G)).astype(np.float16)
-            biases[s] = rng.normal(0.0, 0.5, size=(cap, dim // G)).astype(np.float16)
+            scales[s] = to_elem(rng.uniform(0.01, 0.1, size=(cap, dim // G)), elem)
+            biases[s] = to_elem(rng.normal(0.0, 0.5, size=(cap, dim // G)), elem)
         out[name + "_packed"] = packed
         out[name + "_scales"] = scales
         out[name + "_biases"] = biases
     sinks = rng.standard_normal(nQ).astype(np.float32) if cfg.get("sinks") else None
     mode = cfg.get("mask")
     if mode == "alibi":
-        mask = alibi_bias(nQ, B, L, q_l)
+        mask = alibi_bias(nQ, B, L, q_l, elem)
         if cfg.get("mask_stride") is None:
             cfg["mask_stride"] = L
         cfg["mask_head_stride"] = q_l * cfg["mask_stride"]
