@@ -84,12 +84,14 @@ def quant_alg(c):
         L = min(W, L)   # a sliding window reads only its last W tokens
     packed = 2 * B * nKV * L * dim * bits // 8
     sb = 4 * B * nKV * L * (dim // G) * 2
-    qb = B * nQ * q_l * dim * 2
-    mask = 0 if c["mask"] is None else B * nQ * q_l * L * 2
+    esz = 4 if c.get("elem") == "f32" else 2   # bytes of a Q / scale / bias / out element
+    sb = sb * esz // 2
+    qb = B * nQ * q_l * dim * esz
+    mask = 0 if c["mask"] is None else B * nQ * q_l * L * esz
     if c.get("mask_bool") is not None:
         mask = B * nQ * q_l * L * 4
     sinks = 0 if c["sinks"] is None else nQ * 4
-    out = B * nQ * q_l * dim * 2
+    out = B * nQ * q_l * dim * esz
     flops = 4 * (B * nQ * q_l) * L * dim
     return dict(bytes=packed + sb + qb + mask + sinks + out, kv_bytes=packed + sb,
                 flops=flops)
@@ -204,8 +206,8 @@ def cpu_baseline(name, c, alg, quant):
                                scale=c["scale"], sinks=c["sinks"], mask=mask,
                                mask_bool=mb, mask_head_stride=c["mask_head_stride"],
                                mask_stride=c["mask_stride"],
-                               window_size=c.get("window_size", 0), rows=rows,
-                               nthreads=threads)
+                               window_size=c.get("window_size", 0),
+                               elem=c.get("elem", "f16"), rows=rows, nthreads=threads)
         dt = time.perf_counter() - t
     else:
         H, q_l = c["n_heads"], c["q_l"]
@@ -265,9 +267,18 @@ def main():
     ncopies = max(1, min(64, math.ceil(ROTATE_BYTES / alg["bytes"])))
     if quant:
         names = ("q", "k_packed", "k_scales", "k_biases", "v_packed", "v_scales", "v_biases")
-        base = {n: to_dev(c[n]) for n in names}
+        elem_t = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[
+            c.get("elem", "f16")]
+        q_dtype = {"f16": 1, "bf16": 2, "f32": 0}[c.get("elem", "f16")]
+
+        def to_dev_e(a):   # bf16 arrays hold bit patterns (uint16)
+            t = to_dev(a)
+            return t.view(torch.bfloat16) if c.get("elem") == "bf16" else t
+        base = {n: (to_dev if n == "k_packed" or n == "v_packed" else to_dev_e)(c[n])
+                for n in names}
         base["sinks"] = None if c["sinks"] is None else to_dev(c["sinks"])
-        base["mask"] = None if c["mask"] is None else to_dev(np.ascontiguousarray(c["mask"]).ravel())
+        base["mask"] = (None if c["mask"] is None else
+                        to_dev_e(np.ascontiguousarray(c["mask"]).ravel()))
         mask_kind = 0 if c["mask"] is None else 1
         if c.get("mask_bool") is not None:
             base["mask"] = to_dev(np.ascontiguousarray(c["mask_bool"]).ravel().view(np.int32))
@@ -278,9 +289,9 @@ def main():
         span = min(window, L) if window else L
         nwg = args.nwg or ta.quant_pick_nwg(B, nQ, nKV, dim, span, q_l, bits=c["bits"],
                                             group_size=c["group_size"],
-                                            mask_kind=mask_kind)
+                                            mask_kind=mask_kind, q_dtype=q_dtype)
         nrows, D = B * nQ * q_l, dim
-        out_dtype = torch.float16
+        out_dtype = elem_t
     else:
         base = {"q": to_dev(c["q"]), "k": to_dev(c["k"]), "v": to_dev(c["v"])}
         ws = c.get("window_start")
@@ -310,7 +321,7 @@ def main():
     for cp in copies:
         if quant:
             kvb = (ctypes.c_size_t * 6)(*[nb(cp[n]) for n in names[1:]])
-            head = (vp(cp["q"]), 1, nb(cp["q"]), vp(cp["k_packed"]), vp(cp["k_scales"]),
+            head = (vp(cp["q"]), q_dtype, nb(cp["q"]), vp(cp["k_packed"]), vp(cp["k_scales"]),
                     vp(cp["k_biases"]), vp(cp["v_packed"]), vp(cp["v_scales"]),
                     vp(cp["v_biases"]), kvb, vp(cp["sinks"]), nb(cp["sinks"]),
                     vp(cp["mask"]))
@@ -337,7 +348,8 @@ def main():
                      vp(P), nb(P), vp(O), nb(O), H, Hk, D, L, c["kv_capacity"], q_l,
                      c["mask_stride"], c["scale"], nwg, ctypes.c_void_p(sptr))
             calls.append((lib.tree_attn_forward, fargs))
-    rargs = (vp(part), nb(part), vp(out), 1 if out_dtype == torch.float16 else 0,
+    rargs = (vp(part), nb(part), vp(out),
+             {torch.float16: 1, torch.bfloat16: 2}.get(out_dtype, 0),
              nb(out), nrows, D, nwg, ctypes.c_void_p(sptr))
 
     def step(i, ev=None):
@@ -416,7 +428,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if kind in ("f16", "quant") else "f32",
+        "dtype": (c.get("elem", "f16") if quant else "f16" if kind == "f16" else "f32"),
         "data": "synthetic (seeded normal Q/K/V, random tree)",
         "config": {"workload": args.workload, "nwg": nwg, "input_copies": ncopies,
                    "alg_bytes": alg["bytes"], "alg_flops": alg["flops"],

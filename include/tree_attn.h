@@ -61,6 +61,7 @@ extern "C" {
 /* Element types. */
 #define TA_F32 0
 #define TA_F16 1
+#define TA_BF16 2 /* bfloat16: quantized path element type, merge output */
 
 /* Mask sentinels ([OPS] mask constants).  A mask cell <= TA_MASKED excludes
  * the key; any larger value is ADDED to the scaled logit (0 = attended). */
@@ -69,7 +70,8 @@ extern "C" {
 
 /* Mask kinds of tree_attn_quant_forward_ex. */
 #define TA_MASK_NONE 0 /* no mask buffer: the implicit causal rule */
-#define TA_MASK_F16 1  /* additive fp16 bias ([FQS] float-mask macro) */
+#define TA_MASK_F16 1  /* additive bias in the element type T ([FQS] float-mask
+                          macro); fp16 when T is fp16 */
 #define TA_MASK_BOOL 2 /* u32 visibility words ([FQS] bool-mask macro) */
 
 /*
@@ -117,7 +119,7 @@ TA_API uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
 TA_API uint32_t tree_attn_quant_pick_nwg_ex(uint32_t batch, uint32_t n_q_heads,
                                      uint32_t n_kv_heads, uint32_t dim,
                                      uint32_t kv_seq_len, uint32_t q_l, uint32_t bits,
-                                     uint32_t group_size, int mask_kind,
+                                     uint32_t group_size, int mask_kind, int q_dtype,
                                      uint32_t num_cus);
 
 /*
@@ -199,8 +201,8 @@ TA_API int tree_attn_decode(const float *q, size_t q_bytes, const void *k,
  *
  *   partials  DEVICE f32, layout of tree_attn_partials_bytes, for `nrows`
  *             rows, `head_dim` columns and `nwg` splits.
- *   out       DEVICE out_dtype (TA_F32 or TA_F16) [nrows, head_dim];
- *             fp16 results are rounded to nearest even.
+ *   out       DEVICE out_dtype (TA_F32, TA_F16 or TA_BF16) [nrows, head_dim];
+ *             fp16 and bf16 results are rounded to nearest even.
  * head_dim must be a multiple of 4 in [4, 512]; nwg >= 1.
  */
 TA_API int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
@@ -220,28 +222,35 @@ TA_API int tree_attn_reduce(const float *partials, size_t partials_bytes, void *
  *   out[q_idx, i, :] = softmax over {keys, sink} of the values (sink value 0)
  * The sink, when `sinks` is given, is one virtual key with raw logit
  * sinks[q_idx % n_q_heads] (no scale, no mask) ([FQS] accumulator start).
- * maskv is an additive fp16 bias ([FQS] float-mask macro): cell at element
+ * T, the element type of q, the scales, biases, mask and out ([FQS] kernels
+ * are generic in it), is fp16, bf16 or fp32 (q_dtype).
+ * maskv is an additive bias in T ([FQS] float-mask macro): cell at element
  * offset q_idx*mask_head_stride + i*mask_stride + t; cells <= TA_MASKED
  * exclude the key.  mask_head_stride = q_l*mask_stride gives a per-row
  * mask ([FQS] shape [B*nQ, tokens] when q_l = 1); 0 broadcasts one
  * [q_l, mask_stride] tree mask to every head.  mask == NULL selects the
  * implicit causal rule (every token when q_l = 1).
  *
- *   q          DEVICE f16 [batch*n_q_heads, q_l, dim]                (q_bytes)
+ *   q          DEVICE T   [batch*n_q_heads, q_l, dim]                (q_bytes)
  *   k_packed   DEVICE u32 [batch*n_kv_heads, kv_capacity, dim/pf]    (kv_bytes[0])
- *   k_scales   DEVICE f16 [batch*n_kv_heads, kv_capacity, dim/group] (kv_bytes[1])
- *   k_biases   DEVICE f16 same shape as k_scales                     (kv_bytes[2])
+ *   k_scales   DEVICE T   [batch*n_kv_heads, kv_capacity, dim/group] (kv_bytes[1])
+ *   k_biases   DEVICE T   same shape as k_scales                     (kv_bytes[2])
  *   v_packed, v_scales, v_biases: same shapes                (kv_bytes[3..5])
  *   sinks      DEVICE f32 [n_q_heads] or NULL                        (sinks_bytes)
- *   mask       DEVICE f16 or NULL                                    (mask_bytes)
+ *   mask       DEVICE T or NULL, aligned to sizeof(T)                (mask_bytes)
  *   partials   as tree_attn_forward with n_heads = batch*n_q_heads
- *   out        DEVICE f16 [batch*n_q_heads, q_l, dim], written iff nwg == 1
+ *   out        DEVICE T   [batch*n_q_heads, q_l, dim], written iff nwg == 1
  *
- * q_dtype must be TA_F16 (scales, biases, mask and out share it); bits is
- * 4 or 8; dim is 64, 96, 128, 256 or 512 ([FQS] instantiations); group_size
- * is 32, 64 or 128 and divides dim (so 32 at dim 96); kv_capacity >= kv_seq_len > 0 (and even when group_size ==
- * dim); mask_stride >= kv_seq_len when a mask is given.  With nwg > 1 follow with tree_attn_reduce(out_dtype =
- * TA_F16, nrows = batch*n_q_heads*q_l, head_dim = dim).
+ * q_dtype is TA_F16, TA_BF16 or TA_F32 (T).  Q enters the matrix
+ * instructions as fp16: exactly for fp16, converted for bf16 (exact for
+ * magnitudes in fp16's normal range), as an fp16 hi + lo pair for fp32.
+ * Scales, biases and the mask are used in fp32; out is rounded to nearest
+ * even.  bits is 4 or 8; dim is 64, 96, 128, 256 or 512 ([FQS]
+ * instantiations); group_size is 32, 64 or 128 and divides dim (so 32 at
+ * dim 96); kv_capacity >= kv_seq_len > 0 (and even when group_size == dim
+ * with a 2-byte T); mask_stride >= kv_seq_len when a mask is given.  With
+ * nwg > 1 follow with tree_attn_reduce(out_dtype = q_dtype, nrows =
+ * batch*n_q_heads*q_l, head_dim = dim).
  */
 TA_API int tree_attn_quant_forward(
     const void *q, int q_dtype, size_t q_bytes, const uint32_t *k_packed,

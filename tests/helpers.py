@@ -30,19 +30,29 @@ def max_abs(a, b):
     return float(np.max(np.abs(a - b))) if a.size else 0.0
 
 
-def assert_close(got, ref, tol, what="", f16_out=False):
-    """max |got - ref| <= tol.  With f16_out the result was rounded to fp16 by
-    contract, so each element may also carry that rounding: half an fp16 ulp
-    of the exact value is added to its bound."""
+def bf16_ulp(x):
+    """Spacing of bfloat16 numbers at |x| (7 stored mantissa bits)."""
+    a = np.abs(np.asarray(x, dtype=np.float64)).astype(np.float32)
+    e = ((a.view(np.uint32) >> np.uint32(23)) & np.uint32(0xff)).astype(np.int64)
+    return np.ldexp(1.0, np.maximum(e, 1) - 127 - 7)
+
+
+def assert_close(got, ref, tol, what="", f16_out=False, out_elem=None):
+    """max |got - ref| <= tol.  With f16_out (or out_elem "f16" / "bf16") the
+    result was rounded to that type by contract, so each element may also
+    carry that rounding: half an ulp of the exact value is added to its
+    bound."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), "non-finite output " + what
     diff = np.abs(got - ref)
     bound = np.full(ref.shape, float(tol))
-    if f16_out:
+    if f16_out or out_elem == "f16":
         ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
         bound = bound + 0.5 * ulp
+    elif out_elem == "bf16":
+        bound = bound + 0.5 * bf16_ulp(ref)
     worst = int(np.argmax(diff - bound)) if diff.size else 0
     ok = bool(np.all(diff <= bound))
     assert ok, "%s error %.3e > bound %.3e at flat index %d (max-abs %.3e)" % (

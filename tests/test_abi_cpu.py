@@ -77,15 +77,17 @@ def test_quant_pick_nwg_ex_follows_the_variant_footprint(lib):
     # without a device: two wavefronts per SIMD at dim 128, and the LDS of the
     # variant: 4-bit stages fit eight workgroups a CU, 8-bit ones six
     f = lib.tree_attn_quant_pick_nwg_ex
-    assert f(4, 32, 8, 128, 16384, 1, 4, 64, 1, 0) == 64
-    assert f(4, 32, 8, 128, 16384, 1, 8, 64, 1, 0) == 48
-    assert f(4, 32, 8, 128, 16384, 1, 4, 64, 2, 0) == 64
+    assert f(4, 32, 8, 128, 16384, 1, 4, 64, 1, 1, 0) == 64
+    assert f(4, 32, 8, 128, 16384, 1, 8, 64, 1, 1, 0) == 48
+    assert f(4, 32, 8, 128, 16384, 1, 4, 64, 2, 1, 0) == 64
     # a short sequence caps the splits at two tiles each
-    assert f(4, 32, 8, 128, 4096, 1, 4, 64, 1, 0) == 64
-    assert f(4, 32, 8, 128, 512, 1, 4, 64, 1, 0) == 8
+    assert f(4, 32, 8, 128, 4096, 1, 4, 64, 1, 1, 0) == 64
+    assert f(4, 32, 8, 128, 512, 1, 4, 64, 1, 1, 0) == 8
+    # fp32 elements: wider scale/bias slices, still within the 8-per-CU plan
+    assert f(4, 32, 8, 128, 16384, 1, 4, 64, 1, 0, 0) >= 48
     # degenerate shapes and unsupported variants still give a usable count
-    assert f(0, 32, 8, 128, 16384, 1, 4, 64, 1, 0) == 1
-    assert f(4, 32, 8, 96, 16384, 1, 4, 32, 1, 0) >= 1
+    assert f(0, 32, 8, 128, 16384, 1, 4, 64, 1, 1, 0) == 1
+    assert f(4, 32, 8, 96, 16384, 1, 4, 32, 1, 1, 0) >= 1
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -216,7 +218,10 @@ def qf(lib, **kw):
 
 @no_gpu_only
 @pytest.mark.parametrize("kw,code,word", [
-    (dict(q_dtype=0), L.TA_EUNSUPPORTED, "dtype"),
+    (dict(q_dtype=3), L.TA_EUNSUPPORTED, "dtype"),
+    (dict(q_dtype=0, q_bytes=128 * 128 * 4 - 1), L.TA_ESIZE, "q buffer"),   # fp32 elements
+    (dict(q_dtype=2, kv_bytes=[BIG, 32 * 16384 * 2 * 2 - 1, BIG, BIG, BIG, BIG]),
+     L.TA_ESIZE, "k_scales"),                                          # bf16 elements
     (dict(bits=3), L.TA_EUNSUPPORTED, "bits"),
     (dict(dim=80), L.TA_EUNSUPPORTED, "dim"),
     (dict(dim=96), L.TA_EINVAL, "divisible"),      # dim 96 needs group_size 32

@@ -28,20 +28,36 @@ def ta():
     return ta
 
 
-def qcase(seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, cap=None, window=0):
+def qcase(seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, cap=None, window=0,
+          elem="f16"):
     return inputs.quant_case(dict(batch=B, n_q_heads=nQ, n_kv_heads=nKV, dim=dim,
                                   kv_seq_len=L, kv_capacity=cap or (L + 5 + (L + 5) % 2), q_l=q_l,
                                   bits=bits, group_size=G, sinks=sinks, mask=mask,
-                                  window_size=window),
+                                  window_size=window, elem=elem),
                              seed=seed)
+
+
+def dev_e(a, elem):
+    """A T-typed array on the device (bf16 arrays hold uint16 bit patterns)."""
+    import torch
+    t = dev(a)
+    return t.view(torch.bfloat16) if elem == "bf16" else t
+
+
+def host_f(t):
+    """Device result -> float64 numpy (bf16 widens exactly through fp32)."""
+    import torch
+    return host(t.float() if t.dtype == torch.bfloat16 else t).astype(np.float64)
 
 
 def gpu_run(ta, c, nwg=None):
     import torch
-    t = {k: dev(c[k]) for k in ("q", "k_packed", "k_scales", "k_biases", "v_packed",
-                                "v_scales", "v_biases")}
+    e = c.get("elem", "f16")
+    t = {k: (dev(c[k]) if k.endswith("packed") else dev_e(c[k], e))
+         for k in ("q", "k_packed", "k_scales", "k_biases", "v_packed", "v_scales",
+                   "v_biases")}
     sinks = None if c["sinks"] is None else dev(c["sinks"])
-    mask = None if c["mask"] is None else dev(np.ascontiguousarray(c["mask"]).ravel())
+    mask = None if c["mask"] is None else dev_e(np.ascontiguousarray(c["mask"]).ravel(), e)
     mb = c.get("mask_bool")
     mb = None if mb is None else dev(np.ascontiguousarray(mb).ravel().view(np.int32))
     out = ta.quant_verify(t["q"], t["k_packed"], t["k_scales"], t["k_biases"],
@@ -53,7 +69,7 @@ def gpu_run(ta, c, nwg=None):
                           mask_stride=c["mask_stride"],
                           window_size=c.get("window_size", 0))
     torch.cuda.synchronize()
-    return host(out)
+    return host_f(out)
 
 
 def ref_run(c, rows=None):
@@ -65,7 +81,7 @@ def ref_run(c, rows=None):
         mask=None if c["mask"] is None else np.ascontiguousarray(c["mask"]).ravel(),
         mask_bool=None if c.get("mask_bool") is None else np.ascontiguousarray(c["mask_bool"]).ravel(),
         mask_head_stride=c["mask_head_stride"], mask_stride=c["mask_stride"],
-        window_size=c.get("window_size", 0), rows=rows)
+        window_size=c.get("window_size", 0), elem=c.get("elem", "f16"), rows=rows)
 
 
 SMALL = [
@@ -235,3 +251,40 @@ def test_quant_ex_entry_matches_plain_entry(ta):
                                   window_size=0, **kw)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ---- bf16 and fp32 element types ----
+
+ELEM = [
+    # seed, elem, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, window, nwg
+    (60, "bf16", 1, 4, 1, 128, 100, 1, 4, 64, False, None, 0, 1),       # direct bf16 out
+    (61, "bf16", 2, 8, 2, 128, 333, 1, 4, 64, True, "alibi", 0, 3),
+    (62, "bf16", 1, 4, 4, 64, 257, 2, 8, 32, True, "bool", 0, 2),
+    (63, "bf16", 2, 6, 2, 256, 190, 1, 4, 128, False, "alibi", 0, None),
+    (64, "bf16", 1, 2, 1, 512, 97, 1, 8, 32, True, None, 0, 2),
+    (65, "bf16", 1, 4, 2, 96, 300, 1, 4, 32, True, "alibi", 77, 3),
+    (66, "bf16", 1, 2, 1, 64, 101, 1, 4, 64, True, "alibi", 0, 2),      # one group per token
+    (70, "f32", 1, 4, 1, 128, 100, 1, 4, 64, False, None, 0, 1),        # direct f32 out
+    (71, "f32", 2, 8, 2, 128, 333, 1, 4, 64, True, "alibi", 0, 3),
+    (72, "f32", 1, 4, 4, 64, 257, 2, 8, 32, True, "bool", 0, 2),
+    (73, "f32", 2, 6, 2, 256, 190, 1, 4, 32, False, "alibi", 0, None),  # 4-byte mask copies
+    (74, "f32", 1, 2, 1, 512, 97, 1, 8, 32, True, "alibi", 0, 2),       # 16-byte scale copies
+    (75, "f32", 1, 4, 2, 96, 300, 3, 4, 32, True, None, 77, 3),
+    (76, "f32", 1, 2, 1, 64, 101, 1, 4, 64, True, "alibi", 0, 2),
+]
+
+
+@pytest.mark.parametrize("seed,elem,B,nQ,nKV,dim,L,q_l,bits,G,sinks,mask,window,nwg", ELEM)
+def test_quant_element_types(ta, seed, elem, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask,
+                             window, nwg):
+    note("quant %s seed=%d dim=%d L=%d q_l=%d bits=%d G=%d sinks=%s mask=%s W=%d nwg=%s"
+         % (elem, seed, dim, L, q_l, bits, G, sinks, mask, window, nwg))
+    c = qcase(seed, B, nQ, nKV, dim, L, q_l, bits, G, sinks, mask, window=window, elem=elem)
+    assert_close(gpu_run(ta, c, nwg), ref_run(c), TOL, "%s %d" % (elem, seed), out_elem=elem)
+
+
+@pytest.mark.parametrize("name", ["quant_4bit_bf16", "quant_4bit_f32"])
+def test_quant_workload_element_types(ta, name):
+    note("workload %s (full)" % name)
+    c = inputs.quant_case(name)
+    assert_close(gpu_run(ta, c), ref_run(c), TOL, name, out_elem=c["elem"])

@@ -20,6 +20,7 @@ MASKED = -65504.0   # mask cell that excludes a key ("ops/tree_attention.rs")
 ATTENDED = 0.0
 TA_F32 = 0
 TA_F16 = 1
+TA_BF16 = 2
 TA_MASK_NONE = 0
 TA_MASK_F16 = 1
 TA_MASK_BOOL = 2
@@ -80,6 +81,15 @@ def _kv_dtype(t):
     raise TreeAttnError(-4, "k/v dtype must be float32 or float16, got %s" % t.dtype)
 
 
+def _elem_dtype(t):
+    """TA_* code of a quantized-path element tensor (queries, scales, biases,
+    float mask, output): float16, bfloat16 or float32; -1 otherwise (the
+    library then rejects the call)."""
+    import torch
+    return {torch.float16: TA_F16, torch.bfloat16: TA_BF16,
+            torch.float32: TA_F32}.get(t.dtype, -1)
+
+
 def partials_bytes(n_heads, head_dim, q_l, nwg) -> int:
     return int(_api().tree_attn_partials_bytes(n_heads, head_dim, q_l, nwg))
 
@@ -91,7 +101,8 @@ def pick_nwg(n_heads, n_kv_heads, head_dim, kv_seq_len, q_l, kv_dtype,
 
 
 def quant_pick_nwg(batch, n_q_heads, n_kv_heads, dim, kv_seq_len, q_l,
-                   num_cus=0, bits=None, group_size=None, mask_kind=None) -> int:
+                   num_cus=0, bits=None, group_size=None, mask_kind=None,
+                   q_dtype=TA_F16) -> int:
     """Split count for the quantized forward; with bits, group_size and
     mask_kind it accounts for how many workgroups of that variant fit a CU
     (tree_attn_quant_pick_nwg_ex)."""
@@ -100,7 +111,7 @@ def quant_pick_nwg(batch, n_q_heads, n_kv_heads, dim, kv_seq_len, q_l,
                                                    dim, kv_seq_len, q_l, num_cus))
     return int(_api().tree_attn_quant_pick_nwg_ex(
         batch, n_q_heads, n_kv_heads, dim, kv_seq_len, q_l, bits, group_size,
-        TA_MASK_F16 if mask_kind is None else mask_kind, num_cus))
+        TA_MASK_F16 if mask_kind is None else mask_kind, q_dtype, num_cus))
 
 
 def tree_attn_forward(q, k, v, mask, *, kv_seq_len, scale, nwg, out=None,
@@ -130,7 +141,7 @@ def tree_attn_reduce(partials, out, *, nrows, head_dim, nwg, stream=None):
     import torch
     _dense(partials, "partials")
     _dense(out, "out")
-    out_dtype = TA_F16 if out.dtype == torch.float16 else TA_F32
+    out_dtype = _elem_dtype(out)
     rc = _api().tree_attn_reduce(_ptr(partials), _nbytes(partials), _ptr(out),
                                  out_dtype, _nbytes(out), nrows, head_dim, nwg,
                                  _stream(stream))
@@ -239,7 +250,7 @@ def tree_attn_quant_forward(q, k_packed, k_scales, k_biases, v_packed,
     kvb = (ctypes.c_size_t * 6)(*[_nbytes(t) for t in (
         k_packed, k_scales, k_biases, v_packed, v_scales, v_biases)])
     rc = _api().tree_attn_quant_forward(
-        _ptr(q), TA_F16 if q.element_size() == 2 and q.is_floating_point() else -1,
+        _ptr(q), _elem_dtype(q),
         _nbytes(q), _ptr(k_packed), _ptr(k_scales), _ptr(k_biases),
         _ptr(v_packed), _ptr(v_scales), _ptr(v_biases), kvb, _ptr(sinks),
         _nbytes(sinks), _ptr(mask), _nbytes(mask), int(mask_head_stride),
@@ -272,7 +283,7 @@ def tree_attn_quant_forward_ex(q, k_packed, k_scales, k_biases, v_packed,
     kvb = (ctypes.c_size_t * 6)(*[_nbytes(t) for t in (
         k_packed, k_scales, k_biases, v_packed, v_scales, v_biases)])
     rc = _api().tree_attn_quant_forward_ex(
-        _ptr(q), TA_F16 if q.element_size() == 2 and q.is_floating_point() else -1,
+        _ptr(q), _elem_dtype(q),
         _nbytes(q), _ptr(k_packed), _ptr(k_scales), _ptr(k_biases),
         _ptr(v_packed), _ptr(v_scales), _ptr(v_biases), kvb, _ptr(sinks),
         _nbytes(sinks), _ptr(mask), int(mask_kind), _nbytes(mask),
@@ -302,9 +313,10 @@ def quant_verify(q, k_packed, k_scales, k_biases, v_packed, v_scales,
         kind = (TA_MASK_BOOL if mask_bool is not None else
                 TA_MASK_F16 if mask is not None else TA_MASK_NONE)
         nwg = quant_pick_nwg(batch, BnQ // batch, n_kv_heads, dim, span, q_l,
-                             bits=bits, group_size=group_size, mask_kind=kind)
+                             bits=bits, group_size=group_size, mask_kind=kind,
+                             q_dtype=_elem_dtype(q))
     if out is None:
-        out = torch.empty((BnQ, q_l, dim), dtype=torch.float16, device=q.device)
+        out = torch.empty((BnQ, q_l, dim), dtype=q.dtype, device=q.device)
     if nwg > 1 and partials is None:
         partials = torch.empty(partials_bytes(BnQ, dim, q_l, nwg) // 4,
                                dtype=torch.float32, device=q.device)

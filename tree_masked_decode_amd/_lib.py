@@ -26,6 +26,7 @@ TA_EUNSUPPORTED = -4
 TA_EHIP = -5
 TA_F32 = 0
 TA_F16 = 1
+TA_BF16 = 2
 TA_MASK_NONE = 0
 TA_MASK_F16 = 1
 TA_MASK_BOOL = 2
@@ -74,7 +75,7 @@ def load():
         lib.tree_attn_pick_nwg.restype = U
         lib.tree_attn_quant_pick_nwg.argtypes = [U, U, U, U, U, U, U]
         lib.tree_attn_quant_pick_nwg.restype = U
-        lib.tree_attn_quant_pick_nwg_ex.argtypes = [U, U, U, U, U, U, U, U, I, U]
+        lib.tree_attn_quant_pick_nwg_ex.argtypes = [U, U, U, U, U, U, U, U, I, I, U]
         lib.tree_attn_quant_pick_nwg_ex.restype = U
         lib.tree_attn_forward.argtypes = [P, Z, P, P, I, Z, P, Z, P, Z, P, Z,
                                           U, U, U, U, U, U, U, F, U, P]

@@ -270,12 +270,13 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
 uint32_t tree_attn_quant_pick_nwg_ex(uint32_t batch, uint32_t n_q_heads,
                                      uint32_t n_kv_heads, uint32_t dim,
                                      uint32_t kv_seq_len, uint32_t q_l, uint32_t bits,
-                                     uint32_t group_size, int mask_kind,
+                                     uint32_t group_size, int mask_kind, int q_dtype,
                                      uint32_t num_cus) {
   if (batch == 0 || n_q_heads == 0 || n_kv_heads == 0 || kv_seq_len == 0 ||
       q_l == 0 || n_q_heads % n_kv_heads != 0)
     return 1;
-  uint32_t per_cu = ta::quant_wgs_per_cu(dim, bits, group_size, mask_kind);
+  const int elem = q_dtype == TA_BF16 ? 1 : q_dtype == TA_F32 ? 2 : 0;
+  uint32_t per_cu = ta::quant_wgs_per_cu(dim, bits, group_size, mask_kind, elem);
   if (per_cu == 0) per_cu = 8u;   // not a supported variant: the plain estimate
   uint32_t rows = q_l * (n_q_heads / n_kv_heads);
   const uint64_t kv = 2ull * batch * n_kv_heads * kv_seq_len * dim * (bits ? bits : 4) / 8;
@@ -321,15 +322,15 @@ int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
                 fn, head_dim);
   if (nwg == 0 || nwg > kMaxNwg)
     return fail(TA_EINVAL, "%s: nwg must be in [1, %u], got %u", fn, kMaxNwg, nwg);
-  if (out_dtype != TA_F32 && out_dtype != TA_F16)
-    return fail(TA_EUNSUPPORTED, "%s: out dtype must be TA_F32 or TA_F16", fn);
+  if (out_dtype != TA_F32 && out_dtype != TA_F16 && out_dtype != TA_BF16)
+    return fail(TA_EUNSUPPORTED, "%s: out dtype must be TA_F32, TA_F16 or TA_BF16", fn);
   if (!partials || !out) return fail(TA_EINVAL, "%s: partials and out must not be NULL", fn);
   if (!aligned16(partials) || ((uintptr_t)out & 7u))
     return fail(TA_EINVAL, "%s: partials must be 16-byte and out 8-byte aligned", fn);
   bool of;
   uint64_t req_part = partials_bytes_u64(nrows, head_dim, nwg, of);
   uint64_t req_out;
-  if (of || !mul3(nrows, head_dim, out_dtype == TA_F16 ? 2 : 4, req_out))
+  if (of || !mul3(nrows, head_dim, out_dtype == TA_F32 ? 4 : 2, req_out))
     return fail(TA_EOVERFLOW, "%s: size computation overflows", fn);
   if (partials_bytes < req_part)
     return fail(TA_ESIZE, "%s: partials buffer too small: have %zu bytes, need >= %llu",
@@ -345,7 +346,7 @@ int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
   a.nrows = nrows;
   a.dim = head_dim;
   a.nwg = nwg;
-  a.out_f16 = out_dtype == TA_F16;
+  a.out_type = out_dtype == TA_F16 ? 1 : out_dtype == TA_BF16 ? 2 : 0;
   return hip_status(ta::launch_reduce(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -364,9 +365,11 @@ static int quant_forward(
                 fn);
   if ((mask_kind == TA_MASK_NONE) != (mask == nullptr))
     return fail(TA_EINVAL, "%s: mask must be NULL exactly when mask_kind is TA_MASK_NONE", fn);
-  const uint64_t cell_bytes = mask_kind == TA_MASK_BOOL ? 4 : 2;
-  if (q_dtype != TA_F16)
-    return fail(TA_EUNSUPPORTED, "%s: queries/scales/biases/out dtype must be TA_F16", fn);
+  if (q_dtype != TA_F16 && q_dtype != TA_BF16 && q_dtype != TA_F32)
+    return fail(TA_EUNSUPPORTED,
+                "%s: queries/scales/biases/mask/out dtype must be TA_F16, TA_BF16 or TA_F32", fn);
+  const uint64_t esz = q_dtype == TA_F32 ? 4 : 2;   // bytes of a T element
+  const uint64_t cell_bytes = mask_kind == TA_MASK_BOOL ? 4 : esz;
   if (bits != 4 && bits != 8)
     return fail(TA_EUNSUPPORTED, "%s: bits must be 4 or 8, got %u", fn, bits);
   if (dim != 64 && dim != 96 && dim != 128 && dim != 256 && dim != 512)
@@ -395,8 +398,9 @@ static int quant_forward(
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(TA_EINVAL, "%s: scale must be finite", fn);
   // Scales/biases are read four tokens at a time as 32-bit words.
-  if (group_size == dim && (kv_capacity & 1u))
-    return fail(TA_EUNSUPPORTED, "%s: kv_capacity must be even when group_size == dim", fn);
+  if (esz == 2 && group_size == dim && (kv_capacity & 1u))
+    return fail(TA_EUNSUPPORTED,
+                "%s: kv_capacity must be even when group_size == dim (2-byte scales)", fn);
   if (!kv_bytes) return fail(TA_EINVAL, "%s: kv_bytes must not be NULL", fn);
   if (!q || !k_packed || !k_scales || !k_biases || !v_packed || !v_scales || !v_biases)
     return fail(TA_EINVAL, "%s: q and the six K/V buffers must not be NULL", fn);
@@ -413,8 +417,8 @@ static int quant_forward(
   const uint64_t BnQ = (uint64_t)batch * n_q_heads, BnKV = (uint64_t)batch * n_kv_heads;
   const uint64_t pf = 32 / bits;
   uint64_t req_q, req_packed, req_sb, req_out, req_sinks = 0, req_mask = 0, req_part = 0;
-  if (!mul4(BnQ, q_l, dim, 2, req_q) || !mul4(BnKV, kv_capacity, dim / pf, 4, req_packed) ||
-      !mul4(BnKV, kv_capacity, dim / group_size, 2, req_sb))
+  if (!mul4(BnQ, q_l, dim, esz, req_q) || !mul4(BnKV, kv_capacity, dim / pf, 4, req_packed) ||
+      !mul4(BnKV, kv_capacity, dim / group_size, esz, req_sb))
     return fail(TA_EOVERFLOW, "%s: size computation overflows", fn);
   req_out = req_q;
   if (sinks) req_sinks = (uint64_t)n_q_heads * 4;
@@ -455,17 +459,18 @@ static int quant_forward(
     return fail(TA_EUNSUPPORTED, "%s: batch*n_q_heads*q_l too large", fn);
 
   ta::QuantArgs a;
-  a.q = static_cast<const ta::half_t *>(q);
+  a.q = q;
+  a.elem = q_dtype == TA_BF16 ? 1 : q_dtype == TA_F32 ? 2 : 0;
   a.kp = k_packed;
   a.vp = v_packed;
-  a.ks = static_cast<const ta::half_t *>(k_scales);
-  a.kb = static_cast<const ta::half_t *>(k_biases);
-  a.vs = static_cast<const ta::half_t *>(v_scales);
-  a.vb = static_cast<const ta::half_t *>(v_biases);
+  a.ks = k_scales;
+  a.kb = k_biases;
+  a.vs = v_scales;
+  a.vb = v_biases;
   a.sinks = sinks;
-  a.mask = mask_kind == TA_MASK_F16 ? static_cast<const ta::half_t *>(mask) : nullptr;
+  a.mask = mask_kind == TA_MASK_F16 ? mask : nullptr;
   a.mbool = mask_kind == TA_MASK_BOOL ? static_cast<const uint32_t *>(mask) : nullptr;
-  a.out = static_cast<ta::half_t *>(out);
+  a.out = out;
   a.mask_head_stride = mask ? mask_head_stride : 0;
   a.mask_stride = mask ? mask_stride : kv_seq_len;
   a.batch = batch;

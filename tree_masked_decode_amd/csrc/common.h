@@ -49,19 +49,20 @@ struct FwdArgs {
 // Quantized forward.
 // ---------------------------------------------------------------------------
 struct QuantArgs {
-  const half_t *q;            // [BnQ, q_l, dim]
+  const void *q;              // [BnQ, q_l, dim] T
   const uint32_t *kp, *vp;    // [BnKV, cap, dim/pf]
-  const half_t *ks, *kb, *vs, *vb;  // [BnKV, cap, dim/G]
+  const void *ks, *kb, *vs, *vb;  // [BnKV, cap, dim/G] T
   const float *sinks;         // [nQ] or nullptr
-  const half_t *mask;         // f16 additive or nullptr
+  const void *mask;           // T additive or nullptr
   const uint32_t *mbool;      // u32 visibility words or nullptr (never both)
   float *part_o, *part_sm;
-  half_t *out;                // [BnQ, q_l, dim]
+  void *out;                  // [BnQ, q_l, dim] T
   uint64_t mask_head_stride;
   uint32_t mask_stride;
   uint32_t batch, nq, nkv, repeat, kv_seq_len, kv_capacity, q_l;
   uint32_t nwg, rows, row_tiles, n_tiles, units;
   uint32_t key_lo;            // first token the sliding window keeps (0: all)
+  int elem;                   // T: 0 fp16, 1 bf16, 2 fp32
   float qscale;               // scale * log2(e)
 };
 
@@ -72,8 +73,16 @@ struct ReduceArgs {
   const float *part_o, *part_sm;
   void *out;
   uint32_t nrows, dim, nwg;
-  int out_f16;
+  int out_type;   // 0 fp32, 1 fp16, 2 bf16
 };
+
+// fp32 -> bfloat16, round to nearest even (a NaN stays a quiet NaN).
+__device__ inline uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
 
 constexpr int kMaxTreeNodes = 1024;
 struct MaskArgs {
@@ -102,8 +111,9 @@ uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows);
 uint32_t f32_tile_keys(uint32_t head_dim);
 uint32_t quant_tile_keys(uint32_t dim);
 // Resident workgroups per CU of the quantized kernel variant (0: no such
-// variant); mask_kind 0 none, 1 fp16, 2 u32.
-uint32_t quant_wgs_per_cu(uint32_t dim, uint32_t bits, uint32_t group, int mask_kind);
+// variant); mask_kind 0 none, 1 additive T, 2 u32; elem 0 fp16, 1 bf16, 2 fp32.
+uint32_t quant_wgs_per_cu(uint32_t dim, uint32_t bits, uint32_t group, int mask_kind,
+                          int elem);
 
 // Asynchronous global -> LDS copies: every lane moves 16 (or 4) bytes from its
 // own global address to lds + 16 * lane (4 * lane), `lds` being the

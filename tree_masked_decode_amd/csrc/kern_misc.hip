@@ -76,7 +76,7 @@ __device__ inline float wave_sum(float x) {
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-template <bool OUT_F16, uint32_t T, uint32_t C>
+template <int OUT, uint32_t T, uint32_t C>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   // T threads per column set, C float4 columns per thread (dim = 4 T C at
   // most), G split groups
@@ -162,9 +162,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
 #pragma unroll
     for (uint32_t gg = 1; gg < G; ++gg) sum += s_part[gg][d4];
     sum *= inv;
-    if (OUT_F16) {
+    if (OUT == 1) {
       half4_t h = {(half_t)sum[0], (half_t)sum[1], (half_t)sum[2], (half_t)sum[3]};
       reinterpret_cast<half4_t *>(a.out)[r * d4n + d4] = h;
+    } else if (OUT == 2) {
+      const uint32_t lo = f32_to_bf16(sum[0]) | ((uint32_t)f32_to_bf16(sum[1]) << 16);
+      const uint32_t hi = f32_to_bf16(sum[2]) | ((uint32_t)f32_to_bf16(sum[3]) << 16);
+      reinterpret_cast<u32x2 *>(a.out)[r * d4n + d4] = u32x2{lo, hi};
     } else {
       reinterpret_cast<floatx4 *>(a.out)[r * d4n + d4] = sum;
     }
@@ -174,10 +178,12 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
 template <uint32_t T, uint32_t C>
 hipError_t launch_reduce_t(const ReduceArgs &a, hipStream_t s) {
   dim3 grid(a.nrows);
-  if (a.out_f16)
-    hipLaunchKernelGGL((reduce_kernel<true, T, C>), grid, dim3(256), 0, s, a);
+  if (a.out_type == 1)
+    hipLaunchKernelGGL((reduce_kernel<1, T, C>), grid, dim3(256), 0, s, a);
+  else if (a.out_type == 2)
+    hipLaunchKernelGGL((reduce_kernel<2, T, C>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((reduce_kernel<false, T, C>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((reduce_kernel<0, T, C>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

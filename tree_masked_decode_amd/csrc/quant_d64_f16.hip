@@ -1,0 +1,18 @@
+// quant_d64_f16.hip -- the head-dim-64 variants of the quantized kernel with
+// fp16 queries, scales, biases, mask and output.
+#include "quant_impl.h"
+
+namespace ta {
+
+static_assert(BN == 32, "quant.hip reports 32-key tiles (quant_tile_keys)");
+
+hipError_t launch_quant_d64_f16(const QuantArgs &a, uint32_t bits, uint32_t group,
+                               hipStream_t s) {
+  return launch_qb<64, 0>(a, bits, group, s);
+}
+
+uint32_t quant_wgs_d64_f16(uint32_t bits, uint32_t group, int mask_kind) {
+  return wgs_per_cu_b<64, 0>(bits, group, mask_kind);
+}
+
+}  // namespace ta

@@ -94,6 +94,28 @@ __device__ inline half8_t word_codes(const uint32_t *w, uint32_t m) {
   return __builtin_bit_cast(half8_t, r);
 }
 
+// Element types of the queries, scales, biases, float mask and output
+// ("ffai/flash_quantized_sdpa.rs" kernels are generic in that type T).
+enum { kF16 = 0, kBF16 = 1, kF32 = 2 };
+template <int ET> struct Elem {
+  static constexpr int SZ = ET == kF32 ? 4 : 2;   // bytes
+};
+// Element i of a T array (global memory, LDS or registers), as fp32.
+template <int ET> __device__ inline float elem_f32(const void *base, size_t i) {
+  if (ET == kF32) return reinterpret_cast<const float *>(base)[i];
+  const uint16_t b = reinterpret_cast<const uint16_t *>(base)[i];
+  if (ET == kBF16) return __uint_as_float((uint32_t)b << 16);
+  return (float)__builtin_bit_cast(half_t, b);
+}
+template <int ET> __device__ inline void store_elem(void *base, size_t i, float x) {
+  if (ET == kF32)
+    reinterpret_cast<float *>(base)[i] = x;
+  else if (ET == kBF16)
+    reinterpret_cast<uint16_t *>(base)[i] = f32_to_bf16(x);
+  else
+    reinterpret_cast<half_t *>(base)[i] = (half_t)x;
+}
+
 // Dim index of slot j of a step whose first word is w0 (see word_codes).
 template <int BITS>
 __device__ inline uint32_t slot_dim(uint32_t w0, int j) {
@@ -105,8 +127,10 @@ __device__ inline uint32_t slot_dim(uint32_t w0, int j) {
   return 4u * (w0 + (uint32_t)(j >> 2)) + pi8[j & 3];
 }
 
-template <int DIM, int BITS, int G>
+template <int DIM, int BITS, int G, int ET = kF16>
 struct QShape {
+  static constexpr int ESZ = Elem<ET>::SZ;     // bytes of a scale / bias
+  static constexpr int EPW = 4 / ESZ;          // of them per 32-bit word
   static constexpr int WPK = DIM * BITS / 32;  // 32-bit words per token row
   static constexpr int NG = DIM / G;           // scale groups per token
   static constexpr int WPS = BITS / 4;         // words per MFMA step per lane
@@ -118,7 +142,7 @@ struct QShape {
   static constexpr int VTOT = BN * WPK / 4;            // V 16-byte chunks of a tile
   static constexpr int VCH = (VTOT + kThreads - 1) / kThreads;  // ... per lane
   static constexpr int RS = BN + 4;            // LDS row stride (words)
-  static constexpr int SBW = 4 * NG / 2;       // u32 words of 4 keys' scales
+  static constexpr int SBW = 4 * NG / EPW;     // u32 words of 4 keys' scales
   static_assert(VCH >= 1, "tile too small");
   static_assert(RUN * 4 == GW, "lane runs must tile a group");
   // LDS stage: K words, V words, K scales, K biases, V scales, V biases, mask
@@ -127,37 +151,56 @@ struct QShape {
   // bytes of the last copy when a tile is not a whole number of copies
   // (dim 96 at 4 bits: 1.5 KB); its lanes past that leave it alone
   static constexpr int KT_TAIL = KT % 1024;
-  static constexpr int SBB = BN * NG * 2;              // bytes of one scale/bias slice
-  // the four slices back to back (4 SBB = 256 NG bytes) move in SB_I
-  // 4-byte-per-lane copies; lane l of copy i takes byte 256 i + 4 l of that
-  // region, i.e. slice (256 i + 4 l) / SBB
-  static constexpr int SB_I = 4 * SBB / 256;
+  static constexpr int SBB = BN * NG * ESZ;            // bytes of one scale/bias slice
+  // the four slices back to back (4 SBB = 128 NG ESZ bytes) move in SB_I
+  // copies of SB_W bytes per lane; lane l of copy i takes byte SB_W (64 i +
+  // l) of that region, i.e. slice SB_W (64 i + l) / SBB.  16-byte copies when
+  // a token's values fill whole 16-byte chunks (so that a chunk never
+  // straddles two tokens) and the region is whole copies, else 4-byte ones.
+  static constexpr bool SB_WIDE = (NG * ESZ) % 16 == 0 && (4 * SBB) % 1024 == 0;
+  static constexpr int SB_W = SB_WIDE ? 16 : 4;
+  static constexpr int SB_I = 4 * SBB / (64 * SB_W);
   static constexpr int SBP = SBB;
-  static constexpr int MB = 16 * BN * 2;               // mask cells of 16 rows
   static constexpr int VL = WPK * RS * 4;              // V transpose area
   static_assert(WPK % 4 == 0, "token rows of whole 16-byte chunks");
 };
 
-// Mask modes: none (implicit causal); an fp16 additive mask in 16-byte
-// copies (row starts and kv_seq_len multiples of 8 cells), 4-byte copies
-// (multiples of 2) or per-lane register loads (any alignment); or a u32
-// visibility mask ("ffai/flash_quantized_sdpa.rs", bool-mask macro) in
-// 16-byte copies of eight rows (row starts and kv_seq_len multiples of 4
-// cells) or 4-byte copies of two rows (any layout).
+// Mask modes: none (implicit causal); an additive mask of T cells in
+// 16-byte copies (row starts and kv_seq_len multiples of 16 / sizeof(T)
+// cells), 4-byte copies (multiples of 4 / sizeof(T)) or per-lane register
+// loads (any alignment); or a u32 visibility mask
+// ("ffai/flash_quantized_sdpa.rs", bool-mask macro) in 16-byte or 4-byte
+// copies.  A copy mode moves the 16 rows x 32 cells of a tile, row r at byte
+// 32 r CB (CB = cell bytes), lane l of copy i taking row RPC i + l / LPR and
+// cells CPL (l % LPR) .. (CPL cells per lane, LPR lanes per row, RPC rows
+// per copy).
 enum { kMaskNone = 0, kMaskB128 = 1, kMaskB32 = 2, kMaskReg = 3, kMaskBool = 4,
        kMaskBoolB128 = 5 };
-template <int DIM, int BITS, int G, int MM> struct QStage {
-  using S = QShape<DIM, BITS, G>;
-  static constexpr int MASK_I = MM == kMaskB128 ? 1 : MM == kMaskB32 ? 4
-                               : MM == kMaskBool ? 8 : MM == kMaskBoolB128 ? 2 : 0;
-  static constexpr int M_BYTES = (MM == kMaskBool || MM == kMaskBoolB128) ? 2 * S::MB
-                                 : (MM == kMaskB128 || MM == kMaskB32) ? S::MB : 0;
+template <int MM, int ET> struct MaskGeom {
+  static constexpr bool BOOL = MM == kMaskBool || MM == kMaskBoolB128;
+  static constexpr bool DMA = BOOL || MM == kMaskB128 || MM == kMaskB32;
+  static constexpr bool WIDE = MM == kMaskB128 || MM == kMaskBoolB128;  // 16-byte copies
+  static constexpr int CB = BOOL ? 4 : Elem<ET>::SZ;       // cell bytes
+  static constexpr int CPL = (WIDE ? 16 : 4) / CB;         // cells per lane
+  static constexpr int LPR = BN / CPL;                     // lanes per row
+  static constexpr int RPC = kThreads / LPR;               // rows per copy
+  static constexpr int NC = DMA ? 16 / RPC : 0;            // copies per tile
+  static constexpr int BYTES = DMA ? 16 * BN * CB : 0;     // per stage
+  static constexpr int STEP = WIDE ? 1024 : 256;           // LDS bytes per copy
+  static_assert(!DMA || (RPC * LPR == kThreads && NC * RPC == 16), "mask copy geometry");
+};
+template <int DIM, int BITS, int G, int MM, int ET> struct QStage {
+  using S = QShape<DIM, BITS, G, ET>;
+  using MG = MaskGeom<MM, ET>;
+  static constexpr int MASK_I = MG::NC;
+  static constexpr int M_BYTES = MG::BYTES;
   static constexpr int BYTES = 2 * S::KT + 4 * S::SBP + M_BYTES;
   static constexpr int PER_TILE = 2 * S::KT_I + S::SB_I + MASK_I;
   // Eight one-wavefront workgroups share a CU at dim <= 128 (two per SIMD),
   // so a workgroup keeps within 20 KB of LDS there; wider heads run fewer.
   static constexpr int BUDGET = DIM <= 128 ? 20 * 1024 : 48 * 1024;
-  static constexpr int NS = (3 * BYTES + S::VL <= BUDGET) ? 3 : 2;
+  // (and a wavefront's copy counter tracks at most 63 copies in flight)
+  static constexpr int NS = (3 * BYTES + S::VL <= BUDGET && 2 * PER_TILE <= 63) ? 3 : 2;
   static constexpr int LDS = NS * BYTES + S::VL;
   static_assert(PER_TILE * (NS - 1) <= 63, "vmcnt range");
 };
@@ -169,10 +212,11 @@ __device__ inline uint32_t step_word(int g, int sub, uint32_t gp) {
   return (uint32_t)(g * S::GW) + gp * S::RUN + (uint32_t)(sub * S::WPS);
 }
 
-template <int DIM, int BITS, int G, int MM>
+template <int DIM, int BITS, int G, int MM, int ET>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
-  using S = QShape<DIM, BITS, G>;
-  using ST = QStage<DIM, BITS, G, MM>;
+  using S = QShape<DIM, BITS, G, ET>;
+  using ST = QStage<DIM, BITS, G, MM, ET>;
+  using MG = MaskGeom<MM, ET>;
   constexpr bool IMPLICIT = MM == kMaskNone;
   constexpr int NG = S::NG, STEPS = S::STEPS, DB = S::DB, NS = ST::NS;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -192,26 +236,32 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   const uint32_t node = valid ? gr / a.repeat : 0u;
   const uint32_t qidx = kv * a.repeat + (valid ? gr % a.repeat : 0u);
 
-  // ---- Q as given (fp16, exact), in the K operand's slot order; the
-  // attention scale is applied to the fp32 dot products afterwards ----
-  half8_t qf[STEPS];
+  // ---- Q in the K operand's slot order; the attention scale is applied
+  // to the fp32 dot products afterwards.  fp16 Q is used exactly; bf16 Q
+  // becomes fp16 (exact for magnitudes in fp16's normal range); fp32 Q is an
+  // fp16 hi + lo pair (two matrix instructions per step). ----
+  constexpr bool QLO = ET == kF32;
+  half8_t qf[STEPS], qfl[QLO ? STEPS : 1];
   float qsum[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) qsum[g] = 0.0f;
   {
-    const half_t *qrow = a.q + ((size_t)qidx * a.q_l + node) * DIM;
+    const size_t qrow = ((size_t)qidx * a.q_l + node) * DIM;
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int sub = 0; sub < S::SPG; ++sub) {
         const uint32_t w0 = step_word<DIM, BITS, G>(g, sub, gp);
-        half8_t f;
+        half8_t f, fl;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          f[j] = valid ? qrow[slot_dim<BITS>(w0, j)] : (half_t)0.0f;
-          qsum[g] += (float)f[j];
+          const float x = valid ? elem_f32<ET>(a.q, qrow + slot_dim<BITS>(w0, j)) : 0.0f;
+          f[j] = (half_t)x;
+          if (QLO) fl[j] = (half_t)(x - (float)f[j]);
+          qsum[g] += ET == kF16 ? (float)f[j] : x;
         }
         qf[g * S::SPG + sub] = f;
+        if (QLO) qfl[(g * S::SPG + sub) % (QLO ? STEPS : 1)] = fl;
       }
   }
 #pragma unroll
@@ -223,11 +273,12 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   const size_t kvrow0 = (size_t)kv * a.kv_capacity;
   const uint32_t *KP = a.kp + kvrow0 * S::WPK;
   const uint32_t *VP = a.vp + kvrow0 * S::WPK;
-  const half_t *KS = a.ks + kvrow0 * NG, *KB = a.kb + kvrow0 * NG;
-  const half_t *VS = a.vs + kvrow0 * NG, *VB = a.vb + kvrow0 * NG;
-  const half_t *mrow = (MM == kMaskReg) ? a.mask + (size_t)qidx * a.mask_head_stride +
-                                                (size_t)node * a.mask_stride
-                                          : nullptr;
+  constexpr int ESZ = S::ESZ;
+  const char *KS = reinterpret_cast<const char *>(a.ks) + kvrow0 * NG * ESZ;
+  const char *KB = reinterpret_cast<const char *>(a.kb) + kvrow0 * NG * ESZ;
+  const char *VS = reinterpret_cast<const char *>(a.vs) + kvrow0 * NG * ESZ;
+  const char *VB = reinterpret_cast<const char *>(a.vb) + kvrow0 * NG * ESZ;
+  const size_t mrow = (size_t)qidx * a.mask_head_stride + (size_t)node * a.mask_stride;
   const int64_t causal_last = (int64_t)a.kv_seq_len - (int64_t)a.q_l + (int64_t)node;
   const uint32_t L = a.kv_seq_len;
   // sliding window ("ffai/flash_quantized_sdpa.rs" causal / sliding-window
@@ -253,40 +304,32 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   t1 += tile_lo;
   const uint32_t t_first = t0;
   auto stage_off = [&](uint32_t t) -> uint32_t { return ((t - t_first) % NS) * ST::BYTES; };
-  // mask row of the workgroup's row r (rows past the end reuse row 0)
-  auto mask_row = [&](uint32_t r) -> const half_t * {
-    uint32_t g2 = rt * 16u + r;
-    if (g2 >= a.rows) g2 = rt * 16u;
-    const uint32_t q2 = kv * a.repeat + g2 % a.repeat;
-    return a.mask + (size_t)q2 * a.mask_head_stride + (size_t)(g2 / a.repeat) * a.mask_stride;
-  };
   // Per-lane source pointers of the copies: a tile's K words, V words and
   // each scale/bias slice are contiguous in memory, so every copy of a full
   // tile is the lane's pointer plus a wave-uniform tile offset.  A tile that
   // reaches past kv_seq_len takes the clamped path instead.
   const char *kp_l = reinterpret_cast<const char *>(KP) + 16u * lane;
   const char *vp_l = reinterpret_cast<const char *>(VP) + 16u * lane;
-  const half_t *sarr[4] = {KS, KB, VS, VB};
+  const char *sarr[4] = {KS, KB, VS, VB};
   const char *sb_l[S::SB_I];
 #pragma unroll
   for (int i = 0; i < S::SB_I; ++i) {
-    const uint32_t o = 256u * i + 4u * lane;
-    sb_l[i] = reinterpret_cast<const char *>(sarr[o / S::SBB]) + o % S::SBB;
+    const uint32_t o = S::SB_W * (64u * i + lane);
+    sb_l[i] = sarr[o / S::SBB] + o % S::SBB;
   }
-  const half_t *mrow_l = nullptr;
-  if (MM == kMaskB128) mrow_l = mask_row(lane / 4u) + 8u * (lane % 4u);
-  // bool mask: copy i moves rows 2i, 2i + 1 (lane / 32), cell lane % 32
-  // (4-byte copies) or rows 8i .. 8i + 7 (lane / 8), cells 4 (lane % 8) ..
-  // + 3 (16-byte copies)
-  constexpr int MB_N = MM == kMaskBool ? 8 : MM == kMaskBoolB128 ? 2 : 1;
-  const uint32_t *mb_l[MB_N];
-  if (MM == kMaskBool || MM == kMaskBoolB128) {
+  // mask copies: the row each copy gives this lane, as a byte pointer to its
+  // first cell (rows past the end reuse the workgroup's row 0)
+  const char *mbase = MG::BOOL ? reinterpret_cast<const char *>(a.mbool)
+                               : reinterpret_cast<const char *>(a.mask);
+  const char *m_l[MG::NC > 0 ? MG::NC : 1];
+  if (MG::DMA) {
 #pragma unroll
-    for (int i = 0; i < MB_N; ++i) {
-      uint32_t g2 = rt * 16u + (MM == kMaskBool ? 2u * i + lane / 32u : 8u * i + lane / 8u);
-      if (g2 >= a.rows) g2 = rt * 16u;   // rows past the end reuse row 0
+    for (int i = 0; i < MG::NC; ++i) {
+      uint32_t g2 = rt * 16u + MG::RPC * i + lane / MG::LPR;
+      if (g2 >= a.rows) g2 = rt * 16u;
       const uint32_t q2 = kv * a.repeat + g2 % a.repeat;
-      mb_l[i] = a.mbool + (size_t)q2 * a.mask_head_stride + (size_t)(g2 / a.repeat) * a.mask_stride;
+      m_l[i] = mbase + ((size_t)q2 * a.mask_head_stride +
+                        (size_t)(g2 / a.repeat) * a.mask_stride) * MG::CB;
     }
   }
   auto issue = [&](uint32_t t) {
@@ -301,9 +344,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
           dma_b128(vp_l + kvo + 1024u * i, sb + S::KT + 1024u * i);
         }
       }
-      const size_t so = (size_t)key0 * (2u * NG);
+      const size_t so = (size_t)key0 * NG * ESZ;
 #pragma unroll
-      for (int i = 0; i < S::SB_I; ++i) dma_b32(sb_l[i] + so, sb + 2u * S::KT + 256u * i);
+      for (int i = 0; i < S::SB_I; ++i) {
+        if (S::SB_WIDE)
+          dma_b128(sb_l[i] + so, sb + 2u * S::KT + 1024u * i);
+        else
+          dma_b32(sb_l[i] + so, sb + 2u * S::KT + 256u * i);
+      }
     } else {
       // keys past kv_seq_len re-read row L - 1 (or the word that holds it)
 #pragma unroll
@@ -319,43 +367,32 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < S::SB_I; ++i) {
-        const uint32_t o = 256u * i + 4u * lane;
-        const uint32_t h = (o % S::SBB) / 2u;               // first half of the word
-        uint32_t key = key0 + h / NG;
-        if (key >= L) key = NG == 1 ? ((L - 1u) & ~1u) : L - 1u;
-        dma_b32(sarr[o / S::SBB] + (size_t)key * NG + h % NG, sb + 2u * S::KT + 256u * i);
+        const uint32_t o = S::SB_W * (64u * i + lane);
+        const uint32_t e = (o % S::SBB) / ESZ;              // first element of the copy
+        uint32_t key = key0 + e / NG;
+        // a word holds two tokens' values when NG == 1 at two bytes each
+        if (key >= L) key = (ESZ == 2 && NG == 1) ? ((L - 1u) & ~1u) : L - 1u;
+        const char *g = sarr[o / S::SBB] + ((size_t)key * NG + e % NG) * ESZ;
+        if (S::SB_WIDE)
+          dma_b128(g, sb + 2u * S::KT + 1024u * i);
+        else
+          dma_b32(g, sb + 2u * S::KT + 256u * i);
       }
     }
-    if (MM == kMaskB128) {
-      // lane: row lane / 4, cells 8 (lane % 4) .. + 7
-      if (key0 + BN <= L) {
-        dma_b128(mrow_l + key0, sb + 2u * S::KT + 4u * S::SBP);
-      } else {
-        uint32_t key = key0 + 8u * (lane % 4u);
-        if (key >= L) key = L - 8u;
-        dma_b128(mask_row(lane / 4u) + key, sb + 2u * S::KT + 4u * S::SBP);
+    if (MG::DMA) {
+      // past kv_seq_len (a multiple of CPL in these modes): re-read the
+      // chunk that ends at cell L - 1 (never used)
+      uint32_t cell = key0 + MG::CPL * (lane % MG::LPR);
+      if (cell >= L) cell = L - MG::CPL;
+#pragma unroll
+      for (int i = 0; i < MG::NC; ++i) {
+        const char *g = m_l[i] + (size_t)cell * MG::CB;
+        const uint32_t la = sb + 2u * S::KT + 4u * S::SBP + MG::STEP * i;
+        if (MG::WIDE)
+          dma_b128(g, la);
+        else
+          dma_b32(g, la);
       }
-    } else if (MM == kMaskB32) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // lane: row 4i + lane / 16, cells 2 (lane % 16), + 1
-        uint32_t key = key0 + 2u * (lane % 16u);
-        if (key >= L) key = L - 2u;
-        dma_b32(mask_row(4u * i + lane / 16u) + key, sb + 2u * S::KT + 4u * S::SBP + 256u * i);
-      }
-    } else if (MM == kMaskBool) {
-      // past kv_seq_len: re-read cell L - 1 of the row (never used)
-      const uint32_t cell = min(key0 + lane % 32u, L - 1u);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma_b32(mb_l[i] + cell, sb + 2u * S::KT + 4u * S::SBP + 256u * i);
-    } else if (MM == kMaskBoolB128) {
-      // past kv_seq_len (a multiple of 4): re-read cells L - 4 .. L - 1
-      uint32_t cell = key0 + 4u * (lane % 8u);
-      if (cell >= L) cell = L - 4u;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dma_b128(mb_l[i] + cell, sb + 2u * S::KT + 4u * S::SBP + 1024u * i);
     }
   };
   // wait until tile t has landed; `after` later tiles (0 .. NS - 1) may
@@ -377,8 +414,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 #pragma unroll
     for (int arr = 0; arr < 4; ++arr)
       SBl[arr] = reinterpret_cast<const uint32_t *>(st + 2 * S::KT + arr * S::SBP);
-    const half_t *Ml = reinterpret_cast<const half_t *>(st + 2 * S::KT + 4 * S::SBP);
-    const uint32_t *Mb = reinterpret_cast<const uint32_t *>(st + 2 * S::KT + 4 * S::SBP);
+    const char *Ml = st + 2 * S::KT + 4 * S::SBP;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint32_t kr = 16u * kb + n;   // key within the tile
@@ -392,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       const uint32_t k4 = 16u * kb + 4u * gp;
 #pragma unroll
       for (int w = 0; w < S::SBW; ++w) {
-        const uint32_t wi = (k4 * NG) / 2u + w;
+        const uint32_t wi = (k4 * NG) / S::EPW + w;
         T.ksb[kb][0][w] = SBl[0][wi];
         T.ksb[kb][1][w] = SBl[1][wi];
         T.vsb[kb][0][w] = SBl[2][wi];
@@ -406,11 +442,12 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
         if (IMPLICIT) {
           mv = (in && (int64_t)kk <= causal_last) ? 0.0f : kMasked;
         } else if (MM == kMaskReg) {
-          mv = in ? (float)mrow[kk] : kMasked;
-        } else if (MM == kMaskBool || MM == kMaskBoolB128) {
-          mv = (in && Mb[n * BN + k4 + j] != 0u) ? 0.0f : kMasked;
+          mv = in ? elem_f32<ET>(a.mask, mrow + kk) : kMasked;
+        } else if (MG::BOOL) {
+          mv = (in && reinterpret_cast<const uint32_t *>(Ml)[n * BN + k4 + j] != 0u) ? 0.0f
+                                                                                 : kMasked;
         } else {
-          const float x = (float)Ml[n * BN + k4 + j];  // always in the stage
+          const float x = elem_f32<ET>(Ml, n * BN + k4 + j);  // always in the stage
           mv = in ? x : kMasked;
         }
         T.m[kb][j] = mv;
@@ -470,21 +507,24 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
           half8_t kf = word_codes<BITS>(&T.kw[kb][g][sub * S::WPS], cmask);
           sacc[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[g * S::SPG + sub],
                                                                sacc[g][kb], 0, 0, 0);
+          if (QLO)
+            sacc[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                kf, qfl[(g * S::SPG + sub) % (QLO ? STEPS : 1)], sacc[g][kb], 0, 0, 0);
         }
       }
     float s[2][4];
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const half_t *ksc = reinterpret_cast<const half_t *>(T.ksb[kb][0]);
-      const half_t *kbi = reinterpret_cast<const half_t *>(T.ksb[kb][1]);
+      const uint32_t *ksc = T.ksb[kb][0];
+      const uint32_t *kbi = T.ksb[kb][1];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x = 0.0f;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          x = fmaf((float)ksc[j * NG + g], sacc[g][kb][j], x);
-          x = fmaf((float)kbi[j * NG + g], qsum[g], x);
+          x = fmaf(elem_f32<ET>(ksc, j * NG + g), sacc[g][kb][j], x);
+          x = fmaf(elem_f32<ET>(kbi, j * NG + g), qsum[g], x);
         }
         const float mv = T.m[kb][j];
         x = (mv > kMasked) ? fmaf(x, a.qscale, mv * kLog2e) : -INFINITY;
@@ -517,13 +557,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const half_t *vsc = reinterpret_cast<const half_t *>(T.vsb[j >> 2][0]);
-        const half_t *vbi = reinterpret_cast<const half_t *>(T.vsb[j >> 2][1]);
-        const float w = p[j] * (float)vsc[(j & 3) * NG + g];
+        const uint32_t *vsc = T.vsb[j >> 2][0];
+        const uint32_t *vbi = T.vsb[j >> 2][1];
+        const float w = p[j] * elem_f32<ET>(vsc, (j & 3) * NG + g);
         const half_t hi = (half_t)w;
         pf[g][j] = hi;
         pl[g][j] = (half_t)(w - (float)hi);
-        acc = fmaf(p[j], (float)vbi[(j & 3) * NG + g], acc);
+        acc = fmaf(p[j], elem_f32<ET>(vbi, (j & 3) * NG + g), acc);
       }
       pb[g] = pb[g] * alpha + acc;
     }
@@ -597,8 +637,17 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     for (int db = 0; db < DB; ++db) {
       const int g = (16 * db) / G;
       floatx4 o = (oacc[db] + pb[g]) * inv;
-      half4_t h = {(half_t)o[0], (half_t)o[1], (half_t)o[2], (half_t)o[3]};
-      *reinterpret_cast<half4_t *>(a.out + rid * DIM + 16 * db + 4 * gp) = h;
+      const size_t off = rid * DIM + 16 * db + 4 * gp;
+      if (ET == kF32) {
+        *reinterpret_cast<floatx4 *>(reinterpret_cast<float *>(a.out) + off) = o;
+      } else if (ET == kBF16) {
+        const uint32_t lo = f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+        const uint32_t hi = f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + off) = u32x2{lo, hi};
+      } else {
+        half4_t h = {(half_t)o[0], (half_t)o[1], (half_t)o[2], (half_t)o[3]};
+        *reinterpret_cast<half4_t *>(reinterpret_cast<half_t *>(a.out) + off) = h;
+      }
     }
   } else {
     const size_t nrows = (size_t)a.batch * a.nq * a.q_l;
@@ -615,64 +664,66 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   }
 }
 
-template <int DIM, int BITS, int G, int MM>
+template <int DIM, int BITS, int G, int MM, int ET>
 hipError_t launch_qm(const QuantArgs &a, hipStream_t s) {
-  using ST = QStage<DIM, BITS, G, MM>;
+  using ST = QStage<DIM, BITS, G, MM, ET>;
   static const bool attr_set = [] {
-    (void)hipFuncSetAttribute((const void *)quant_kernel<DIM, BITS, G, MM>,
+    (void)hipFuncSetAttribute((const void *)quant_kernel<DIM, BITS, G, MM, ET>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     return true;
   }();
   (void)attr_set;
   dim3 grid(grid_size(a.units, a.row_tiles));
-  hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, MM>), grid, dim3(kThreads), ST::LDS, s, a);
+  hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, MM, ET>), grid, dim3(kThreads), ST::LDS, s, a);
   return hipGetLastError();
 }
 
-template <int DIM, int BITS, int G>
+template <int DIM, int BITS, int G, int ET>
 hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
   if (a.mbool != nullptr) {
     const uint64_t words = a.mask_head_stride | a.mask_stride | a.kv_seq_len |
                            (uint64_t)((uintptr_t)a.mbool / sizeof(uint32_t));
-    if (words % 4 == 0) return launch_qm<DIM, BITS, G, kMaskBoolB128>(a, s);
-    return launch_qm<DIM, BITS, G, kMaskBool>(a, s);
+    if (words % 4 == 0) return launch_qm<DIM, BITS, G, kMaskBoolB128, ET>(a, s);
+    return launch_qm<DIM, BITS, G, kMaskBool, ET>(a, s);
   }
-  if (a.mask == nullptr) return launch_qm<DIM, BITS, G, kMaskNone>(a, s);
+  if (a.mask == nullptr) return launch_qm<DIM, BITS, G, kMaskNone, ET>(a, s);
+  constexpr uint64_t esz = Elem<ET>::SZ;
   const uint64_t all = a.mask_head_stride | a.mask_stride | a.kv_seq_len |
-                       (uint64_t)((uintptr_t)a.mask / sizeof(half_t));
-  if (all % 8 == 0) return launch_qm<DIM, BITS, G, kMaskB128>(a, s);
-  if (all % 2 == 0) return launch_qm<DIM, BITS, G, kMaskB32>(a, s);
-  return launch_qm<DIM, BITS, G, kMaskReg>(a, s);
+                       (uint64_t)((uintptr_t)a.mask / esz);
+  if (all % (16 / esz) == 0) return launch_qm<DIM, BITS, G, kMaskB128, ET>(a, s);
+  if (all % (4 / esz) == 0) return launch_qm<DIM, BITS, G, kMaskB32, ET>(a, s);
+  if constexpr (ET != kF32) return launch_qm<DIM, BITS, G, kMaskReg, ET>(a, s);
+  return hipErrorInvalidValue;   // (4-byte cells always take 4-byte copies)
 }
 
-template <int DIM, int BITS>
+template <int DIM, int BITS, int ET>
 hipError_t launch_qg(const QuantArgs &a, uint32_t G, hipStream_t s) {
   switch (G) {
-    case 32: return launch_q<DIM, BITS, 32>(a, s);
+    case 32: return launch_q<DIM, BITS, 32, ET>(a, s);
     case 64:
-      if constexpr (DIM % 64 == 0) return launch_q<DIM, BITS, 64>(a, s);
+      if constexpr (DIM % 64 == 0) return launch_q<DIM, BITS, 64, ET>(a, s);
       return hipErrorInvalidValue;
     case 128:
-      if constexpr (DIM % 128 == 0) return launch_q<DIM, BITS, 128>(a, s);
+      if constexpr (DIM % 128 == 0) return launch_q<DIM, BITS, 128, ET>(a, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int DIM>
+template <int DIM, int ET>
 hipError_t launch_qb(const QuantArgs &a, uint32_t bits, uint32_t G, hipStream_t s) {
-  return bits == 4 ? launch_qg<DIM, 4>(a, G, s) : launch_qg<DIM, 8>(a, G, s);
+  return bits == 4 ? launch_qg<DIM, 4, ET>(a, G, s) : launch_qg<DIM, 8, ET>(a, G, s);
 }
 
 // Workgroups of one variant a CU holds: the runtime's occupancy answer for
 // the kernel with its LDS, or, with no device to ask, the plan's budgets
 // (two wavefronts per SIMD up to dim 128, one above; 160 KB of LDS).
-template <int DIM, int BITS, int G, int MM>
+template <int DIM, int BITS, int G, int MM, int ET>
 uint32_t wgs_per_cu() {
-  using ST = QStage<DIM, BITS, G, MM>;
+  using ST = QStage<DIM, BITS, G, MM, ET>;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_kernel<DIM, BITS, G, MM>, kThreads,
-                                                   ST::LDS) == hipSuccess &&
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_kernel<DIM, BITS, G, MM, ET>,
+                                                   kThreads, ST::LDS) == hipSuccess &&
       n > 0)
     return (uint32_t)n;
   (void)hipGetLastError();
@@ -681,33 +732,33 @@ uint32_t wgs_per_cu() {
   return by_regs < by_lds ? by_regs : by_lds;
 }
 
-template <int DIM, int BITS, int G>
+template <int DIM, int BITS, int G, int ET>
 uint32_t wgs_per_cu_m(int mask_kind) {
-  // the fp16 mask's copy modes share one footprint (the register-load mode
-  // is smaller); both u32 copy modes share one too
-  if (mask_kind == 2) return wgs_per_cu<DIM, BITS, G, kMaskBoolB128>();
-  if (mask_kind == 1) return wgs_per_cu<DIM, BITS, G, kMaskB128>();
-  return wgs_per_cu<DIM, BITS, G, kMaskNone>();
+  // the T mask's copy modes share one footprint (the register-load mode is
+  // smaller); both u32 copy modes share one too
+  if (mask_kind == 2) return wgs_per_cu<DIM, BITS, G, kMaskBoolB128, ET>();
+  if (mask_kind == 1) return wgs_per_cu<DIM, BITS, G, kMaskB128, ET>();
+  return wgs_per_cu<DIM, BITS, G, kMaskNone, ET>();
 }
 
-template <int DIM, int BITS>
+template <int DIM, int BITS, int ET>
 uint32_t wgs_per_cu_g(uint32_t G, int mask_kind) {
   switch (G) {
-    case 32: return wgs_per_cu_m<DIM, BITS, 32>(mask_kind);
+    case 32: return wgs_per_cu_m<DIM, BITS, 32, ET>(mask_kind);
     case 64:
-      if constexpr (DIM % 64 == 0) return wgs_per_cu_m<DIM, BITS, 64>(mask_kind);
+      if constexpr (DIM % 64 == 0) return wgs_per_cu_m<DIM, BITS, 64, ET>(mask_kind);
       return 0;
     case 128:
-      if constexpr (DIM % 128 == 0) return wgs_per_cu_m<DIM, BITS, 128>(mask_kind);
+      if constexpr (DIM % 128 == 0) return wgs_per_cu_m<DIM, BITS, 128, ET>(mask_kind);
       return 0;
     default: return 0;
   }
 }
 
-template <int DIM>
+template <int DIM, int ET>
 uint32_t wgs_per_cu_b(uint32_t bits, uint32_t G, int mask_kind) {
-  return bits == 4 ? wgs_per_cu_g<DIM, 4>(G, mask_kind)
-                   : bits == 8 ? wgs_per_cu_g<DIM, 8>(G, mask_kind) : 0;
+  return bits == 4 ? wgs_per_cu_g<DIM, 4, ET>(G, mask_kind)
+                   : bits == 8 ? wgs_per_cu_g<DIM, 8, ET>(G, mask_kind) : 0;
 }
 
 }  // namespace

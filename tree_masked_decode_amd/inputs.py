@@ -66,6 +66,16 @@ QUANT_WORKLOADS = {
     "quant_8bit": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
                        kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=8,
                        group_size=64, sinks=True, mask="alibi", nwg=None),
+    # the 4-bit decode with bfloat16 / fp32 queries, scales, biases, bias and
+    # output (the page's kernels are generic in that type)
+    "quant_4bit_bf16": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
+                            kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=4,
+                            group_size=64, sinks=True, mask="alibi", nwg=None,
+                            elem="bf16"),
+    "quant_4bit_f32": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
+                           kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=4,
+                           group_size=64, sinks=True, mask="alibi", nwg=None,
+                           elem="f32"),
     # sliding-window decode: only the last 4096 of 16384 tokens are attended
     "quant_4bit_window": dict(batch=4, n_q_heads=32, n_kv_heads=8, dim=128,
                               kv_seq_len=16384, kv_capacity=16384, q_l=1, bits=4,
