@@ -112,8 +112,8 @@ TA_API uint32_t tree_attn_quant_pick_nwg(uint32_t batch, uint32_t n_q_heads,
  * the call will run: bits, group_size and mask_kind (TA_MASK_*) set its
  * registers and LDS, and so how many workgroups a CU holds at once.  That
  * number comes from the HIP runtime's occupancy query for the variant on the
- * current device; without a device it is estimated from the variant's LDS
- * size.  With a sliding window pass min(window_size, kv_seq_len) as
+ * current device (capped at two wavefronts per SIMD); without a device it is
+ * estimated from the variant's LDS size.  With a sliding window pass min(window_size, kv_seq_len) as
  * kv_seq_len.  Always >= 1.
  */
 TA_API uint32_t tree_attn_quant_pick_nwg_ex(uint32_t batch, uint32_t n_q_heads,

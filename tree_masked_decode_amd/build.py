@@ -32,6 +32,16 @@ CFLAGS = [
 ]
 
 
+# Per-file flags.  The quantized kernel at head dims up to 128 keeps its
+# matrix-instruction accumulators in ordinary VGPRs: its inline rescale of O
+# otherwise makes the compiler copy every accumulator between AGPRs and
+# VGPRs once per tile.  Wider heads need the AGPRs for O.
+FILE_FLAGS = {
+    "quant_d%d_%s.hip" % (d, t): ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    for d in (64, 96, 128) for t in ("f16", "bf16", "f32")
+}
+
+
 def _headers():
     return glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(
         os.path.join(ROOT, "include", "*.h"))
@@ -67,7 +77,8 @@ def build(force: bool = False, verbose: bool = False, extra=()) -> str:
         if force or _stale(o, [s, *hdrs]):
             jobs.append((s, o))
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        for msg in ex.map(lambda j: _compile(j[0], j[1], list(extra)), jobs):
+        for msg in ex.map(lambda j: _compile(
+                j[0], j[1], FILE_FLAGS.get(os.path.basename(j[0]), []) + list(extra)), jobs):
             if verbose and msg.strip():
                 print(msg)
     if force or jobs or _stale(LIB, objs):

@@ -277,7 +277,10 @@ uint32_t tree_attn_quant_pick_nwg_ex(uint32_t batch, uint32_t n_q_heads,
     return 1;
   const int elem = q_dtype == TA_BF16 ? 1 : q_dtype == TA_F32 ? 2 : 0;
   uint32_t per_cu = ta::quant_wgs_per_cu(dim, bits, group_size, mask_kind, elem);
-  if (per_cu == 0) per_cu = 8u;   // not a supported variant: the plain estimate
+  // Not a supported variant: the plain estimate.  Beyond two wavefronts per
+  // SIMD the four SIMDs of a CU no longer get equal shares (10 workgroups
+  // put three on two of them), which measured slower than 8.
+  if (per_cu == 0 || per_cu > 8u) per_cu = 8u;
   uint32_t rows = q_l * (n_q_heads / n_kv_heads);
   const uint64_t kv = 2ull * batch * n_kv_heads * kv_seq_len * dim * (bits ? bits : 4) / 8;
   const uint64_t part = (uint64_t)batch * n_q_heads * q_l * (dim + 2) * 4;

@@ -45,6 +45,7 @@ namespace {
 
 constexpr int kThreads = 64;   // one wavefront per workgroup
 constexpr int BN = 32;         // keys per tile
+constexpr float kLazyQ = 8.0f; // lazy-rescale threshold of the running max (base 2)
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -527,14 +528,19 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
           x = fmaf(elem_f32<ET>(kbi, j * NG + g), qsum[g], x);
         }
         const float mv = T.m[kb][j];
-        x = (mv > kMasked) ? fmaf(x, a.qscale, mv * kLog2e) : -INFINITY;
+        // an excluded cell adds -inf: the arithmetic above stays unconditional
+        x = fmaf(x, a.qscale, (mv > kMasked) ? mv * kLog2e : -INFINITY);
         s[kb][j] = x;
         tmax = fmaxf(tmax, x);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(Mrow, tmax);
+    // Lazy rescale: the reference max M moves only when the tile's max
+    // exceeds it by more than kLazyQ (base 2); until then p <= 2^kLazyQ, held
+    // exactly by the fp32 sums and by the fp16 hi + lo P * scale pair, and
+    // O, S and M stay consistent: the same softmax.
+    const float m_new = (tmax > Mrow + kLazyQ) ? tmax : Mrow;
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(Mrow - m_use);
     float p[8];
