@@ -130,6 +130,14 @@ __device__ inline void dma_b32(const void *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
                : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (global_load_lds_dwordx4 v_off, s[base]): a loop that walks
+// tiles only moves the scalar base, the per-lane offsets stay put.
+__device__ inline void dma_b128_s(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "s"(lds)
+               : "memory", "m0");
+}
 template <int N> __device__ inline void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }

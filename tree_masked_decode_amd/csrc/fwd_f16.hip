@@ -56,6 +56,9 @@ constexpr int kLdsBytes = 160 * 1024;
 // Lazy-rescale threshold of the running max, in base-2 logit units.
 constexpr float kLazy = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
+// LDS operand reads kept in flight ahead of the matrix instructions
+constexpr int kAheadQK = 4;
+constexpr int kAheadPV = 4;
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -92,6 +95,24 @@ template <int CH> __device__ inline uint32_t swz_v(uint32_t row, uint32_t chunk)
   return chunk ^ ((2u * (row & 15u)) & (uint32_t)(CH - 1));
 }
 
+// Instruction-order hint for a block of LDS operand reads feeding matrix
+// instructions: the first AHEAD groups of RD reads go out, then every group
+// of MF matrix instructions is followed by the reads of the group AHEAD steps
+// later, so that AHEAD operand loads are in flight while the matrix cores
+// run instead of each instruction waiting out one LDS round trip.  (Order
+// only: the compiler's wait counts keep every use after its load.)
+template <int STEPS, int RD, int MF, int AHEAD>
+__device__ inline void lds_mfma_pipeline() {
+  static_assert(AHEAD >= 1 && AHEAD <= STEPS, "prefetch depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < STEPS - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, MF * AHEAD, 0);
+}
+
 template <int D, int RB, int MROWS, bool VEC, int W>
 __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   constexpr bool IMPLICIT = MROWS == 0;
@@ -116,7 +137,8 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   const uint32_t last_row = min(row0 + S::RPW, a.rows) - 1u;
   const uint32_t nnodes = last_row / a.group - node0 + 1u;   // nodes of this workgroup
 
-  // ---- the lane's rows and their Q'^T fragments: row n, d = 32ds + 8gp + 0..7 ----
+  // ---- the lane's rows; their Q'^T fragments (row n, d = 32ds + 8gp + 0..7)
+  // are loaded once the first tiles' copies are on their way ----
   uint32_t node[RB];
   bool valid[RB];
   half8_t qf[RB][DS];
@@ -125,21 +147,27 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
     const uint32_t gr = row0 + wave * 16u * RB + 16u * rb + n;
     valid[rb] = gr < a.rows;
     node[rb] = valid[rb] ? gr / a.group : node0;
-    const uint32_t head = hk * a.group + (valid[rb] ? gr % a.group : 0u);
-    const float *qrow = a.q + ((size_t)head * a.q_l + node[rb]) * D;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      floatx4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-      if (valid[rb]) {
-        x0 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp);
-        x1 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp + 4);
-      }
-      x0 *= a.scale;
-      x1 *= a.scale;
-      qf[rb][ds] = half8_t{(half_t)x0[0], (half_t)x0[1], (half_t)x0[2], (half_t)x0[3],
-                           (half_t)x1[0], (half_t)x1[1], (half_t)x1[2], (half_t)x1[3]};
-    }
   }
+  auto load_q = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint32_t gr = row0 + wave * 16u * RB + 16u * rb + n;
+      const uint32_t head = hk * a.group + (valid[rb] ? gr % a.group : 0u);
+      const float *qrow = a.q + ((size_t)head * a.q_l + node[rb]) * D;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        // (a row past the end reads node0's row of its kv head's first head,
+        // in bounds, and is zeroed: no branch splits the loads)
+        floatx4 x0 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp);
+        floatx4 x1 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp + 4);
+        const float sc = valid[rb] ? a.scale : 0.0f;
+        x0 *= sc;
+        x1 *= sc;
+        qf[rb][ds] = half8_t{(half_t)x0[0], (half_t)x0[1], (half_t)x0[2], (half_t)x0[3],
+                             (half_t)x1[0], (half_t)x1[1], (half_t)x1[2], (half_t)x1[3]};
+      }
+    }
+  };
 
   const size_t kvbase = (size_t)hk * a.kv_capacity * D;
   const half_t *K = static_cast<const half_t *>(a.k) + kvbase;
@@ -151,12 +179,15 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   // tile, W_i = wave * KV_PW + i; chunk p is row p / CH, physical chunk
   // p % CH, holding logical chunk (p % CH) ^ (row & 15).
   uint32_t kv_row[S::KV_PW], kv_col[S::KV_PW], v_col[S::KV_PW];
+  uint32_t k_off[S::KV_PW], v_off[S::KV_PW];   // byte offsets within a full tile
 #pragma unroll
   for (int i = 0; i < S::KV_PW; ++i) {
     const uint32_t p = (wave * S::KV_PW + i) * 64u + lane;
     kv_row[i] = p / S::CH;
     kv_col[i] = 8u * swz(kv_row[i], p % S::CH);
     v_col[i] = 8u * swz_v<S::CH>(kv_row[i], p % S::CH);
+    k_off[i] = 2u * (kv_row[i] * D + kv_col[i]);
+    v_off[i] = 2u * (kv_row[i] * D + v_col[i]);
   }
   // mask: node rows of BN cells (128 bytes) back to back; a 16-byte copy
   // covers 8 rows (lane / 8, cells 4 (lane % 8) ..), a 4-byte copy 2 rows
@@ -181,16 +212,29 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
     const uint32_t key0 = t * BN;
     const uint32_t sb = stage_addr(t, t0);
     const bool full = key0 + BN <= L;
+    if (full) {
+      // every key of the tile is below kv_seq_len: a scalar tile base plus
+      // the lane's fixed offset
+      const half_t *base = (PART == 0 ? K : V) + (size_t)key0 * D;
 #pragma unroll
-    for (int i = 0; i < S::KV_PW; ++i) {
-      // keys past kv_seq_len re-read the last valid row (never used)
-      uint32_t key = key0 + kv_row[i];
-      if (!full) key = min(key, L - 1u);
-      const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
-      if (PART == 0)
-        dma_b128(K + (size_t)key * D + kv_col[i], la);
-      else
-        dma_b128(V + (size_t)key * D + v_col[i], la + S::KV_BYTES);
+      for (int i = 0; i < S::KV_PW; ++i) {
+        const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
+        if (PART == 0)
+          dma_b128_s(base, k_off[i], la);
+        else
+          dma_b128_s(base, v_off[i], la + S::KV_BYTES);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::KV_PW; ++i) {
+        // keys past kv_seq_len re-read the last valid row (never used)
+        const uint32_t key = min(key0 + kv_row[i], L - 1u);
+        const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
+        if (PART == 0)
+          dma_b128(K + (size_t)key * D + kv_col[i], la);
+        else
+          dma_b128(V + (size_t)key * D + v_col[i], la + S::KV_BYTES);
+      }
     }
     if (PART == 1) {
 #pragma unroll
@@ -298,6 +342,7 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
           sacc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[rb][ds], sacc[rb][kb], 0, 0, 0);
       }
     }
+    lds_mfma_pipeline<DS * KB, 1, RB, kAheadQK>();
     // online softmax per row block; P^T operands
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -362,6 +407,8 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
       for (int rb = 0; rb < RB; ++rb)
         oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[rb], oacc[rb][db], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);   // the row-sum instructions
+    lds_mfma_pipeline<DB, 2, RB, kAheadPV>();
   };
   // The rare rescale of O and S: kept out of the tile loop below so that the
   // accumulators stay in the matrix-core registers inside it.
@@ -388,6 +435,9 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
       issue(t0 + s, t0, std::integral_constant<int, 0>{});
       issue(t0 + s, t0, std::integral_constant<int, 1>{});
     }
+  // Q after the first copies: the two memory latencies overlap (the wait the
+  // compiler puts before Q's first use also covers those copies)
+  load_q();
   // Top of tile t: wait for its copies, barrier (every wavefront is done with
   // tile t - 1), then start refilling tile t - 1's stage with tile t + NS - 1
   // (K now, V and mask once the scores are out: refill_rest).

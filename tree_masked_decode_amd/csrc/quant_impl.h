@@ -241,9 +241,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   // to the fp32 dot products afterwards.  fp16 Q is used exactly; bf16 Q
   // becomes fp16 (exact for magnitudes in fp16's normal range); fp32 Q is an
   // fp16 hi + lo pair (two matrix instructions per step). ----
+  // (loaded once the first tiles' copies are on their way, so that the two
+  // memory latencies overlap; a row past the end reads row 0 of its kv
+  // stream's first query head, in bounds, and is zeroed)
   constexpr bool QLO = ET == kF32;
   half8_t qf[STEPS], qfl[QLO ? STEPS : 1];
   float qsum[NG];
+  auto load_q = [&]() {
 #pragma unroll
   for (int g = 0; g < NG; ++g) qsum[g] = 0.0f;
   {
@@ -256,7 +260,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
         half8_t f, fl;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float x = valid ? elem_f32<ET>(a.q, qrow + slot_dim<BITS>(w0, j)) : 0.0f;
+          const float xr = elem_f32<ET>(a.q, qrow + slot_dim<BITS>(w0, j));
+          const float x = valid ? xr : 0.0f;
           f[j] = (half_t)x;
           if (QLO) fl[j] = (half_t)(x - (float)f[j]);
           qsum[g] += ET == kF16 ? (float)f[j] : x;
@@ -270,6 +275,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     qsum[g] += __shfl_xor(qsum[g], 16);
     qsum[g] += __shfl_xor(qsum[g], 32);
   }
+  };
 
   const size_t kvrow0 = (size_t)kv * a.kv_capacity;
   const uint32_t *KP = a.kp + kvrow0 * S::WPK;
@@ -606,6 +612,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 #pragma unroll
   for (int i = 0; i < NS; ++i)
     if (t0 + i < t1) issue(t0 + i);
+  load_q();
   Tile cur;
   for (uint32_t t = t0; t < t1; ++t) {
     wait_tile(min(t1 - 1u - t, (uint32_t)(NS - 1)));
