@@ -188,39 +188,58 @@ def record_traffic(workload, fetch_csv, write_csv):
 # --------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample of rows
 # --------------------------------------------------------------------------
+CPU_SAMPLE_S = 12.0   # target wall time of the measured oracle sample
+
+
 def cpu_baseline(name, c, alg, quant):
+    """A pilot over a few rows sizes the sample; the measured run then takes
+    evenly spaced rows for about CPU_SAMPLE_S seconds (all rows if fewer)."""
     import oracle
     import numpy as np
     threads = max(1, min(16, os.cpu_count() or 1))
     if quant:
         nrows = c["q"].shape[0] * c["q"].shape[1]
-        rows = [(r // c["q_l"], r % c["q_l"]) for r in range(0, nrows, max(1, nrows // 32))]
+        to_row = lambda r: (r // c["q_l"], r % c["q_l"])
         mask = None if c["mask"] is None else np.ascontiguousarray(c["mask"]).ravel()
         mb = c.get("mask_bool")
         mb = None if mb is None else np.ascontiguousarray(mb).ravel()
-        t = time.perf_counter()
-        oracle.quant_attention(c["q"], c["k_packed"], c["k_scales"], c["k_biases"],
-                               c["v_packed"], c["v_scales"], c["v_biases"],
-                               n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
-                               bits=c["bits"], group_size=c["group_size"],
-                               scale=c["scale"], sinks=c["sinks"], mask=mask,
-                               mask_bool=mb, mask_head_stride=c["mask_head_stride"],
-                               mask_stride=c["mask_stride"],
-                               window_size=c.get("window_size", 0),
-                               elem=c.get("elem", "f16"), rows=rows, nthreads=threads)
-        dt = time.perf_counter() - t
+
+        def run(rows):
+            oracle.quant_attention(c["q"], c["k_packed"], c["k_scales"], c["k_biases"],
+                                   c["v_packed"], c["v_scales"], c["v_biases"],
+                                   n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
+                                   bits=c["bits"], group_size=c["group_size"],
+                                   scale=c["scale"], sinks=c["sinks"], mask=mask,
+                                   mask_bool=mb, mask_head_stride=c["mask_head_stride"],
+                                   mask_stride=c["mask_stride"],
+                                   window_size=c.get("window_size", 0),
+                                   elem=c.get("elem", "f16"), rows=rows, nthreads=threads)
     else:
-        H, q_l = c["n_heads"], c["q_l"]
-        nrows = H * q_l
-        step = max(1, nrows // 64)
-        rows = [(r // H, r % H) for r in range(0, nrows, step)]
+        H = c["n_heads"]
+        nrows = H * c["q_l"]
+        to_row = lambda r: (r // H, r % H)
         ws = c.get("window_start")
         mask = (None if ws is not None else
                 oracle.tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"]))
+
+        def run(rows):
+            oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
+                             kv_seq_len=c["kv_seq_len"], scale=c["scale"],
+                             window_start=ws or 0, rows=rows, nthreads=threads)
+
+    def sample(n):
+        step = max(1, nrows // max(1, n))
+        return [to_row(r) for r in range(0, nrows, step)][:max(1, n)]
+
+    rows = sample(min(nrows, 2 * threads))
+    t = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t
+    if dt < CPU_SAMPLE_S and len(rows) < nrows:
+        n = min(nrows, max(len(rows) + 1, int(len(rows) * CPU_SAMPLE_S / max(dt, 1e-3))))
+        rows = sample(n)
         t = time.perf_counter()
-        oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
-                         kv_seq_len=c["kv_seq_len"], scale=c["scale"],
-                         window_start=ws or 0, rows=rows, nthreads=threads)
+        run(rows)
         dt = time.perf_counter() - t
     us_call = dt * 1e6 * nrows / len(rows)
     return {"value": round(alg["bytes"] / (us_call * 1e-6) / 1e9, 4), "unit": "GB/s",
