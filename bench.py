@@ -191,9 +191,12 @@ def record_traffic(workload, fetch_csv, write_csv):
 CPU_SAMPLE_S = 12.0   # target wall time of the measured oracle sample
 
 
-def cpu_baseline(name, c, alg, quant):
+def cpu_baseline(name, c, alg, quant, gpu_out=None, tol=None, out_elem=None):
     """A pilot over a few rows sizes the sample; the measured run then takes
-    evenly spaced rows for about CPU_SAMPLE_S seconds (all rows if fewer)."""
+    evenly spaced rows for about CPU_SAMPLE_S seconds (all rows if fewer).
+    With gpu_out (the GPU result of the same inputs, [rows, D]) the sampled
+    rows are also compared with it: max-abs error against tol, plus half an
+    ulp of the output type for fp16 / bf16 outputs."""
     import oracle
     import numpy as np
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -205,7 +208,7 @@ def cpu_baseline(name, c, alg, quant):
         mb = None if mb is None else np.ascontiguousarray(mb).ravel()
 
         def run(rows):
-            oracle.quant_attention(c["q"], c["k_packed"], c["k_scales"], c["k_biases"],
+            return oracle.quant_attention(c["q"], c["k_packed"], c["k_scales"], c["k_biases"],
                                    c["v_packed"], c["v_scales"], c["v_biases"],
                                    n_kv_heads=c["n_kv_heads"], kv_seq_len=c["kv_seq_len"],
                                    bits=c["bits"], group_size=c["group_size"],
@@ -223,31 +226,46 @@ def cpu_baseline(name, c, alg, quant):
                 oracle.tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"]))
 
         def run(rows):
-            oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
+            return oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
                              kv_seq_len=c["kv_seq_len"], scale=c["scale"],
                              window_start=ws or 0, rows=rows, nthreads=threads)
 
     def sample(n):
         step = max(1, nrows // max(1, n))
-        return [to_row(r) for r in range(0, nrows, step)][:max(1, n)]
+        return list(range(0, nrows, step))[:max(1, n)]
 
-    rows = sample(min(nrows, 2 * threads))
+    flat = sample(min(nrows, 2 * threads))
     t = time.perf_counter()
-    run(rows)
+    ref = run([to_row(r) for r in flat])
     dt = time.perf_counter() - t
-    if dt < CPU_SAMPLE_S and len(rows) < nrows:
-        n = min(nrows, max(len(rows) + 1, int(len(rows) * CPU_SAMPLE_S / max(dt, 1e-3))))
-        rows = sample(n)
+    if dt < CPU_SAMPLE_S and len(flat) < nrows:
+        n = min(nrows, max(len(flat) + 1, int(len(flat) * CPU_SAMPLE_S / max(dt, 1e-3))))
+        flat = sample(n)
         t = time.perf_counter()
-        run(rows)
+        ref = run([to_row(r) for r in flat])
         dt = time.perf_counter() - t
+    rows = flat
+    parity = None
+    if gpu_out is not None:
+        got = np.asarray(gpu_out, dtype=np.float64)[flat]
+        ref = np.asarray(ref, dtype=np.float64).reshape(got.shape)
+        diff = np.abs(got - ref)
+        bound = np.full(ref.shape, float(tol))
+        if out_elem == "f16":
+            bound += 0.5 * np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        elif out_elem == "bf16":
+            a = np.abs(ref).astype(np.float32)
+            e = ((a.view(np.uint32) >> np.uint32(23)) & np.uint32(0xff)).astype(np.int64)
+            bound += 0.5 * np.ldexp(1.0, np.maximum(e, 1) - 127 - 7)
+        parity = {"rows": len(flat), "max_abs_err": float(diff.max()), "tol": float(tol),
+                  "ok": bool(np.all(np.isfinite(got)) and np.all(diff <= bound))}
     us_call = dt * 1e6 * nrows / len(rows)
     return {"value": round(alg["bytes"] / (us_call * 1e-6) / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": "%d of %d output rows of %s (each row over all %d keys), "
                       "%.2f s wall; scaled to the whole call"
                       % (len(rows), nrows, name, c["kv_seq_len"], dt),
-            "us_per_call": round(us_call, 1)}
+            "us_per_call": round(us_call, 1), "parity": parity}
 
 
 # --------------------------------------------------------------------------
@@ -384,6 +402,8 @@ def main():
             rc = lib.tree_attn_reduce(*rargs)
             if rc != 0:
                 raise RuntimeError("reduce failed: %s" % _lib.last_error())
+        if ev is not None:
+            ev[2].record(stream)
 
     if args.copy_calibration:
         # a plain device copy of known size, for scaling the PMC byte counters
@@ -402,8 +422,7 @@ def main():
 
     # ---- timed region (cold: rotating copies) ----
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -411,8 +430,14 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
-    fwd_ms = [a.elapsed_time(b) for a, b in evs]
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    call_ms = [e[0].elapsed_time(e[2]) for e in evs]
     fwd_avg_ms = statistics.fmean(fwd_ms)
+
+    def spread(ms):
+        q = np.percentile(np.asarray(ms) * 1e3, [50, 10, 90])
+        return {"median": round(float(q[0]), 2), "p10": round(float(q[1]), 2),
+                "p90": round(float(q[2]), 2)}
     print("timed: %d steps, %.3f ms/step" % (K, ms_step), file=sys.stderr, flush=True)
 
     # ---- warm: one input set, back to back (cache-resident) ----
@@ -422,6 +447,22 @@ def main():
         step(0)
     torch.cuda.synchronize()
     warm_ms = (time.perf_counter() - tw0) * 1e3 / K
+
+    # ---- context: streaming bandwidth of this GPU ----
+    # a device-to-device copy of 1 GiB (reads and writes every byte once),
+    # reported as (read + write bytes) / time, best of five
+    src = torch.ones(ROTATE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    rd = []
+    for _ in range(5):
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        dst.copy_(src)
+        b_ev.record(stream)
+        b_ev.synchronize()
+        rd.append(a_ev.elapsed_time(b_ev))
+    copy_gbs = 2 * ROTATE_BYTES / (min(rd) * 1e-3) / 1e9
+    del src, dst
 
     us_call = ms_step * 1e3
     gbs = alg["bytes"] / (ms_step * 1e-3) / 1e9
@@ -455,6 +496,9 @@ def main():
         "us_per_call": round(us_call, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "warm_us_per_call": round(warm_ms * 1e3, 2),
+        "call_us_events": spread(call_ms),
+        "forward_us_events": spread(fwd_ms),
+        "copy_1GiB_GBs": round(copy_gbs, 1),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(args.workload, kind),
@@ -463,7 +507,14 @@ def main():
                      "mfma_frac": round(fwd_tfs / MFMA_F16_PEAK_TFS, 4)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.workload, c, alg, quant)
+        # the last call above ran on the base input set: compare it with the
+        # oracle on the baseline's sample of rows
+        torch.cuda.synchronize()
+        gpu_out = out.float().cpu().numpy()
+        elem = c.get("elem", "f16") if quant else None
+        tol = 1e-4 if kind == "f32" else 2e-3
+        result["cpu_baseline"] = cpu_baseline(args.workload, c, alg, quant, gpu_out=gpu_out,
+                                              tol=tol, out_elem=elem)
     print(json.dumps(result), flush=True)
 
 
