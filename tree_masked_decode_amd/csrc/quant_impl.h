@@ -197,9 +197,11 @@ template <int DIM, int BITS, int G, int MM, int ET> struct QStage {
   static constexpr int M_BYTES = MG::BYTES;
   static constexpr int BYTES = 2 * S::KT + 4 * S::SBP + M_BYTES;
   static constexpr int PER_TILE = 2 * S::KT_I + S::SB_I + MASK_I;
-  // Eight one-wavefront workgroups share a CU at dim <= 128 (two per SIMD),
-  // so a workgroup keeps within 20 KB of LDS there; wider heads run fewer.
-  static constexpr int BUDGET = DIM <= 128 ? 20 * 1024 : 48 * 1024;
+  // At dim <= 128 the registers allow three one-wavefront workgroups per
+  // SIMD, twelve per CU, so a workgroup keeps within 160 KB / 12 of LDS
+  // there (two stages; measured faster than three stages at eight per CU);
+  // wider heads run fewer.
+  static constexpr int BUDGET = DIM <= 128 ? 160 * 1024 / 12 : 48 * 1024;
   // (and a wavefront's copy counter tracks at most 63 copies in flight)
   static constexpr int NS = (3 * BYTES + S::VL <= BUDGET && 2 * PER_TILE <= 63) ? 3 : 2;
   static constexpr int LDS = NS * BYTES + S::VL;
