@@ -261,8 +261,15 @@ def cpu_baseline(name, c, alg, quant, gpu_out=None, tol=None, out_elem=None):
         parity = {"rows": len(flat), "max_abs_err": float(diff.max()), "tol": float(tol),
                   "ok": bool(np.all(np.isfinite(got)) and np.all(diff <= bound))}
     us_call = dt * 1e6 * nrows / len(rows)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                         None)
+    except OSError:
+        pass
     return {"value": round(alg["bytes"] / (us_call * 1e-6) / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "cpu_model": model, "kind": "oracle",
             "sample": "%d of %d output rows of %s (each row over all %d keys), "
                       "%.2f s wall; scaled to the whole call"
                       % (len(rows), nrows, name, c["kv_seq_len"], dt),
