@@ -122,20 +122,26 @@ uint32_t quant_wgs_per_cu(uint32_t dim, uint32_t bits, uint32_t group, int mask_
 // with wait_vm<N>(), N = vector-memory operations the wavefront issued later
 // that may stay in flight (an undercount of those is never allowed; extra
 // later operations only make the wait stricter).
+// (`lds` and a scalar base are wave-uniform by contract; readfirstlane puts
+// them in SGPRs even where the compiler cannot prove that uniformity, which
+// the "s" operands require.)
+__device__ inline uint32_t sgpr_u32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ inline void dma_b128(const void *g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(sgpr_u32(lds))
                : "memory", "m0");
 }
 __device__ inline void dma_b32(const void *g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(sgpr_u32(lds))
                : "memory", "m0");
 }
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset (global_load_lds_dwordx4 v_off, s[base]): a loop that walks
 // tiles only moves the scalar base, the per-lane offsets stay put.
 __device__ inline void dma_b128_s(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
-               "s"(lds)
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t bs = ((uint64_t)sgpr_u32((uint32_t)(b >> 32)) << 32) | sgpr_u32((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"((const void *)(uintptr_t)bs), "s"(sgpr_u32(lds))
                : "memory", "m0");
 }
 template <int N> __device__ inline void wait_vm() {
