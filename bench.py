@@ -489,6 +489,23 @@ def main():
     else:
         bound, achieved, peak, unit = "hbm", fwd_gbs, HBM_PEAK_GBS, "GB/s"
 
+    # ---- aside: the tree-mask build (setup, not part of a verify call) ----
+    mask_us = None
+    if not quant and c.get("window_start") is None:
+        m_out = torch.empty_like(base["mask"])
+        ta.build_tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"], out=m_out)
+        torch.cuda.synchronize()
+        mt = []
+        for _ in range(10):
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            ta.build_tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"], out=m_out)
+            b_ev.record(stream)
+            b_ev.synchronize()
+            mt.append(a_ev.elapsed_time(b_ev) * 1e3)
+        mask_us = round(statistics.median(mt), 2)
+        del m_out
+
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -511,6 +528,7 @@ def main():
         "call_us_events": spread(call_ms),
         "forward_us_events": spread(fwd_ms),
         "copy_1GiB_GBs": round(copy_gbs, 1),
+        "build_tree_mask_us": mask_us,
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(args.workload, kind),
