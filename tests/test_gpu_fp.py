@@ -82,6 +82,12 @@ SMALL = [
     (7, 8, 8, 512, 611, 9, "f16", 3),
     (8, 6, 1, 128, 2049, 33, "f16", 5),   # 198 rows: 4 row tiles, last ragged
     (9, 2, 1, 256, 65, 1, "f16", 7),      # more splits than tiles
+    # launch plans and mask-tile heights of the fp16 kernel
+    (10, 12, 2, 128, 700, 32, "f16", None),  # d 128, 3 row blocks (192 rows), 32 mask rows
+    (11, 4, 2, 128, 900, 100, "f16", 3),     # d 128, 2 row blocks, 128 mask rows
+    (12, 2, 1, 128, 500, 190, "f16", 2),     # d 128, 3 row blocks, 192 mask rows
+    (13, 4, 4, 256, 600, 100, "f16", 2),     # d 256, group 1: 128 mask rows
+    (14, 16, 8, 512, 700, 40, "f16", 4),     # d 512: 80 rows in 2 row tiles, 64 mask rows
 ]
 
 
