@@ -253,6 +253,21 @@ def test_edges(ta, kvd):
                                   scale=c["scale"]), tol, "additive")
 
 
+@pytest.mark.parametrize("kvd", ["f32", "f16"])
+def test_dead_band_inside_one_split(ta, kvd):
+    # live tiles, then whole tiles masked for every row (skipped), then live
+    # tiles again, all in one split: the tile after the band must be fetched
+    # although the band's arithmetic was skipped
+    note("dead band inside one split %s" % kvd)
+    c = small_case(20, 8, 2, 128, 700, 6, kvd)
+    m = oracle.tree_mask(c["parents"], 700)
+    m[:, 96:352] = -65504.0      # tiles 3..10 of 32 keys (and 6..21 of 16)
+    ref = oracle.attention(c["q"], c["k"], c["v"], m, n_kv_heads=2, kv_seq_len=700,
+                           scale=c["scale"])
+    for nwg in (1, 2):
+        assert_close(run_verify(ta, c, m, nwg=nwg), ref, TOL[kvd], "band nwg=%d" % nwg)
+
+
 def test_unaligned_mask_stride(ta):
     note("odd mask stride (scalar mask path)")
     c = small_case(19, 8, 2, 256, 501, 6, "f16", stride=503)

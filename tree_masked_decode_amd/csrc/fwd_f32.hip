@@ -101,6 +101,27 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   constexpr int kRowsPerThread = kRT * BN / kThreads;
   constexpr int kRowStep = kThreads / BN;
 
+  // K/V tile loads go into registers one tile ahead, so that their latency
+  // overlaps the arithmetic of the tile before (keys past kv_seq_len read as
+  // zero).
+  constexpr int kLoadsPerThread = BN * D / 4 / kThreads;
+  static_assert(kLoadsPerThread * kThreads * 4 == BN * D, "tile / thread shape");
+  floatx4 kreg[kLoadsPerThread], vreg[kLoadsPerThread];
+  auto load_kv = [&](uint32_t t) {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) {
+      const uint32_t e = tid + (uint32_t)i * kThreads;
+      const uint32_t key = e / (D / 4), c4 = e % (D / 4);
+      kreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      vreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (t * BN + key < a.kv_seq_len) {
+        kreg[i] = *reinterpret_cast<const floatx4 *>(K + (size_t)(t * BN + key) * D + 4 * c4);
+        vreg[i] = *reinterpret_cast<const floatx4 *>(V + (size_t)(t * BN + key) * D + 4 * c4);
+      }
+    }
+  };
+  if (t0 < t1) load_kv(t0);
+
   for (uint32_t t = t0; t < t1; ++t) {
     const uint32_t key0 = t * BN;
     // --- mask cells of this thread's (row, key) pairs; tile liveness ---
@@ -116,31 +137,38 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
     }
     // Every cell of the tile masked: skip it ("tree_attention.metal" skips a
     // chunk whose cells are all at or below -65504).
-    if (!__syncthreads_or(live)) continue;
+    if (!__syncthreads_or(live)) {
+      if (t + 1 < t1) load_kv(t + 1);   // (the registers held this tile)
+      continue;
+    }
 
-    // --- stage K/V tile (keys past kv_seq_len read as zero) ---
-    for (uint32_t e = tid; e < (uint32_t)(BN * D / 4); e += kThreads) {
-      uint32_t key = e / (D / 4), c4 = e % (D / 4);
-      floatx4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (key0 + key < a.kv_seq_len) {
-        kx = *reinterpret_cast<const floatx4 *>(K + (size_t)(key0 + key) * D + 4 * c4);
-        vx = *reinterpret_cast<const floatx4 *>(V + (size_t)(key0 + key) * D + 4 * c4);
-      }
+    // --- stage the K/V tile from registers, then fetch the next live one ---
 #pragma unroll
-      for (int x = 0; x < 4; ++x) Ks[key * S::KST + 4 * c4 + x] = kx[x];
-      *reinterpret_cast<floatx4 *>(Vs + key * D + 4 * c4) = vx;
+    for (int i = 0; i < kLoadsPerThread; ++i) {
+      const uint32_t e = tid + (uint32_t)i * kThreads;
+      const uint32_t key = e / (D / 4), c4 = e % (D / 4);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) Ks[key * S::KST + 4 * c4 + x] = kreg[i][x];
+      *reinterpret_cast<floatx4 *>(Vs + key * D + 4 * c4) = vreg[i];
     }
     __syncthreads();
+    if (t + 1 < t1) load_kv(t + 1);
 
     // --- scores s = scale*log2e * q.k + log2e * mask (base-2 logits) ---
+    // (four partial sums over d, so that the FMA chains overlap)
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {
       uint32_t r = sr + u * kRowStep;
       const float *qr = Qs + r * S::QST;
       const float *kr = Ks + sj * S::KST;
-      float dot = 0.0f;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) dot = fmaf(qr[d], kr[d], dot);
+      float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+      for (int d = 0; d < D; d += 4) {
+        const floatx4 q4 = *reinterpret_cast<const floatx4 *>(qr + d);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) d4[x] = fmaf(q4[x], kr[d + x], d4[x]);
+      }
+      const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
       float s = fmaf(dot, a.qscale, mval[u] * kLog2e);
       Ps[r * S::PST + sj] = (mval[u] > kMasked) ? s : -INFINITY;
     }
@@ -180,11 +208,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
     for (int k = 0; k < S::EPT; ++k) {
       uint32_t e = tid + k * kThreads;
       uint32_t r = e / D, d = e % D;
-      float o = acc[k] * Arow[r];
       const float *pr = Ps + r * S::PST;
-#pragma unroll 8
-      for (int j = 0; j < BN; ++j) o = fmaf(pr[j], Vs[j * D + d], o);
-      acc[k] = o;
+      float o4[4] = {acc[k] * Arow[r], 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < BN; j += 4)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o4[x] = fmaf(pr[j + x], Vs[(j + x) * D + d], o4[x]);
+      acc[k] = (o4[0] + o4[1]) + (o4[2] + o4[3]);
     }
     __syncthreads();
   }
