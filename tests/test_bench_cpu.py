@@ -7,6 +7,7 @@ check must pass; a planted error in one element must fail it."""
 from __future__ import annotations
 
 import os
+import subprocess
 import sys
 
 import numpy as np
@@ -79,3 +80,11 @@ def test_baseline_sample_size(monkeypatch, target, expect_all):
     else:
         assert n == min(total, 4)
     assert r["parity"] is None
+
+
+def test_bench_refuses_several_gpus():
+    # one GPU only: the refusal comes before anything touches a device
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
