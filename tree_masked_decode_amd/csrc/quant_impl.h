@@ -67,6 +67,14 @@ __device__ inline uint32_t masked_codes_to_h2(uint32_t x, uint32_t m) {
   const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
   return as_u(h - k1024);
 }
+// The same for codes in bits 4..7 of each half, (x & (m << 4)): 1024 + 16c
+// as fp16, mapped to c exactly by one packed fma, (y / 16 - 64).
+__device__ inline uint32_t masked_hi_codes_to_h2(uint32_t x, uint32_t m4) {
+  const half2_t h = as_h2((x & m4) | 0x64006400u);
+  const half2_t s = {(half_t)0.0625f, (half_t)0.0625f};
+  const half2_t b = {(half_t)-64.0f, (half_t)-64.0f};
+  return as_u(h * s + b);
+}
 template <int BITS> __device__ inline uint32_t code_pair_mask() {
   uint32_t m;
   if (BITS == 4)
@@ -82,10 +90,13 @@ template <int BITS>
 __device__ inline half8_t word_codes(const uint32_t *w, uint32_t m) {
   u32x4 r;
   if (BITS == 4) {
+    // odd nibbles in place (no shift); one shift brings nibbles 2, 3 (and
+    // 6, 7) down to bits 0..7
+    const uint32_t w8 = w[0] >> 8;
     r[0] = masked_codes_to_h2(w[0], m);
-    r[1] = masked_codes_to_h2(w[0] >> 4, m);
-    r[2] = masked_codes_to_h2(w[0] >> 8, m);
-    r[3] = masked_codes_to_h2(w[0] >> 12, m);
+    r[1] = masked_hi_codes_to_h2(w[0], m << 4);
+    r[2] = masked_codes_to_h2(w8, m);
+    r[3] = masked_hi_codes_to_h2(w8, m << 4);
   } else {
     r[0] = masked_codes_to_h2(w[0], m);
     r[1] = masked_codes_to_h2(w[0] >> 8, m);
@@ -499,9 +510,20 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     Srow = (gp == 0) ? 1.0f : 0.0f;
   }
 
-  const uint32_t vshift = (BITS == 4) ? 4u * (n & 7u) : 8u * (n & 3u);
-  const uint32_t vmask = (1u << BITS) - 1u;
   const uint32_t cmask = code_pair_mask<BITS>();
+  // V code extraction, two keys at a time: v_perm_b32 moves the byte that
+  // holds the lane's code (dim 16db + n) out of each key's word into bytes 0
+  // and 2; the code mask and 1024.0's exponent turn them into an fp16 pair
+  // 1024 + c (low nibble or byte) or 1024 + 16c (high nibble), and one
+  // packed fma maps that to c exactly: (y - 1024) or (y / 16 - 64).
+  const uint32_t vbyte = (BITS == 4) ? ((n & 7u) >> 1) : (n & 3u);
+  const uint32_t vsel = vbyte | (0x0Cu << 8) | ((4u + vbyte) << 16) | (0x0Cu << 24);
+  const bool vhi = BITS == 4 && (n & 1u) != 0u;
+  const uint32_t vcm = (BITS == 4) ? (vhi ? 0x00F000F0u : 0x000F000Fu) : 0x00FF00FFu;
+  const half2_t vmul = vhi ? half2_t{(half_t)0.0625f, (half_t)0.0625f}
+                           : half2_t{(half_t)1.0f, (half_t)1.0f};
+  const half2_t vadd = vhi ? half2_t{(half_t)-64.0f, (half_t)-64.0f}
+                           : half2_t{(half_t)-1024.0f, (half_t)-1024.0f};
 
   auto compute = [&](const Tile &T) {
     // scores, one accumulator per scale group
@@ -591,15 +613,16 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       const uint32_t w = (16u * db + n) * BITS / 32u;
       const u32x4 lo = *reinterpret_cast<const u32x4 *>(&vlds[w * S::RS + 8u * gp]);
       const u32x4 hi = *reinterpret_cast<const u32x4 *>(&vlds[w * S::RS + 8u * gp + 4u]);
-      uint32_t c[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = (lo[j] >> vshift) & vmask;
-        c[4 + j] = (hi[j] >> vshift) & vmask;
-      }
       u32x4 r;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = codes_to_h2(c[2 * e] | (c[2 * e + 1] << 16));
+      for (int e = 0; e < 4; ++e) {
+        // keys of slots 2e (low half) and 2e + 1 (high half)
+        const uint32_t w0 = e < 2 ? lo[2 * e] : hi[2 * e - 4];
+        const uint32_t w1 = e < 2 ? lo[2 * e + 1] : hi[2 * e - 3];
+        const uint32_t x = __builtin_amdgcn_perm(w1, w0, vsel);
+        const half2_t y = as_h2((x & vcm) | 0x64006400u);
+        r[e] = as_u(y * vmul + vadd);
+      }
       const int g = (16 * db) / G;
       const half8_t vf = __builtin_bit_cast(half8_t, r);
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[g], oacc[db], 0, 0, 0);
