@@ -43,10 +43,12 @@ def run_verify(ta, c, mask_np, nwg=None, **kw):
     return host(out)
 
 
-def small_case(seed, H, Hk, D, L, q_l, kvd, tree="dynamic", cap=None, stride=None):
+def small_case(seed, H, Hk, D, L, q_l, kvd, tree="dynamic", cap=None, stride=None,
+               scale=None):
     return inputs.fp_case(dict(n_heads=H, n_kv_heads=Hk, head_dim=D, kv_seq_len=L,
                                kv_capacity=cap or L + 7, q_l=q_l, tree=tree,
-                               mask_stride=stride or L, kv_dtype=kvd, kv_std=1.0),
+                               mask_stride=stride or L, kv_dtype=kvd, kv_std=1.0,
+                               scale=scale),
                           seed=seed)
 
 
@@ -130,6 +132,9 @@ def test_workload_fixed_tree(ta):
 
 
 def _sampled(ta, name, nrows, gpu_mask=True):
+    """Run a workload at full size in bench.py's launch configuration and
+    compare nrows (node, head) rows with the oracle (every row if nrows is
+    None)."""
     import torch
     c = inputs.fp_case(name)
     L, H = c["kv_seq_len"], c["n_heads"]
@@ -141,23 +146,28 @@ def _sampled(ta, name, nrows, gpu_mask=True):
     torch.cuda.synchronize()
     got = host(out)
     assert np.all(np.isfinite(got))
-    rows = sample_rows(c["q_l"], H, nrows)
-    ref = oracle.attention(c["q"], c["k"], c["v"], mask_np, n_kv_heads=c["n_kv_heads"],
-                           kv_seq_len=L, scale=c["scale"], rows=rows)
-    sel = np.stack([got[i, h] for i, h in rows])
-    assert_close(sel, ref, TOL["f16"], name)
+    if nrows is None:
+        ref = oracle.attention(c["q"], c["k"], c["v"], mask_np, n_kv_heads=c["n_kv_heads"],
+                               kv_seq_len=L, scale=c["scale"])
+        assert_close(got, ref, TOL["f16"], name)
+    else:
+        rows = sample_rows(c["q_l"], H, nrows)
+        ref = oracle.attention(c["q"], c["k"], c["v"], mask_np, n_kv_heads=c["n_kv_heads"],
+                               kv_seq_len=L, scale=c["scale"], rows=rows)
+        sel = np.stack([got[i, h] for i, h in rows])
+        assert_close(sel, ref, TOL["f16"], name)
     return c, (q, k, v, m), nwg, got
 
 
 def test_workload_dynamic_tree_32k(ta):
-    note("workload dynamic_tree_32k (sampled rows)")
-    _sampled(ta, "dynamic_tree_32k", 64)
+    note("workload dynamic_tree_32k (every row)")
+    _sampled(ta, "dynamic_tree_32k", None)
 
 
 def test_workload_long_context_128k(ta):
     import torch
     note("workload long_context_128k (sampled rows) + byte identity")
-    c, (q, k, v, m), nwg, got = _sampled(ta, "long_context_128k", 16)
+    c, (q, k, v, m), nwg, got = _sampled(ta, "long_context_128k", 64)
     implicit = ta.verify(q, k, v, None, kv_seq_len=c["kv_seq_len"], scale=c["scale"],
                          nwg=nwg)
     torch.cuda.synchronize()
@@ -297,6 +307,115 @@ def test_reduce_alone_on_oracle_partials(ta):
         T.tree_attn_reduce(part, out, nrows=nrows, head_dim=D, nwg=nw)
         torch.cuda.synchronize()
         assert_close(host(out), oracle.lse_combine(o_un, s, mx), tol, "reduce")
+
+
+# --------------------------------------------------------------------------
+# the wide fp16 forward (head dim 256, at least 192 rows per kv head: one
+# wavefront per SIMD with 48 rows, 192-row tiles, 4-stage K/V ring, mask
+# cells classified per tile)
+# --------------------------------------------------------------------------
+WIDE = [
+    # seed, H, Hk, L, q_l, tree, nwg, softmax scale (None: 1/sqrt(256))
+    (60, 24, 4, 1000, 64, "dynamic", 3, None),    # 384 rows: two row tiles; ragged tail
+    (61, 12, 2, 2049, 40, "dynamic", 5, None),    # 240 rows: the second tile has 3 padding waves
+    (62, 16, 4, 777, 64, "dynamic", None, None),  # group 4: two mask copies per wavefront
+    (63, 24, 4, 3000, 64, "binary", 2, 0.125),    # logits twice as wide: the reference max moves
+    (64, 24, 4, 40, 32, "dynamic", 1, None),      # one partial tile, direct output
+    (65, 24, 4, 5000, 64, "chain", 7, None),
+    (66, 12, 2, 33, 32, "dynamic", 2, None),      # two tiles, the second holds one key
+    (67, 48, 8, 1500, 16, "binary", None, None),  # group 6, 96 rows: not wide (reference plan)
+]
+
+
+@pytest.mark.parametrize("seed,H,Hk,L,q_l,tree,nwg,scale", WIDE)
+def test_wide_forward_parity(ta, seed, H, Hk, L, q_l, tree, nwg, scale):
+    note("wide seed=%d H=%d Hk=%d L=%d q_l=%d %s nwg=%s scale=%s" %
+         (seed, H, Hk, L, q_l, tree, nwg, scale))
+    c = small_case(seed, H, Hk, 256, L, q_l, "f16", tree=tree, scale=scale)
+    mask = oracle.tree_mask(c["parents"], L, c["mask_stride"])
+    got = run_verify(ta, c, mask, nwg=nwg)
+    ref = oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=Hk,
+                           kv_seq_len=L, scale=c["scale"])
+    assert_close(got, ref, TOL["f16"], "wide %d" % seed)
+
+
+@pytest.mark.parametrize("nwg", [1, 4])
+def test_wide_chain_byte_identical_to_implicit(ta, nwg):
+    note("wide byte identity nwg=%d" % nwg)
+    L, q_l = 1500, 40
+    c = small_case(68, 24, 4, 256, L, q_l, "f16", tree="chain")
+    mask = oracle.tree_mask(c["parents"], L, L)
+    a = run_verify(ta, c, mask, nwg=nwg)
+    b = run_verify(ta, c, None, nwg=nwg)
+    ref = oracle.attention(c["q"], c["k"], c["v"], None, n_kv_heads=4, kv_seq_len=L,
+                           scale=c["scale"])
+    assert_close(b, ref, TOL["f16"], "wide implicit")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("ws,nwg", [(100, 3), (31, 2), (1990, 5), (0, None)])
+def test_wide_decode_window(ta, ws, nwg):
+    note("wide decode ws=%d nwg=%s" % (ws, nwg))
+    L, q_l = 2000, 40
+    c = small_case(69, 24, 4, 256, L, q_l, "f16", tree="chain")
+    got = run_decode(ta, c, ws, nwg)
+    ref = oracle.attention(c["q"], c["k"], c["v"], None, n_kv_heads=4, kv_seq_len=L,
+                           scale=c["scale"], window_start=ws)
+    assert_close(got, ref, TOL["f16"], "wide decode ws=%d" % ws)
+    abs_pos = L - q_l + np.arange(q_l)
+    assert np.all(got[abs_pos < ws] == 0.0)
+
+
+def test_wide_masks(ta):
+    note("wide masked rows, masked band, additive cells")
+    L, q_l = 1200, 40
+    c = small_case(70, 24, 4, 256, L, q_l, "f16")
+    m = oracle.tree_mask(c["parents"], L)
+    m[:, 96:352] = -65504.0           # a band of whole tiles masked for every row
+    m[3, :] = -65504.0                # a row that sees nothing
+    m[:, 500:510] = -np.inf           # -inf cells are excluded as well
+    got = run_verify(ta, c, m, nwg=3)
+    assert np.all(got[3] == 0.0)
+    assert_close(got, oracle.attention(c["q"], c["k"], c["v"], m, n_kv_heads=4,
+                                       kv_seq_len=L, scale=c["scale"]), TOL["f16"], "band")
+    # additive (non-sentinel) mask values everywhere: every tile takes the
+    # per-cell path
+    m2 = np.random.default_rng(5).uniform(-4, 1, size=(q_l, L)).astype(np.float32)
+    assert_close(run_verify(ta, c, m2, nwg=2),
+                 oracle.attention(c["q"], c["k"], c["v"], m2, n_kv_heads=4, kv_seq_len=L,
+                                  scale=c["scale"]), TOL["f16"], "additive")
+    # prefix fully masked: only ancestors and self
+    m3 = oracle.tree_mask(c["parents"], L)
+    m3[:, :L - q_l] = -65504.0
+    assert_close(run_verify(ta, c, m3, nwg=4),
+                 oracle.attention(c["q"], c["k"], c["v"], m3, n_kv_heads=4, kv_seq_len=L,
+                                  scale=c["scale"]), TOL["f16"], "masked prefix")
+
+
+def test_wide_poisoned_and_deterministic(ta):
+    import torch
+    note("wide poison + determinism")
+    L, stride, cap, q_l = 1100, 1108, 1300, 40
+    c = small_case(71, 24, 4, 256, L, q_l, "f16", cap=cap, stride=stride)
+    mask = oracle.tree_mask(c["parents"], L, stride)
+    clean = run_verify(ta, c, mask, nwg=3)
+    again = run_verify(ta, c, mask, nwg=3)
+    assert np.array_equal(clean.view(np.uint32), again.view(np.uint32))
+    p = dict(c)
+    p["k"] = c["k"].copy()
+    p["v"] = c["v"].copy()
+    p["k"][:, L:] = np.nan
+    p["v"][:, L:] = np.nan
+    pm = mask.copy()
+    pm[:, L:] = 0.0
+    q, k, v, m = gpu_case(p, pm)
+    H = c["q"].shape[0]
+    import tree_masked_decode_amd as T
+    part = torch.full((T.partials_bytes(H, 256, q_l, 3) // 4,), float("nan"), device="cuda")
+    out = torch.full((q_l, H, 256), 12345.0, device="cuda")
+    T.verify(q, k, v, m, kv_seq_len=L, scale=c["scale"], nwg=3, out=out, partials=part)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint32), clean.view(np.uint32))
 
 
 # --------------------------------------------------------------------------

@@ -43,6 +43,7 @@ FILE_FLAGS = {
 # The fp16 forward's inputs are finite by contract: without NaNs to honour,
 # fmaxf on matrix-instruction results needs no canonicalizing instruction.
 FILE_FLAGS["fwd_f16.hip"] = ["-fno-honor-nans"]
+FILE_FLAGS["fwd_wide.hip"] = ["-fno-honor-nans"]
 
 
 def _headers():

@@ -121,7 +121,10 @@ uint32_t tree_attn_pick_nwg(uint32_t n_heads, uint32_t n_kv_heads,
     return 1;
   uint32_t rows = q_l * (n_heads / n_kv_heads);
   bool f16 = kv_dtype == TA_F16;
-  uint32_t rpw = f16 ? ta::f16_rows_per_wg(head_dim, rows) : ta::kF32RowsPerWG;
+  // (the planner assumes a 16-byte aligned mask with a stride of whole
+  // 16-byte chunks, or none)
+  uint32_t rpw = f16 ? ta::f16_rows_per_wg(head_dim, rows, n_heads / n_kv_heads, false, true)
+                     : ta::kF32RowsPerWG;
   uint32_t bn = f16 ? ta::f16_tile_keys(head_dim) : ta::f32_tile_keys(head_dim);
   // One resident fp16 workgroup per CU (its registers fill the SIMDs); the
   // fp32 kernel fits two.
@@ -246,7 +249,9 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
   a.qscale = scale * ta::kLog2e;
   a.scale = scale;
   const bool f16 = kv_dtype == TA_F16;
-  const uint32_t rpw = f16 ? ta::f16_rows_per_wg(head_dim, a.rows) : ta::kF32RowsPerWG;
+  const bool mask_vec = mask == nullptr || ((uintptr_t)mask % 16u == 0 && mask_stride % 4u == 0);
+  const uint32_t rpw = f16 ? ta::f16_rows_per_wg(head_dim, a.rows, a.group, mask == nullptr, mask_vec)
+                           : ta::kF32RowsPerWG;
   const uint32_t bn = f16 ? ta::f16_tile_keys(head_dim) : ta::f32_tile_keys(head_dim);
   a.row_tiles = ceil_div(a.rows, rpw);
   a.n_tiles = ceil_div(kv_seq_len, bn);

@@ -106,8 +106,16 @@ hipError_t launch_tree_mask(const MaskArgs &a, hipStream_t s);
 constexpr uint32_t kF32RowsPerWG = 16;
 constexpr uint32_t kQuantRowsPerWG = 16;
 uint32_t f16_tile_keys(uint32_t head_dim);
-// Rows one workgroup of the fp16 kernel covers for this shape.
-uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows);
+// Rows one workgroup of the fp16 forward covers for this shape (group =
+// query heads per kv head; implicit = no mask buffer; mask_vec = mask rows
+// 16-byte aligned).
+uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows, uint32_t group, bool implicit,
+                         bool mask_vec);
+// The wide fp16 forward (one wavefront per SIMD, 48 rows each): whether it
+// serves this shape, and its launcher.
+bool wide_applies(uint32_t head_dim, uint32_t rows, uint32_t group, bool implicit, bool mask_vec);
+uint32_t wide_rows_per_wg();
+hipError_t launch_forward_wide(const FwdArgs &a, uint32_t head_dim, hipStream_t s);
 uint32_t f32_tile_keys(uint32_t head_dim);
 uint32_t quant_tile_keys(uint32_t dim);
 // Resident workgroups per CU of the quantized kernel variant (0: no such

@@ -585,12 +585,17 @@ static F16Plan f16_plan(uint32_t head_dim, uint32_t rows) {
   return F16Plan{4u, best};
 }
 
-uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows) {
+uint32_t f16_rows_per_wg(uint32_t head_dim, uint32_t rows, uint32_t group, bool implicit,
+                         bool mask_vec) {
+  if (wide_applies(head_dim, rows, group, implicit, mask_vec)) return wide_rows_per_wg();
   const F16Plan p = f16_plan(head_dim, rows);
   return 16u * p.w * p.rb;
 }
 
 hipError_t launch_forward_f16(const FwdArgs &a, uint32_t head_dim, hipStream_t s) {
+  const bool implicit = a.mask == nullptr;
+  const bool vec = ((uintptr_t)a.mask % 16u == 0) && (a.mask_stride % 4u == 0);
+  if (wide_applies(head_dim, a.rows, a.group, implicit, vec)) return launch_forward_wide(a, head_dim, s);
   const F16Plan p = f16_plan(head_dim, a.rows);
   switch (head_dim) {
     case 128:

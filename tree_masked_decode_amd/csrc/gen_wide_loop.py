@@ -1,0 +1,561 @@
+#!/usr/bin/env python3
+"""Generate fwd_wide_loop.inc: the tile loop of the wide fp16 forward
+(fwd_wide.hip) as one CDNA4 inline-assembly block per mask mode.
+
+The loop is written out instruction by instruction because its schedule is
+the point: one wavefront per SIMD keeps O (48 rows x 256 dims, fp32) in the
+accumulation registers, Q'^T (48 rows) in ordinary registers, and streams
+each 32-key tile's K and V operands from LDS into a six-slot register ring
+four operands ahead of the matrix instructions that use them; the softmax of
+tile t (exp2 + fp16 packing + a packed-integer range check) is interleaved
+with the score instructions of tile t+1.  The compiler, given the same work
+in C++, serialises the LDS reads behind their matrix instructions and moves
+accumulators between register files every tile.
+
+Usage: python gen_wide_loop.py  (writes fwd_wide_loop.inc next to itself).
+
+Register map (fixed; fwd_wide.hip binds its variables to these ranges):
+  a[0:191]    O^T accumulators, block (rb, db) at a[64 rb + 4 db : +3]
+  a[192:203]  row sums (ones . P^T), rb at a[192 + 4 rb : +3]
+  a[204:206]  the reference max the pending scores were issued with, saved
+              when a slow step moves M (see "stale" below)
+  v[0:95]     Q'^T fragments, (rb, ds) at v[32 rb + 4 ds : +3]
+  v[96:143]   scores, buffer b (tile parity), (rb, kb) at v[96 + 24 b + 8 rb + 4 kb : +3]
+  v[144:155]  P^T fragments (fp16), rb at v[144 + 4 rb : +3]
+  v[156:159]  a half8 of ones (row-sum operand)
+  v[160:171]  score accumulator input -M' (four copies), rb at v[160 + 4 rb : +3]
+  v[172:174]  reference max M of each row block (base 2; -inf until a key is seen)
+  v[175]      4 gp
+  v[176:199]  operand ring, 6 slots of 4 registers; temporaries in the slow paths
+  v[200:207]  softmax temporaries
+  v[208:215]  LDS address of K chunk (n, 4 ds + gp) of stage 0 (with the swizzle)
+  v[216:231]  LDS address of the V^T read of d-block db, stage 0
+  v[232:235]  byte offset of K copy i within a full tile (V at v[236:239])
+  v[240:241]  byte offset of the mask copy j of this lane (its node row + 16 (lane % 8))
+  v[242]      LDS address of this lane's 16 bytes of the stage-0 mask area
+  v[243]      16 (lane % 8)
+  v[244:246]  LDS address of row block rb's mask cells (node - nlo) * 128 + 16 gp, stage 0
+  v[247:249]  last key row block rb may see under the implicit rule (L - q_l + node)
+  a[208:211]  tile row of K/V copy i
+  (v[250:255] stay free for the compiler's whole-wave register needs)
+SGPRs s80..s99 are the loop's own (declared clobbered):
+  s80 t  s81 last tile  s82 flags (bit 0: every M finite, bit 1: stale)
+  s83 s84 temporaries  s85 fetch tile u  s[86:87] K tile pointer
+  s[88:89] V tile pointer  s[90:91] mask tile pointer  s92 first key of u
+  s93 next tile tn  s94 first key of tn  s95 L - 1  s[96:97] return address
+  s[98:99] 64-bit temporary, and the return address of the rescale
+
+Hazards (gfx950, as the compiler itself spaces them): a matrix result read by
+a VALU needs 8 wait states, a VALU result read by a matrix instruction 2, an
+exp result read by a VALU 1, a VALU result read by v_permlane*_swap 2.  The
+loop never reads a matrix result within 8 instructions of the instruction
+that writes it; where the distance is not structural it pads with s_nop.
+"""
+
+import os
+
+D, RB, W, NS, BN = 256, 3, 4, 4, 32
+KVB = BN * D * 2          # bytes of one K (or V) tile
+DS, DB = D // 32, D // 16
+KV_PW = KVB // 1024 // W  # 1 KB copies per wavefront per K (or V) tile
+RING = 6
+AHEAD = 4
+LAZY = 15.0               # the reference max moves when a tile's row max exceeds it by > 15 (base 2)
+LAZY_F16 = 0x7800         # 2^15 as fp16 bits: a fast-path p above it needs a new reference
+
+F32_NEG65504 = 0xC77FE000
+F32_LOG2E = 0x3FB8AA3B
+F32_NEGINF = 0xFF800000
+F32_LAZY = 0x41700000     # 15.0
+
+
+def r4(base):
+    return "v[%d:%d]" % (base, base + 3)
+
+
+def O(rb, db):
+    b = 64 * rb + 4 * db
+    return "a[%d:%d]" % (b, b + 3)
+
+
+def RS(rb):
+    b = 192 + 4 * rb
+    return "a[%d:%d]" % (b, b + 3)
+
+
+def AREF(rb):
+    return "a%d" % (204 + rb)
+
+
+def Q(rb, ds):
+    return r4(32 * rb + 4 * ds)
+
+
+def S(buf, rb, kb, j=None):
+    b = 96 + 24 * buf + 8 * rb + 4 * kb
+    return r4(b) if j is None else "v%d" % (b + j)
+
+
+def P(rb, k=None):
+    b = 144 + 4 * rb
+    return r4(b) if k is None else "v%d" % (b + k)
+
+
+ONES = "v[156:159]"
+
+
+def C(rb, j=None):
+    b = 160 + 4 * rb
+    return r4(b) if j is None else "v%d" % (b + j)
+
+
+def M2(rb):
+    return "v%d" % (172 + rb)
+
+
+def B(i):
+    return r4(176 + 4 * (i % RING))
+
+
+def Blo(i):
+    b = 176 + 4 * (i % RING)
+    return "v[%d:%d]" % (b, b + 1)
+
+
+def Bhi(i):
+    b = 176 + 4 * (i % RING)
+    return "v[%d:%d]" % (b + 2, b + 3)
+
+
+def T(k):
+    return "v%d" % (200 + k)
+
+
+def OFFK(ds):
+    return "v%d" % (208 + ds)
+
+
+def OFFV(db):
+    return "v%d" % (216 + db)
+
+
+def KOFF(i):
+    return "v%d" % (232 + i)
+
+
+def VOFF(i):
+    return "v%d" % (236 + i)
+
+
+MROW = ["v240", "v241"]
+MCHK = "v242"
+M16 = "v243"
+
+
+def MCELL(rb):
+    return "v%d" % (244 + rb)
+
+
+def CLIM(rb):
+    return "v%d" % (247 + rb)
+
+
+def KVROW(i):
+    return "a%d" % (208 + i)
+
+
+GP4 = "v175"
+
+
+class Gen:
+    def __init__(self, ml):
+        self.ml = ml            # 0: implicit causal rule; 1 or 2: mask copies per lane per tile
+        self.lines = []
+
+    def e(self, s):
+        # labels carry the asm instance's unique number (%=): the three mask
+        # modes are three asm statements in one object file
+        if s.startswith("s_branch ") or s.startswith("s_cbranch_"):
+            s += "_%="
+        self.lines.append(s)
+
+    def label(self, name):
+        self.lines.append(name + "_%=:")
+
+    @property
+    def pt(self):
+        return 2 * KV_PW + self.ml
+
+    def mask_stage(self, st):
+        return st * W * self.ml * 1024
+
+    # ---- copies of tile u (s85) into stage sd ----
+    def dma(self, st):
+        sd = (st + 3) % NS
+        e = self.e
+        e("s_add_u32 s85, s80, 3")
+        e("s_min_u32 s85, s85, s81")
+        e("s_lshl_b32 s92, s85, 5")
+        e("s_add_u32 s83, s92, 32")
+        e("s_cmp_le_u32 s83, %[L]")
+        e("s_cbranch_scc0 .Lwpdma%d" % st)
+        e("s_lshl_b32 s83, s85, 14")
+        e("s_add_u32 s86, %[kb0], s83")
+        e("s_addc_u32 s87, %[kb1], 0")
+        e("s_add_u32 s88, %[vb0], s83")
+        e("s_addc_u32 s89, %[vb1], 0")
+        for i in range(KV_PW):
+            e("s_add_u32 m0, %%[m0k], %d" % (sd * KVB + i * 1024))
+            e("global_load_lds_dwordx4 %s, s[86:87]" % KOFF(i))
+        for i in range(KV_PW):
+            e("s_add_u32 m0, %%[m0k], %d" % (NS * KVB + sd * KVB + i * 1024))
+            e("global_load_lds_dwordx4 %s, s[88:89]" % VOFF(i))
+        if self.ml:
+            e("s_lshl_b32 s83, s92, 2")
+            e("s_add_u32 s90, %[mb0], s83")
+            e("s_addc_u32 s91, %[mb1], 0")
+            for j in range(self.ml):
+                e("s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(sd) + j * 1024))
+                e("global_load_lds_dwordx4 %s, s[90:91]" % MROW[j])
+        e("s_branch .Lwdmad%d" % st)
+        # a tile that ends past kv_seq_len: per-lane rows clamped to L - 1
+        self.label(".Lwpdma%d" % st)
+        for part, off, base in ((0, KOFF, ("%[kb0]", "%[kb1]")), (1, VOFF, ("%[vb0]", "%[vb1]"))):
+            e("s_mov_b32 s98, %s" % base[0])
+            e("s_mov_b32 s99, %s" % base[1])
+            for i in range(KV_PW):
+                e("v_accvgpr_read_b32 %s, %s" % (T(5), KVROW(i)))
+                e("v_lshlrev_b32 %s, 9, %s" % (T(0), T(5)))
+                e("v_sub_u32 %s, %s, %s" % (T(0), off(i), T(0)))
+                e("v_add_u32 %s, s92, %s" % (T(1), T(5)))
+                e("v_min_u32 %s, s95, %s" % (T(1), T(1)))
+                e("v_lshl_add_u32 %s, %s, 9, %s" % (T(1), T(1), T(0)))
+                e("s_add_u32 m0, %%[m0k], %d" % (part * NS * KVB + sd * KVB + i * 1024))
+                e("global_load_lds_dwordx4 %s, s[98:99]" % T(1))
+        if self.ml:
+            # key of the lane's chunk, clamped to the chunk that holds L - 1
+            e("v_lshrrev_b32 %s, 2, %s" % (T(2), M16))
+            e("v_add_u32 %s, s92, %s" % (T(2), T(2)))
+            e("v_cmp_gt_u32_e32 vcc, %%[L], %s" % T(2))
+            e("v_mov_b32 %s, %%[lclamp]" % T(3))
+            e("v_cndmask_b32_e32 %s, %s, %s, vcc" % (T(2), T(3), T(2)))
+            e("v_lshlrev_b32 %s, 2, %s" % (T(2), T(2)))
+            e("s_mov_b32 s98, %[mb0]")
+            e("s_mov_b32 s99, %[mb1]")
+            for j in range(self.ml):
+                e("v_sub_u32 %s, %s, %s" % (T(4), MROW[j], M16))
+                e("v_add_u32 %s, %s, %s" % (T(4), T(4), T(2)))
+                e("s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(sd) + j * 1024))
+                e("global_load_lds_dwordx4 %s, s[98:99]" % T(4))
+        self.label(".Lwdmad%d" % st)
+
+    # ---- is tile tn (s93, first key s94, stage stn) free of per-cell work? ----
+    def class_check(self, tag, stn, slow_label):
+        e = self.e
+        e("s_add_u32 s83, s94, 32")
+        e("s_cmp_le_u32 s83, %[L]")
+        e("s_cbranch_scc0 %s" % slow_label)
+        if self.ml == 0:
+            e("s_cmp_lt_u32 s94, %[keylo]")
+            e("s_cbranch_scc1 %s" % slow_label)
+            e("s_add_u32 s83, s94, 31")
+            e("s_cmp_gt_i32 s83, %[climit]")
+            e("s_cbranch_scc1 %s" % slow_label)
+        else:
+            e("ds_read_b128 v[200:203], %s offset:%d" % (MCHK, self.mask_stage(stn)))
+            if self.ml == 2:
+                e("ds_read_b128 v[204:207], %s offset:%d" % (MCHK, self.mask_stage(stn) + 1024))
+            e("s_waitcnt lgkmcnt(0)")
+            e("v_or3_b32 %s, %s, %s, %s" % (T(0), T(0), T(1), T(2)))
+            e("v_or_b32_e32 %s, %s, %s" % (T(0), T(0), T(3)))
+            if self.ml == 2:
+                e("v_or3_b32 %s, %s, %s, %s" % (T(0), T(0), T(4), T(5)))
+                e("v_or3_b32 %s, %s, %s, %s" % (T(0), T(0), T(6), T(7)))
+            e("v_cmp_ne_u32_e32 vcc, 0, %s" % T(0))
+            e("s_cmp_eq_u64 vcc, 0")
+            e("s_cbranch_scc0 %s" % slow_label)
+
+    # ---- per-cell accumulator inputs of tile tn into score buffer nxt ----
+    def slow_class(self, stn, nxt):
+        e = self.e
+        e("v_add_u32 %s, s94, %s" % (T(0), GP4))        # key of the lane's first cell (kb 0, j 0)
+        if self.ml:
+            e("v_sub_u32 %s, %%[L], %s" % (T(1), T(0)))  # keys left in range from there (signed)
+            for rb in range(RB):
+                for kb in range(2):
+                    e("ds_read_b128 %s, %s offset:%d" % (B(2 * rb + kb), MCELL(rb), self.mask_stage(stn) + 64 * kb))
+            e("s_waitcnt lgkmcnt(0)")
+            e("s_mov_b32 s83, 0x%08x" % F32_NEG65504)
+            e("s_mov_b32 s84, 0x%08x" % F32_LOG2E)
+            e("v_mov_b32_e32 %s, 0x%08x" % (T(3), F32_NEGINF))
+            for rb in range(RB):
+                for kb in range(2):
+                    xb = 176 + 4 * ((2 * rb + kb) % RING)
+                    for j in range(4):
+                        x = "v%d" % (xb + j)
+                        e("v_cmp_gt_i32_e64 s[98:99], %s, %d" % (T(1), 16 * kb + j))
+                        e("v_cmp_lt_f32_e32 vcc, s83, %s" % x)
+                        e("s_and_b64 vcc, vcc, s[98:99]")
+                        e("v_fma_f32 %s, %s, s84, %s" % (T(2), x, C(rb, 0)))
+                        e("v_cndmask_b32_e32 %s, %s, %s, vcc" % (S(nxt, rb, kb, j), T(3), T(2)))
+        else:
+            e("v_mov_b32_e32 %s, 0x%08x" % (T(3), F32_NEGINF))
+            for rb in range(RB):
+                for kb in range(2):
+                    for j in range(4):
+                        e("v_add_u32 %s, %d, %s" % (T(2), 16 * kb + j, T(0)))
+                        e("v_cmp_ge_i32_e64 s[98:99], %s, %s" % (CLIM(rb), T(2)))
+                        e("v_cmp_gt_u32_e32 vcc, %%[L], %s" % T(2))
+                        e("s_and_b64 vcc, vcc, s[98:99]")
+                        e("v_cmp_le_u32_e64 s[98:99], %%[keylo], %s" % T(2))
+                        e("s_and_b64 vcc, vcc, s[98:99]")
+                        e("v_cndmask_b32_e32 %s, %s, %s, vcc" % (S(nxt, rb, kb, j), T(3), C(rb, 0)))
+        e("s_nop 1")
+
+    # ---- the fast softmax of buffer cur: exp2, fp16 packing, range check ----
+    def softmax_list(self, cur):
+        L = []
+        for rb in range(RB):
+            for kb in range(2):
+                for j in range(4):
+                    L.append("v_exp_f32_e32 %s, %s" % (T(4 * kb + j), S(cur, rb, kb, j)))
+            for k in range(4):
+                L.append("v_cvt_pk_f16_f32 %s, %s, %s" % (P(rb, k), T(2 * k), T(2 * k + 1)))
+        words = [P(rb, k) for rb in range(RB) for k in range(4)]
+        L.append("v_pk_max_u16 %s, %s, %s" % (T(0), words[0], words[1]))
+        for w in words[2:]:
+            L.append("v_pk_max_u16 %s, %s, %s" % (T(0), T(0), w))
+        L.append("v_and_b32_e32 %s, 0xffff, %s" % (T(1), T(0)))
+        L.append("v_lshrrev_b32_e32 %s, 16, %s" % (T(2), T(0)))
+        L.append("v_max_u32_e32 %s, %s, %s" % (T(1), T(1), T(2)))
+        L.append("v_cmp_lt_u32_e32 vcc, 0x%x, %s" % (LAZY_F16, T(1)))
+        return L
+
+    # ---- scores of tile tn (stage stn) into buffer nxt, with the softmax of cur interleaved ----
+    def region_a(self, stn, nxt, cur, fast_c, with_softmax):
+        e = self.e
+        valu = self.softmax_list(cur) if with_softmax else []
+        per = [[] for _ in range(16)]
+        # spread the VALU work over the 16 operand steps
+        for idx, ins in enumerate(valu):
+            per[min(15, idx * 16 // max(1, len(valu)))].append(ins)
+        nread = 16
+
+        def kread(i):
+            ds, kb = i >> 1, i & 1
+            e("ds_read_b128 %s, %s offset:%d" % (B(i), OFFK(ds), stn * KVB + kb * 16 * D * 2))
+        for i in range(AHEAD):
+            kread(i)
+        for i in range(16):
+            ds, kb = i >> 1, i & 1
+            issued = min(nread, i + AHEAD)
+            e("s_waitcnt lgkmcnt(%d)" % (issued - i - 1))
+            for rb in range(RB):
+                if ds == 0:
+                    src_c = C(rb) if fast_c else S(nxt, rb, kb)
+                else:
+                    src_c = S(nxt, rb, kb)
+                e("v_mfma_f32_16x16x32_f16 %s, %s, %s, %s" % (S(nxt, rb, kb), B(i), Q(rb, ds), src_c))
+            if i + AHEAD < nread:
+                kread(i + AHEAD)
+            for ins in per[i]:
+                e(ins)
+
+    # ---- O^T += V^T P^T and the row sums, stage st ----
+    def region_b(self, st):
+        e = self.e
+        e("s_nop 1")
+        for rb in range(RB):
+            e("v_mfma_f32_16x16x32_f16 %s, %s, %s, %s" % (RS(rb), ONES, P(rb), RS(rb)))
+
+        def vread(db):
+            e("ds_read_b64_tr_b16 %s, %s offset:%d" % (Blo(db), OFFV(db), st * KVB))
+            e("ds_read_b64_tr_b16 %s, %s offset:%d" % (Bhi(db), OFFV(db), st * KVB + 16 * D * 2))
+        for db in range(AHEAD):
+            vread(db)
+        for db in range(DB):
+            issued = 2 * min(DB, db + AHEAD)
+            e("s_waitcnt lgkmcnt(%d)" % (issued - 2 * (db + 1)))
+            for rb in range(RB):
+                e("v_mfma_f32_16x16x32_f16 %s, %s, %s, %s" % (O(rb, db), B(db), P(rb), O(rb, db)))
+            if db + AHEAD < DB:
+                vread(db + AHEAD)
+
+    def step(self, st):
+        e = self.e
+        cur, nxt, stn = st & 1, (st & 1) ^ 1, (st + 1) % NS
+        self.label(".Lwstep%d" % st)
+        e("s_waitcnt vmcnt(%d)" % self.pt)
+        e("s_barrier")
+        self.dma(st)
+        e("s_add_u32 s93, s80, 1")
+        e("s_min_u32 s93, s93, s81")
+        e("s_lshl_b32 s94, s93, 5")
+        self.class_check(st, stn, ".Lwcslow%d" % st)
+        self.region_a(stn, nxt, cur, True, True)
+        e("s_branch .Lwadone%d" % st)
+        self.label(".Lwcslow%d" % st)
+        self.slow_class(stn, nxt)
+        self.region_a(stn, nxt, cur, False, True)
+        self.label(".Lwadone%d" % st)
+        # fast path kept iff no p above the bound, every M finite and none stale
+        e("s_cmp_eq_u64 vcc, 0")
+        e("s_cselect_b32 s83, s82, 0")
+        e("s_cmp_eq_u32 s83, 1")
+        e("s_cbranch_scc1 .Lwpv%d" % st)
+        e("s_getpc_b64 s[96:97]")
+        e("s_add_u32 s96, s96, 12")
+        e("s_addc_u32 s97, s97, 0")
+        e("s_branch .Lwsslow%d" % cur)
+        self.label(".Lwpv%d" % st)
+        self.region_b(st)
+        e("s_add_u32 s80, s80, 1")
+        e("s_cmp_ge_u32 s80, %[t1]")
+        e("s_cbranch_scc1 .Lwend")
+
+    # ---- slow softmax of buffer cur (called; returns through s[96:97]) ----
+    def slow_softmax(self, cur):
+        e = self.e
+        self.label(".Lwsslow%d" % cur)
+        ref, tmx, tmp, mnew, msub = "v176", "v177", "v178", "v180", "v181"
+        e("s_mov_b64 s[86:87], 0")          # rows whose M moves
+        e("s_mov_b64 s[88:89], 0")          # rows that need O rescaled
+        e("s_mov_b64 s[90:91], exec")       # rows whose M is finite
+        e("s_mov_b32 s84, 0x%08x" % F32_NEGINF)
+        for rb in range(RB):
+            alpha = "v%d" % (184 + rb)
+            # the reference the scores were issued with
+            e("s_bitcmp1_b32 s82, 1")
+            e("s_cbranch_scc1 .Lwref%d_%d" % (cur, rb))
+            e("v_sub_f32_e32 %s, 0, %s" % (ref, C(rb, 0)))
+            e("s_branch .Lwrefd%d_%d" % (cur, rb))
+            self.label(".Lwref%d_%d" % (cur, rb))
+            e("v_accvgpr_read_b32 %s, %s" % (ref, AREF(rb)))
+            self.label(".Lwrefd%d_%d" % (cur, rb))
+            for kb in range(2):
+                for j in range(4):
+                    e("v_add_f32_e32 %s, %s, %s" % (T(4 * kb + j), S(cur, rb, kb, j), ref))
+            e("v_max3_f32 %s, %s, %s, %s" % (tmx, T(0), T(1), T(2)))
+            e("v_max3_f32 %s, %s, %s, %s" % (tmx, tmx, T(3), T(4)))
+            e("v_max3_f32 %s, %s, %s, %s" % (tmx, tmx, T(5), T(6)))
+            e("v_max_f32_e32 %s, %s, %s" % (tmx, tmx, T(7)))
+            for sw in ("v_permlane16_swap_b32_e32", "v_permlane32_swap_b32_e32"):
+                e("v_mov_b32_e32 %s, %s" % (tmp, tmx))
+                e("s_nop 1")
+                e("%s %s, %s" % (sw, tmx, tmp))
+                e("v_max_f32_e32 %s, %s, %s" % (tmx, tmx, tmp))
+            # mnew = tmax if tmax > M + LAZY (also when M is -inf and tmax is not), else M
+            e("v_add_f32_e32 %s, 0x%08x, %s" % (tmp, F32_LAZY, M2(rb)))
+            e("v_cmp_gt_f32_e32 vcc, %s, %s" % (tmx, tmp))
+            e("v_cndmask_b32_e32 %s, %s, %s, vcc" % (mnew, M2(rb), tmx))
+            # alpha = 2^(M - mnew) where a finite M moves, else 1 (O and the
+            # row sum are still zero while M is -inf)
+            e("v_sub_f32_e32 %s, %s, %s" % (alpha, M2(rb), mnew))
+            e("v_exp_f32_e32 %s, %s" % (alpha, alpha))
+            e("v_cmp_neq_f32_e32 vcc, %s, %s" % (mnew, M2(rb)))
+            e("s_or_b64 s[86:87], s[86:87], vcc")
+            e("v_cmp_neq_f32_e64 s[98:99], s84, %s" % M2(rb))
+            e("s_and_b64 vcc, vcc, s[98:99]")
+            e("v_cndmask_b32_e32 %s, 1.0, %s, vcc" % (alpha, alpha))
+            e("v_cmp_neq_f32_e32 vcc, 1.0, %s" % alpha)
+            e("s_or_b64 s[88:89], s[88:89], vcc")
+            # the scores of the next tile were issued with the current -C
+            e("v_sub_f32_e32 %s, 0, %s" % (tmp, C(rb, 0)))
+            e("v_accvgpr_write_b32 %s, %s" % (AREF(rb), tmp))
+            e("v_mov_b32_e32 %s, %s" % (M2(rb), mnew))
+            # reference used from now on: mnew, or 0 while it is -inf
+            e("v_cmp_neq_f32_e32 vcc, 0x%08x, %s" % (F32_NEGINF, mnew))
+            e("s_and_b64 s[90:91], s[90:91], vcc")
+            e("v_cndmask_b32_e32 %s, 0, %s, vcc" % (msub, mnew))
+            e("v_sub_f32_e32 %s, 0, %s" % (C(rb, 0), msub))
+            for j in range(1, 4):
+                e("v_mov_b32_e32 %s, %s" % (C(rb, j), C(rb, 0)))
+            for k in range(8):
+                e("v_sub_f32_e32 %s, %s, %s" % (T(k), T(k), msub))
+            for k in range(8):
+                e("v_exp_f32_e32 %s, %s" % (T(k), T(k)))
+            e("s_nop 0")
+            for k in range(4):
+                e("v_cvt_pk_f16_f32 %s, %s, %s" % (P(rb, k), T(2 * k), T(2 * k + 1)))
+        # flags: bit 0 every M finite, bit 1 some M moved (pending scores stale)
+        e("s_cmp_eq_u64 s[90:91], exec")
+        e("s_cselect_b32 s82, 1, 0")
+        e("s_cmp_lg_u64 s[86:87], 0")
+        e("s_cselect_b32 s83, 2, 0")
+        e("s_or_b32 s82, s82, s83")
+        e("s_cmp_eq_u64 s[88:89], 0")
+        e("s_cbranch_scc1 .Lwsret%d" % cur)
+        e("s_getpc_b64 s[98:99]")
+        e("s_add_u32 s98, s98, 12")
+        e("s_addc_u32 s99, s99, 0")
+        e("s_branch .Lwrescale")
+        self.label(".Lwsret%d" % cur)
+        e("s_nop 1")
+        e("s_setpc_b64 s[96:97]")
+
+    # ---- O and the row sums times alpha (v184..v186), through ordinary registers ----
+    def rescale(self):
+        e = self.e
+        self.label(".Lwrescale")
+        e("s_nop 7")
+        regs = ["v188", "v189", "v190", "v191"]
+        blocks = [(rb, 64 * rb + 4 * db) for rb in range(RB) for db in range(DB)]
+        blocks += [(rb, 192 + 4 * rb) for rb in range(RB)]
+        for rb, a0 in blocks:
+            for j in range(4):
+                e("v_accvgpr_read_b32 %s, a%d" % (regs[j], a0 + j))
+            for j in range(4):
+                e("v_mul_f32_e32 %s, %s, v%d" % (regs[j], regs[j], 184 + rb))
+            for j in range(4):
+                e("v_accvgpr_write_b32 a%d, %s" % (a0 + j, regs[j]))
+        e("s_nop 3")
+        e("s_setpc_b64 s[98:99]")
+
+    def build(self):
+        e = self.e
+        e("s_mov_b32 s80, %[t0]")
+        e("s_sub_u32 s81, %[t1], 1")
+        e("s_sub_u32 s95, %[L], 1")
+        e("s_mov_b32 s82, 0")
+        e("s_barrier")
+        # scores of the first tile (stage 0, buffer 0)
+        e("s_mov_b32 s93, s80")
+        e("s_lshl_b32 s94, s93, 5")
+        self.class_check("p", 0, ".Lwpcslow")
+        self.region_a(0, 0, 1, True, False)
+        e("s_branch .Lwpdone")
+        self.label(".Lwpcslow")
+        self.slow_class(0, 0)
+        self.region_a(0, 0, 1, False, False)
+        self.label(".Lwpdone")
+        for st in range(NS):
+            self.step(st)
+        e("s_branch .Lwstep0")
+        for cur in range(2):
+            self.slow_softmax(cur)
+        self.rescale()
+        self.label(".Lwend")
+        e("s_waitcnt vmcnt(0)")
+        e("s_nop 7")
+        e("s_nop 7")
+        return self.lines
+
+
+def main():
+    here = os.path.dirname(os.path.abspath(__file__))
+    out = ["// Generated by gen_wide_loop.py -- do not edit.  The tile loop of the",
+           "// wide fp16 forward, one string per mask mode (0: implicit causal rule,",
+           "// 1 / 2: mask cells copied per tile, 16 bytes per lane per copy).",
+           "#pragma once"]
+    for ml in (0, 1, 2):
+        lines = Gen(ml).build()
+        out.append("#define TA_WIDE_LOOP_ML%d \\" % ml)
+        for ln in lines:
+            out.append('  "%s\\n" \\' % ln.replace('"', '\\"'))
+        out.append('  ""')
+    with open(os.path.join(here, "fwd_wide_loop.inc"), "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
+if __name__ == "__main__":
+    main()
