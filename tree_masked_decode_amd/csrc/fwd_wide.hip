@@ -230,7 +230,8 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
   split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
   t0 += tile_lo;
   t1 += tile_lo;
-  auto issue_tile = [&](uint32_t u, uint32_t st) __attribute__((always_inline)) {
+  // K (with the mask cells) and V of tile u into stage st of their rings
+  auto issue_k = [&](uint32_t u, uint32_t st) __attribute__((always_inline)) {
     const uint32_t key0 = u * BN;
     const uint32_t lk = lds0 + st * KVB + wave * S::KV_PW * 1024u;
 #pragma unroll
@@ -239,13 +240,6 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
       const uint32_t key = min(key0 + row, L - 1u);
       dma_b128(reinterpret_cast<const char *>(K + (size_t)key * D) + (k_off[i] - 2u * row * D),
                lk + i * 1024u);
-    }
-#pragma unroll
-    for (int i = 0; i < S::KV_PW; ++i) {
-      const uint32_t row = __float_as_uint(KVROW[i]);
-      const uint32_t key = min(key0 + row, L - 1u);
-      dma_b128(reinterpret_cast<const char *>(V + (size_t)key * D) + (v_off[i] - 2u * row * D),
-               lk + NS * KVB + i * 1024u);
     }
     if constexpr (!IMPLICIT) {
       uint32_t key = key0 + 4u * (lane % 8u);
@@ -256,6 +250,17 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
                  mask_lds + st * (W * S::MB) + j * 1024u);
     }
   };
+  auto issue_v = [&](uint32_t u, uint32_t st) __attribute__((always_inline)) {
+    const uint32_t key0 = u * BN;
+    const uint32_t lv = lds0 + NS * KVB + st * KVB + wave * S::KV_PW * 1024u;
+#pragma unroll
+    for (int i = 0; i < S::KV_PW; ++i) {
+      const uint32_t row = __float_as_uint(KVROW[i]);
+      const uint32_t key = min(key0 + row, L - 1u);
+      dma_b128(reinterpret_cast<const char *>(V + (size_t)key * D) + (v_off[i] - 2u * row * D),
+               lv + i * 1024u);
+    }
+  };
 
   floatx32 O0 = {}, O1 = {}, O2 = {}, O3 = {}, O4 = {}, O5 = {};
   floatx16 R = {}, CM = {};
@@ -264,9 +269,12 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
   CM[15] = __uint_as_float(4u * gp);
   if (t0 < t1) {
     const uint32_t tl = t1 - 1u;
-    issue_tile(t0, 0);
-    issue_tile(min(t0 + 1u, tl), 1);
-    issue_tile(min(t0 + 2u, tl), 2);
+    // the loop expects K (and mask cells) of tiles t0 .. t0+3 and V of
+    // tiles t0 .. t0+2 in their stages (tiles past the split repeat its last)
+#pragma unroll
+    for (uint32_t i = 0; i < 4u; ++i) issue_k(min(t0 + i, tl), i);
+#pragma unroll
+    for (uint32_t i = 0; i < 3u; ++i) issue_v(min(t0 + i, tl), i);
     // Q'^T fragments (Q * scale * log2(e), fp16): row n of each block,
     // d = 32 ds + 8 gp + 0..7
     floatx32 Qv[RB];

@@ -59,7 +59,8 @@ KVB = BN * D * 2          # bytes of one K (or V) tile
 DS, DB = D // 32, D // 16
 KV_PW = KVB // 1024 // W  # 1 KB copies per wavefront per K (or V) tile
 RING = 6
-AHEAD = 4
+AHEAD = 5                 # operand reads in flight ahead of the matrix instructions (ring slot of
+                          # step i+5 is that of step i-1, already consumed)
 LAZY = 15.0               # the reference max moves when a tile's row max exceeds it by > 15 (base 2)
 LAZY_F16 = 0x7800         # 2^15 as fp16 bits: a fast-path p above it needs a new reference
 
@@ -189,50 +190,50 @@ class Gen:
     def mask_stage(self, st):
         return st * W * self.ml * 1024
 
-    # ---- copies of tile u (s85) into stage sd ----
-    def dma(self, st):
-        sd = (st + 3) % NS
+    # ---- copies: K (+ mask cells) of tile t+4 into K stage st, V of tile
+    # t+3 into V stage st+3.  K and V rings are separate, so each part is
+    # fetched three steps before the step that reads it: tile t+4's K is read
+    # at step t+3 (scores of the next tile) and tile t+3's V at step t+3. ----
+    def dma_part(self, st, part, ahead, stage):
         e = self.e
-        e("s_add_u32 s85, s80, 3")
+        tag = "%d_%d" % (st, part)
+        e("s_add_u32 s85, s80, %d" % ahead)
         e("s_min_u32 s85, s85, s81")
         e("s_lshl_b32 s92, s85, 5")
         e("s_add_u32 s83, s92, 32")
         e("s_cmp_le_u32 s83, %[L]")
-        e("s_cbranch_scc0 .Lwpdma%d" % st)
+        e("s_cbranch_scc0 .Lwpdma%s" % tag)
+        off = KOFF if part == 0 else VOFF
+        base = ("%[kb0]", "%[kb1]") if part == 0 else ("%[vb0]", "%[vb1]")
+        lbase = part * NS * KVB + stage * KVB
         e("s_lshl_b32 s83, s85, 14")
-        e("s_add_u32 s86, %[kb0], s83")
-        e("s_addc_u32 s87, %[kb1], 0")
-        e("s_add_u32 s88, %[vb0], s83")
-        e("s_addc_u32 s89, %[vb1], 0")
+        e("s_add_u32 s86, %s, s83" % base[0])
+        e("s_addc_u32 s87, %s, 0" % base[1])
         for i in range(KV_PW):
-            e("s_add_u32 m0, %%[m0k], %d" % (sd * KVB + i * 1024))
-            e("global_load_lds_dwordx4 %s, s[86:87]" % KOFF(i))
-        for i in range(KV_PW):
-            e("s_add_u32 m0, %%[m0k], %d" % (NS * KVB + sd * KVB + i * 1024))
-            e("global_load_lds_dwordx4 %s, s[88:89]" % VOFF(i))
-        if self.ml:
+            e("s_add_u32 m0, %%[m0k], %d" % (lbase + i * 1024))
+            e("global_load_lds_dwordx4 %s, s[86:87]" % off(i))
+        if part == 0 and self.ml:
             e("s_lshl_b32 s83, s92, 2")
             e("s_add_u32 s90, %[mb0], s83")
             e("s_addc_u32 s91, %[mb1], 0")
             for j in range(self.ml):
-                e("s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(sd) + j * 1024))
+                e("s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(stage) + j * 1024))
                 e("global_load_lds_dwordx4 %s, s[90:91]" % MROW[j])
-        e("s_branch .Lwdmad%d" % st)
+        e("s_branch .Lwdmad%s" % tag)
         # a tile that ends past kv_seq_len: per-lane rows clamped to L - 1
-        self.label(".Lwpdma%d" % st)
-        for part, off, base in ((0, KOFF, ("%[kb0]", "%[kb1]")), (1, VOFF, ("%[vb0]", "%[vb1]"))):
-            e("s_mov_b32 s98, %s" % base[0])
-            e("s_mov_b32 s99, %s" % base[1])
-            for i in range(KV_PW):
-                e("v_accvgpr_read_b32 %s, %s" % (T(5), KVROW(i)))
-                e("v_lshlrev_b32 %s, 9, %s" % (T(0), T(5)))
-                e("v_sub_u32 %s, %s, %s" % (T(0), off(i), T(0)))
-                e("v_add_u32 %s, s92, %s" % (T(1), T(5)))
-                e("v_min_u32 %s, s95, %s" % (T(1), T(1)))
-                e("v_lshl_add_u32 %s, %s, 9, %s" % (T(1), T(1), T(0)))
-                e("s_add_u32 m0, %%[m0k], %d" % (part * NS * KVB + sd * KVB + i * 1024))
-                e("global_load_lds_dwordx4 %s, s[98:99]" % T(1))
-        if self.ml:
+        self.label(".Lwpdma%s" % tag)
+        e("s_mov_b32 s98, %s" % base[0])
+        e("s_mov_b32 s99, %s" % base[1])
+        for i in range(KV_PW):
+            e("v_accvgpr_read_b32 %s, %s" % (T(5), KVROW(i)))
+            e("v_lshlrev_b32 %s, 9, %s" % (T(0), T(5)))
+            e("v_sub_u32 %s, %s, %s" % (T(0), off(i), T(0)))
+            e("v_add_u32 %s, s92, %s" % (T(1), T(5)))
+            e("v_min_u32 %s, s95, %s" % (T(1), T(1)))
+            e("v_lshl_add_u32 %s, %s, 9, %s" % (T(1), T(1), T(0)))
+            e("s_add_u32 m0, %%[m0k], %d" % (lbase + i * 1024))
+            e("global_load_lds_dwordx4 %s, s[98:99]" % T(1))
+        if part == 0 and self.ml:
             # key of the lane's chunk, clamped to the chunk that holds L - 1
             e("v_lshrrev_b32 %s, 2, %s" % (T(2), M16))
             e("v_add_u32 %s, s92, %s" % (T(2), T(2)))
@@ -245,15 +246,32 @@ class Gen:
             for j in range(self.ml):
                 e("v_sub_u32 %s, %s, %s" % (T(4), MROW[j], M16))
                 e("v_add_u32 %s, %s, %s" % (T(4), T(4), T(2)))
-                e("s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(sd) + j * 1024))
+                e("s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(stage) + j * 1024))
                 e("global_load_lds_dwordx4 %s, s[98:99]" % T(4))
-        self.label(".Lwdmad%d" % st)
+        self.label(".Lwdmad%s" % tag)
 
-    # ---- is tile tn (s93, first key s94, stage stn) free of per-cell work? ----
-    def class_check(self, tag, stn, slow_label):
+    def dma(self, st):
+        self.dma_part(st, 0, 4, st)
+        self.dma_part(st, 1, 3, (st + 3) % NS)
+
+    def class_read(self, stn):
+        """Issue the mask-word reads of tile tn's class check (into the idle
+        operand ring) so that their latency hides behind the copy issue."""
+        if self.ml:
+            self.e("ds_read_b128 v[176:179], %s offset:%d" % (MCHK, self.mask_stage(stn)))
+            if self.ml == 2:
+                self.e("ds_read_b128 v[180:183], %s offset:%d" % (MCHK, self.mask_stage(stn) + 1024))
+
+    def class_check(self, tag, stn, slow_label, read_done=False):
         e = self.e
+        if self.ml and not read_done:
+            self.class_read(stn)
         e("s_add_u32 s83, s94, 32")
         e("s_cmp_le_u32 s83, %[L]")
+        if self.ml:
+            # (the mask words may still be arriving in the ring that the
+            # per-cell path reuses)
+            e("s_waitcnt lgkmcnt(0)")
         e("s_cbranch_scc0 %s" % slow_label)
         if self.ml == 0:
             e("s_cmp_lt_u32 s94, %[keylo]")
@@ -262,15 +280,12 @@ class Gen:
             e("s_cmp_gt_i32 s83, %[climit]")
             e("s_cbranch_scc1 %s" % slow_label)
         else:
-            e("ds_read_b128 v[200:203], %s offset:%d" % (MCHK, self.mask_stage(stn)))
-            if self.ml == 2:
-                e("ds_read_b128 v[204:207], %s offset:%d" % (MCHK, self.mask_stage(stn) + 1024))
             e("s_waitcnt lgkmcnt(0)")
-            e("v_or3_b32 %s, %s, %s, %s" % (T(0), T(0), T(1), T(2)))
-            e("v_or_b32_e32 %s, %s, %s" % (T(0), T(0), T(3)))
+            e("v_or3_b32 %s, v176, v177, v178" % T(0))
+            e("v_or_b32_e32 %s, %s, v179" % (T(0), T(0)))
             if self.ml == 2:
-                e("v_or3_b32 %s, %s, %s, %s" % (T(0), T(0), T(4), T(5)))
-                e("v_or3_b32 %s, %s, %s, %s" % (T(0), T(0), T(6), T(7)))
+                e("v_or3_b32 %s, %s, v180, v181" % (T(0), T(0)))
+                e("v_or3_b32 %s, %s, v182, v183" % (T(0), T(0)))
             e("v_cmp_ne_u32_e32 vcc, 0, %s" % T(0))
             e("s_cmp_eq_u64 vcc, 0")
             e("s_cbranch_scc0 %s" % slow_label)
@@ -325,16 +340,17 @@ class Gen:
         L.append("v_pk_max_u16 %s, %s, %s" % (T(0), words[0], words[1]))
         for w in words[2:]:
             L.append("v_pk_max_u16 %s, %s, %s" % (T(0), T(0), w))
-        L.append("v_and_b32_e32 %s, 0xffff, %s" % (T(1), T(0)))
-        L.append("v_lshrrev_b32_e32 %s, 16, %s" % (T(2), T(0)))
-        L.append("v_max_u32_e32 %s, %s, %s" % (T(1), T(1), T(2)))
-        L.append("v_cmp_lt_u32_e32 vcc, 0x%x, %s" % (LAZY_F16, T(1)))
+        # both halves saturate to 0 unless above the bound
+        L.append("v_pk_sub_u16 %s, %s, s84 clamp" % (T(1), T(0)))
+        L.append("v_cmp_ne_u32_e32 vcc, 0, %s" % T(1))
         return L
 
     # ---- scores of tile tn (stage stn) into buffer nxt, with the softmax of cur interleaved ----
     def region_a(self, stn, nxt, cur, fast_c, with_softmax):
         e = self.e
         valu = self.softmax_list(cur) if with_softmax else []
+        if with_softmax:
+            e("s_mov_b32 s84, 0x%04x%04x" % (LAZY_F16, LAZY_F16))
         per = [[] for _ in range(16)]
         # spread the VALU work over the 16 operand steps
         for idx, ins in enumerate(valu):
@@ -348,8 +364,10 @@ class Gen:
             kread(i)
         for i in range(16):
             ds, kb = i >> 1, i & 1
-            issued = min(nread, i + AHEAD)
-            e("s_waitcnt lgkmcnt(%d)" % (issued - i - 1))
+            # one wait covers two steps (steps i and i+1)
+            if i % 2 == 0:
+                issued = min(nread, i + AHEAD)
+                e("s_waitcnt lgkmcnt(%d)" % max(0, issued - min(nread, i + 2)))
             for rb in range(RB):
                 if ds == 0:
                     src_c = C(rb) if fast_c else S(nxt, rb, kb)
@@ -374,8 +392,10 @@ class Gen:
         for db in range(AHEAD):
             vread(db)
         for db in range(DB):
-            issued = 2 * min(DB, db + AHEAD)
-            e("s_waitcnt lgkmcnt(%d)" % (issued - 2 * (db + 1)))
+            # one wait covers two d-blocks
+            if db % 2 == 0:
+                issued = 2 * min(DB, db + AHEAD)
+                e("s_waitcnt lgkmcnt(%d)" % max(0, issued - 2 * min(DB, db + 2)))
             for rb in range(RB):
                 e("v_mfma_f32_16x16x32_f16 %s, %s, %s, %s" % (O(rb, db), B(db), P(rb), O(rb, db)))
             if db + AHEAD < DB:
@@ -385,13 +405,14 @@ class Gen:
         e = self.e
         cur, nxt, stn = st & 1, (st & 1) ^ 1, (st + 1) % NS
         self.label(".Lwstep%d" % st)
-        e("s_waitcnt vmcnt(%d)" % self.pt)
+        e("s_waitcnt vmcnt(%d)" % (2 * self.pt))
         e("s_barrier")
+        self.class_read(stn)
         self.dma(st)
         e("s_add_u32 s93, s80, 1")
         e("s_min_u32 s93, s93, s81")
         e("s_lshl_b32 s94, s93, 5")
-        self.class_check(st, stn, ".Lwcslow%d" % st)
+        self.class_check(st, stn, ".Lwcslow%d" % st, read_done=True)
         self.region_a(stn, nxt, cur, True, True)
         e("s_branch .Lwadone%d" % st)
         self.label(".Lwcslow%d" % st)
