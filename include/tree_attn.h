@@ -247,8 +247,8 @@ TA_API int tree_attn_reduce(const float *partials, size_t partials_bytes, void *
  * Scales, biases and the mask are used in fp32; out is rounded to nearest
  * even.  bits is 4 or 8; dim is 64, 96, 128, 256 or 512 ([FQS]
  * instantiations); group_size is 32, 64 or 128 and divides dim (so 32 at
- * dim 96); kv_capacity >= kv_seq_len > 0 (and even when group_size == dim
- * with a 2-byte T); mask_stride >= kv_seq_len when a mask is given.  With
+ * dim 96); kv_capacity >= kv_seq_len > 0 (and even when dim/group_size is
+ * odd with a 2-byte T: group_size == dim, or dim 96); mask_stride >= kv_seq_len when a mask is given.  With
  * nwg > 1 follow with tree_attn_reduce(out_dtype = q_dtype, nrows =
  * batch*n_q_heads*q_l, head_dim = dim).
  */

@@ -240,6 +240,9 @@ def qf(lib, **kw):
     (dict(vb=None), L.TA_EINVAL, "NULL"),
     (dict(mhs=1 << 62), L.TA_EOVERFLOW, "overflow"),
     (dict(dim=64, G=64, cap=16385), L.TA_EUNSUPPORTED, "even"),
+    # three fp16 scales per token: an odd capacity misaligns every other head
+    (dict(dim=96, G=32, cap=16385), L.TA_EUNSUPPORTED, "even"),
+    (dict(dim=96, G=32, cap=16385, q_dtype=2), L.TA_EUNSUPPORTED, "even"),
 ])
 def test_quant_validation(lib, kw, code, word):
     assert qf(lib, **kw) == code

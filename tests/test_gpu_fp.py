@@ -263,6 +263,20 @@ def test_edges(ta, kvd):
                                   scale=c["scale"]), tol, "additive")
 
 
+@pytest.mark.parametrize("H,D,nwg", [(2, 128, 1), (2, 512, 2), (8, 256, 1), (8, 256, 3)])
+def test_implicit_rows_before_the_cache(ta, H, D, nwg):
+    # q_l > kv_seq_len under the implicit rule: nodes 0..35 have their last
+    # visible key before key 0, see nothing and must come out as zeros (the
+    # fast-tile bound of the first workgroup is negative there)
+    note("implicit q_l=100 L=64 H=%d D=%d nwg=%d" % (H, D, nwg))
+    c = small_case(21, H, 1, D, 64, 100, "f16", tree="chain")
+    got = run_verify(ta, c, None, nwg=nwg)
+    ref = oracle.attention(c["q"], c["k"], c["v"], None, n_kv_heads=1, kv_seq_len=64,
+                           scale=c["scale"])
+    assert np.all(got[:36] == 0.0)
+    assert_close(got, ref, TOL["f16"], "q_l=100 L=64")
+
+
 @pytest.mark.parametrize("kvd", ["f32", "f16"])
 def test_dead_band_inside_one_split(ta, kvd):
     # live tiles, then whole tiles masked for every row (skipped), then live

@@ -405,10 +405,14 @@ static int quant_forward(
     return fail(TA_EINVAL, "%s: nwg must be in [1, %u], got %u", fn, kMaxNwg, nwg);
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(TA_EINVAL, "%s: scale must be finite", fn);
-  // Scales/biases are read four tokens at a time as 32-bit words.
-  if (esz == 2 && group_size == dim && (kv_capacity & 1u))
+  // Scales/biases are read four tokens at a time as 32-bit words: a head's
+  // block of them (kv_capacity tokens of (dim/group_size) T each) must start
+  // on a 4-byte boundary, which an odd capacity breaks whenever one token's
+  // scales fill an odd number of 2-byte elements.
+  if ((dim / group_size) * esz % 4 != 0 && (kv_capacity & 1u))
     return fail(TA_EUNSUPPORTED,
-                "%s: kv_capacity must be even when group_size == dim (2-byte scales)", fn);
+                "%s: kv_capacity must be even when dim/group_size is odd with 2-byte scales",
+                fn);
   if (!kv_bytes) return fail(TA_EINVAL, "%s: kv_bytes must not be NULL", fn);
   if (!q || !k_packed || !k_scales || !k_biases || !v_packed || !v_scales || !v_biases)
     return fail(TA_EINVAL, "%s: q and the six K/V buffers must not be NULL", fn);

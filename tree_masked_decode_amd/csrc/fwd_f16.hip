@@ -460,7 +460,10 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   // implicit mask, keys every row of the workgroup attends: there the mask
   // needs no per-cell key checks.
   uint32_t fast = L / BN;
-  if (IMPLICIT) fast = min(fast, (uint32_t)(((int64_t)L - a.q_l + node0 + 1) / BN));
+  // (rows whose last visible key lies before key 0, q_l > kv_seq_len, see
+  // nothing: the bound clamps at 0 instead of wrapping)
+  if (IMPLICIT)
+    fast = min(fast, (uint32_t)(max<int64_t>(0, (int64_t)L - a.q_l + node0 + 1) / BN));
   // a window start inside the first tile: that split checks every cell
   if (IMPLICIT && a.key_lo % BN != 0 && t0 == tile_lo) fast = t0;
   fast = min(max(fast, t0), t1);
