@@ -35,7 +35,12 @@
  * - Device pointers must be 16-byte aligned (torch allocations are).
  * - Calls on one stream are ordered; calls sharing an output or partial
  *   buffer on different streams race and are the caller's to order.
- * - Thread-safe: the only library state is the per-thread error string.
+ * - Thread-safe: the library state is the per-thread error string and, for
+ *   tree_attn_forward_noalloc only, the device address of its static
+ *   scratch on each device (looked up once).
+ * - Only tree_attn_forward_noalloc uses memory the caller did not pass: a
+ *   static device buffer that every device the library runs on holds until
+ *   the process ends.
  */
 #ifndef TREE_ATTN_H
 #define TREE_ATTN_H
@@ -208,6 +213,41 @@ TA_API int tree_attn_decode(const float *q, size_t q_bytes, const void *k,
 TA_API int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
                      int out_dtype, size_t out_bytes, uint32_t nrows,
                      uint32_t head_dim, uint32_t nwg, void *stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * tree_attn_forward followed by tree_attn_reduce (out_dtype TA_F32) in one
+ * call, with the split partials kept in a static device buffer of
+ * TA_NOALLOC_SCRATCH_BYTES that the library owns instead of a caller
+ * buffer.  Arguments, layouts and rules are tree_attn_forward's, without
+ * partials/partials_bytes; `out` ([q_l, n_heads, head_dim] f32) is always
+ * written, for every nwg.  Results are identical, bit for bit, to
+ * tree_attn_forward + tree_attn_reduce with the same nwg.
+ *
+ * - nwg must satisfy tree_attn_partials_bytes(n_heads, head_dim, q_l, nwg)
+ *   <= TA_NOALLOC_SCRATCH_BYTES, else TA_ESIZE (nothing enqueued).  nwg == 1
+ *   uses no scratch.
+ * - No call allocates or frees memory.  The first call on a device looks up
+ *   the buffer's device address there (hipGetSymbolAddress; the stream's
+ *   device, the current device for the null stream) and keeps it; a failed
+ *   lookup returns TA_EHIP.
+ * - One buffer per GPU, shared by every call on that GPU: calls that can
+ *   overlap on one GPU (different streams, or host threads not ordered by
+ *   one stream) race and give wrong results.  Calls on one stream are safe.
+ *   The buffer keeps the last call's contents; nothing in it needs to start
+ *   at zero (every split writes all of its partial rows before the merge
+ *   reads them).
+ */
+#define TA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+TA_API int tree_attn_forward_noalloc(const float *q, size_t q_bytes, const void *k,
+                              const void *v, int kv_dtype, size_t kv_bytes,
+                              const float *mask, size_t mask_bytes, float *out,
+                              size_t out_bytes, uint32_t n_heads, uint32_t n_kv_heads,
+                              uint32_t head_dim, uint32_t kv_seq_len,
+                              uint32_t kv_capacity, uint32_t q_l, uint32_t mask_stride,
+                              float scale, uint32_t nwg, void *stream);
 
 /*
  * Attention over an affine-quantized K/V cache ([FQS] Layout, base and

@@ -131,6 +131,46 @@ def fwd(lib, **kw):
         p["q_l"], p["mask_stride"], p["scale"], p["nwg"], None)
 
 
+def fwd_noalloc(lib, **kw):
+    p = dict(q=FAKE, q_bytes=BIG, k=FAKE, v=FAKE, kv_dtype=1, kv_bytes=BIG,
+             mask=FAKE, mask_bytes=BIG, out=FAKE, out_bytes=BIG, n_heads=32,
+             n_kv_heads=4, head_dim=512, kv_seq_len=2048, kv_capacity=2048, q_l=64,
+             mask_stride=2048, scale=1.0, nwg=15)
+    p.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.tree_attn_forward_noalloc(
+        vp(p["q"]), p["q_bytes"], vp(p["k"]), vp(p["v"]), p["kv_dtype"],
+        p["kv_bytes"], vp(p["mask"]), p["mask_bytes"], vp(p["out"]), p["out_bytes"],
+        p["n_heads"], p["n_kv_heads"], p["head_dim"], p["kv_seq_len"],
+        p["kv_capacity"], p["q_l"], p["mask_stride"], p["scale"], p["nwg"], None)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,code,word", [
+    # 16 splits of 32 x 64 rows x (512 + 2) floats: 67.4 MB > 64 MiB
+    (dict(nwg=16), L.TA_ESIZE, "static scratch"),
+    (dict(nwg=65537), L.TA_EINVAL, "nwg"),
+    (dict(out=None), L.TA_EINVAL, "out"),
+    (dict(nwg=1, out_bytes=64 * 32 * 512 * 4 - 1), L.TA_ESIZE, "output"),
+    (dict(head_dim=64), L.TA_EUNSUPPORTED, "head_dim"),
+    (dict(kv_capacity=100), L.TA_EINVAL, "kv_capacity"),
+    (dict(mask_bytes=64 * 2048 * 4 - 1), L.TA_ESIZE, "mask"),
+])
+def test_noalloc_validation(lib, kw, code, word):
+    # every rule is checked on the host, before the scratch is looked up
+    assert fwd_noalloc(lib, **kw) == code
+    assert word in L.last_error()
+
+
+def test_noalloc_limit_matches_partials_bytes(lib):
+    import tree_masked_decode_amd as T
+    assert T.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert lib.tree_attn_partials_bytes(32, 512, 64, 15) <= T.NOALLOC_SCRATCH_BYTES
+    assert lib.tree_attn_partials_bytes(32, 512, 64, 16) > T.NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert re.search(r"#define TA_NOALLOC_SCRATCH_BYTES \(64ull << 20\)", text)
+
+
 FWD_CASES = [
     # reference unit tests
     (dict(mask_stride=50), L.TA_EINVAL, "mask_stride"),

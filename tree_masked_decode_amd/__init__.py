@@ -29,7 +29,7 @@ __all__ = [
     "MASKED", "ATTENDED", "TreeAttnError", "partials_bytes", "pick_nwg",
     "quant_pick_nwg", "tree_attn_forward", "tree_attn_reduce",
     "tree_attn_quant_forward", "tree_attn_quant_forward_ex", "build_tree_mask",
-    "tree_attn_decode", "verify", "decode", "quant_verify",
+    "tree_attn_decode", "tree_attn_forward_noalloc", "verify", "decode", "quant_verify",
 ]
 
 
@@ -145,6 +145,29 @@ def tree_attn_reduce(partials, out, *, nrows, head_dim, nwg, stream=None):
     rc = _api().tree_attn_reduce(_ptr(partials), _nbytes(partials), _ptr(out),
                                  out_dtype, _nbytes(out), nrows, head_dim, nwg,
                                  _stream(stream))
+    _check(rc)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def tree_attn_forward_noalloc(q, k, v, mask, *, kv_seq_len, scale, nwg, out,
+                              mask_stride=None, stream=None):
+    """Forward plus merge into ``out`` ([q_l, H, D] f32) with the split
+    partials in the library's static device buffer (no allocation in the
+    call).  Calls that overlap on one GPU race on that buffer."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (mask, "mask"), (out, "out")):
+        _dense(t, n)
+    H, q_l, D = q.shape
+    Hk, cap, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != k.dtype or Dk != D:
+        raise ValueError("k and v must share shape and dtype, head_dim must match q")
+    if mask is not None and mask_stride is None:
+        mask_stride = mask.shape[-1]
+    rc = _api().tree_attn_forward_noalloc(
+        _ptr(q), _nbytes(q), _ptr(k), _ptr(v), _kv_dtype(k), _nbytes(k),
+        _ptr(mask), _nbytes(mask), _ptr(out), _nbytes(out), H, Hk, D, kv_seq_len,
+        cap, q_l, mask_stride or 0, float(scale), nwg, _stream(stream))
     _check(rc)
 
 

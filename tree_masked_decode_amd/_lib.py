@@ -39,6 +39,7 @@ EXPORTS = (
     "tree_attn_forward",
     "tree_attn_decode",
     "tree_attn_reduce",
+    "tree_attn_forward_noalloc",
     "tree_attn_quant_forward",
     "tree_attn_quant_forward_ex",
     "build_tree_mask",
@@ -85,6 +86,9 @@ def load():
         lib.tree_attn_decode.restype = I
         lib.tree_attn_reduce.argtypes = [P, Z, P, I, Z, U, U, U, P]
         lib.tree_attn_reduce.restype = I
+        lib.tree_attn_forward_noalloc.argtypes = [P, Z, P, P, I, Z, P, Z, P, Z,
+                                                  U, U, U, U, U, U, U, F, U, P]
+        lib.tree_attn_forward_noalloc.restype = I
         lib.tree_attn_quant_forward.argtypes = [
             P, I, Z, P, P, P, P, P, P, ctypes.POINTER(Z), P, Z, P, Z,
             ctypes.c_uint64, U, P, Z, P, Z, U, U, U, U, U, U, U, U, U, F, U, P]

@@ -11,6 +11,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/tree_attn.h"
@@ -101,6 +102,54 @@ uint32_t pick_splits(uint32_t heads, uint32_t row_tiles, uint32_t n_tiles, uint3
 
 }  // namespace
 
+// Split partials of tree_attn_forward_noalloc: one buffer per GPU, part of
+// this file's device code object (so it exists on every device the library
+// runs on, for the life of the process).  Host code never uses this name for
+// the memory: on the host it only names a stand-in.  The device address comes
+// from the runtime, once per device (static_scratch).
+constexpr uint64_t kStaticScratchBytes = TA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<float *> g_scratch_dev[kMaxDevices];  // zero-initialised (static storage)
+
+// Device address of `scratch` on the device of stream `s` (the current device
+// for the null stream), looked up on the first call for that device with the
+// device current.  nullptr (and the error string set) on failure.
+float *static_scratch(const char *fn, hipStream_t s) {
+  int dev = -1;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(TA_EHIP, "%s: cannot find the stream's device: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(TA_EHIP, "%s: device ordinal %d beyond the %d the library tracks", fn, dev,
+         kMaxDevices);
+    return nullptr;
+  }
+  float *p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  int cur = -1;
+  e = hipGetDevice(&cur);
+  if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+  void *addr = nullptr;
+  hipError_t el = e == hipSuccess ? hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) : e;
+  if (e == hipSuccess && cur != dev) e = hipSetDevice(cur);
+  if (el != hipSuccess || e != hipSuccess || addr == nullptr) {
+    fail(TA_EHIP, "%s: cannot find the static scratch on device %d: %s", fn, dev,
+         hipGetErrorString(el != hipSuccess ? el : e));
+    return nullptr;
+  }
+  // (two threads racing here both store the same address)
+  g_scratch_dev[dev].store(static_cast<float *>(addr), std::memory_order_release);
+  return static_cast<float *>(addr);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *tree_attn_last_error(void) { return g_err.c_str(); }
@@ -157,7 +206,7 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
                       uint32_t n_heads, uint32_t n_kv_heads, uint32_t head_dim,
                       uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
                       uint32_t mask_stride, uint32_t window_start, float scale,
-                      uint32_t nwg, void *stream) {
+                      uint32_t nwg, void *stream, bool static_partials = false) {
   if (window_start >= kv_seq_len && kv_seq_len > 0)
     return fail(TA_EINVAL, "%s: window_start (%u) must be < kv_seq_len (%u)", fn,
                 window_start, kv_seq_len);
@@ -189,7 +238,7 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
   // --- pointers ---
   if (!q || !k || !v) return fail(TA_EINVAL, "%s: q, k and v must not be NULL", fn);
   if (nwg == 1 && !out) return fail(TA_EINVAL, "%s: out must not be NULL when nwg == 1", fn);
-  if (nwg > 1 && !partials)
+  if (nwg > 1 && !partials && !static_partials)
     return fail(TA_EINVAL, "%s: partials must not be NULL when nwg > 1", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) ||
       (out && !aligned16(out)) || (partials && !aligned16(partials)) ||
@@ -221,7 +270,12 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
   if (nwg == 1 && out_bytes < req_out)
     return fail(TA_ESIZE, "%s: output buffer too small: have %zu bytes, need >= %llu", fn,
                 out_bytes, (unsigned long long)req_out);
-  if (nwg > 1 && partials_bytes < req_part)
+  if (static_partials && req_part > kStaticScratchBytes)
+    return fail(TA_ESIZE,
+                "%s: the partials of %u splits need %llu bytes, more than the %llu bytes of "
+                "the static scratch: use fewer splits",
+                fn, nwg, (unsigned long long)req_part, (unsigned long long)kStaticScratchBytes);
+  if (!static_partials && nwg > 1 && partials_bytes < req_part)
     return fail(TA_ESIZE, "%s: partials buffer too small: have %zu bytes, need >= %llu",
                 fn, partials_bytes, (unsigned long long)req_part);
   // row count per kv head and the grid must fit the kernels' 32-bit indices
@@ -260,13 +314,17 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
   if (blocks > 0x7fffffffull)
     return fail(TA_EUNSUPPORTED, "%s: grid too large (n_kv_heads*nwg*row tiles)", fn);
   a.units = (uint32_t)units;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (static_partials && nwg > 1) {
+    partials = static_scratch(fn, s);
+    if (!partials) return TA_EHIP;
+  }
   if (nwg > 1) {
     a.part_o = partials;
     a.part_sm = partials + (size_t)nwg * n_heads * q_l * head_dim;
   } else {
     a.part_o = a.part_sm = nullptr;
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = f16 ? ta::launch_forward_f16(a, head_dim, s)
                      : ta::launch_forward_f32(a, head_dim, s);
   return hip_status(e, fn);
@@ -356,6 +414,35 @@ int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
   a.nwg = nwg;
   a.out_type = out_dtype == TA_F16 ? 1 : out_dtype == TA_BF16 ? 2 : 0;
   return hip_status(ta::launch_reduce(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int tree_attn_forward_noalloc(const float *q, size_t q_bytes, const void *k, const void *v,
+                              int kv_dtype, size_t kv_bytes, const float *mask,
+                              size_t mask_bytes, float *out, size_t out_bytes, uint32_t n_heads,
+                              uint32_t n_kv_heads, uint32_t head_dim, uint32_t kv_seq_len,
+                              uint32_t kv_capacity, uint32_t q_l, uint32_t mask_stride,
+                              float scale, uint32_t nwg, void *stream) {
+  const char *fn = "tree_attn_forward_noalloc";
+  if (!out) return fail(TA_EINVAL, "%s: out must not be NULL", fn);
+  // the forward validates everything (the split results' size against the
+  // static scratch included), then looks the scratch up and launches
+  int rc = fp_forward(fn, q, q_bytes, k, v, kv_dtype, kv_bytes, mask, mask_bytes, nullptr, 0,
+                      out, out_bytes, n_heads, n_kv_heads, head_dim, kv_seq_len, kv_capacity,
+                      q_l, mask_stride, 0u, scale, nwg, stream, true);
+  if (rc != TA_OK || nwg == 1) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *part = static_scratch(fn, s);
+  if (!part) return TA_EHIP;
+  const uint32_t nrows = n_heads * q_l;  // < 2^31: checked by the forward
+  ta::ReduceArgs a;
+  a.part_o = part;
+  a.part_sm = part + (size_t)nwg * nrows * head_dim;
+  a.out = out;
+  a.nrows = nrows;
+  a.dim = head_dim;
+  a.nwg = nwg;
+  a.out_type = 0;
+  return hip_status(ta::launch_reduce(a, s), fn);
 }
 
 static int quant_forward(
