@@ -133,6 +133,15 @@ __device__ inline void wide_loop(floatx32 &O0, floatx32 &O1, floatx32 &O2, float
 #undef TA_WIDE_OPERANDS
 }
 
+// An empty asm that reads three register tuples: the computations that
+// produce them cannot sink below it.  (A device function: the host pass of a
+// kernel body cannot take "v" operands.)
+__device__ __attribute__((always_inline)) inline void hold_vgprs(const floatx32 &a,
+                                                                 const floatx32 &b,
+                                                                 const floatx32 &c) {
+  asm volatile("" ::"v"(a), "v"(b), "v"(c));
+}
+
 template <int D, int RB, int ML>
 __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
   static_assert(D == 256 && RB == 3, "the tile loop is generated for head dim 256, 48 rows per wavefront");
@@ -224,7 +233,7 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
   MISC2[0] = clim[1];
   MISC2[1] = clim[2];
 
-  // ---- split range; the first three tiles go out before Q is read ----
+  // ---- split range ----
   const uint32_t tile_lo = a.key_lo / BN;
   uint32_t t0, t1;
   split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
@@ -269,12 +278,15 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
   CM[15] = __uint_as_float(4u * gp);
   if (t0 < t1) {
     const uint32_t tl = t1 - 1u;
-    // the loop expects K (and mask cells) of tiles t0 .. t0+3 and V of
-    // tiles t0 .. t0+2 in their stages (tiles past the split repeat its last)
-#pragma unroll
-    for (uint32_t i = 0; i < 4u; ++i) issue_k(min(t0 + i, tl), i);
-#pragma unroll
-    for (uint32_t i = 0; i < 3u; ++i) issue_v(min(t0 + i, tl), i);
+    // The loop expects K (and mask cells) of tiles t0 .. t0+3 and V of
+    // tiles t0 .. t0+2 in their stages (tiles past the split repeat its
+    // last), tile t0's complete and the rest issued in the order
+    // K1 V1 K2 V2 K3: its per-step wait then covers each of them in time.
+    // Tile t0 goes out first; Q's loads follow it, and waiting for them
+    // (loads complete in order) completes tile t0 without holding up on the
+    // rest of the ring fill, which is issued after Q is in registers.
+    issue_k(t0, 0);
+    issue_v(t0, 0);
     // Q'^T fragments (Q * scale * log2(e), fp16): row n of each block,
     // d = 32 ds + 8 gp + 0..7
     floatx32 Qv[RB];
@@ -298,6 +310,14 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
         for (int k = 0; k < 4; ++k) Qv[rb][4 * ds + k] = w[k];
       }
     }
+    // (Q in registers before the rest of the fill goes out)
+    hold_vgprs(Qv[0], Qv[1], Qv[2]);
+#pragma unroll
+    for (uint32_t i = 1; i < 3u; ++i) {
+      issue_k(min(t0 + i, tl), i);
+      issue_v(min(t0 + i, tl), i);
+    }
+    issue_k(min(t0 + 3u, tl), 3u);
     const floatx4 ONES = __builtin_bit_cast(floatx4, u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u,
                                                              0x3C003C00u});
     wide_loop<ML>(O0, O1, O2, O3, O4, O5, R, CM, Qv[0], Qv[1], Qv[2], ONES, OFF, MISC, MISC2, KVROW,
