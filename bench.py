@@ -200,7 +200,10 @@ def cpu_baseline(name, c, alg, quant, gpu_out=None, tol=None, out_elem=None):
     ulp of the output type for fp16 / bf16 outputs."""
     import oracle
     import numpy as np
-    threads = max(1, min(16, os.cpu_count() or 1))
+    # the host's cores available to this process; the oracle runs on at most
+    # 16 of them (one GPU's share of the host)
+    host_cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, host_cores))
     if quant:
         nrows = c["q"].shape[0] * c["q"].shape[1]
         to_row = lambda r: (r // c["q_l"], r % c["q_l"])
@@ -261,15 +264,26 @@ def cpu_baseline(name, c, alg, quant, gpu_out=None, tol=None, out_elem=None):
         parity = {"rows": len(flat), "max_abs_err": float(diff.max()), "tol": float(tol),
                   "ok": bool(np.all(np.isfinite(got)) and np.all(diff <= bound))}
     us_call = dt * 1e6 * nrows / len(rows)
-    model = None
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
-                         None)
+            for l in f:
+                k, _, v = l.partition(":")
+                k = k.strip()
+                if k in ("model name", "cpu family", "model", "stepping") and k not in info:
+                    info[k] = v.strip()
+                if not l.strip() and info:
+                    break
     except OSError:
         pass
+    model = None
+    if info:
+        model = "%s (family %s, model %s, stepping %s)" % (
+            info.get("model name", "?"), info.get("cpu family", "?"), info.get("model", "?"),
+            info.get("stepping", "?"))
     return {"value": round(alg["bytes"] / (us_call * 1e-6) / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "cpu_model": model, "kind": "oracle",
+            "cores": threads, "threads": threads, "host_cores": host_cores,
+            "cpu_model": model, "kind": "oracle",
             "sample": "%d of %d output rows of %s (each row over all %d keys), "
                       "%.2f s wall; scaled to the whole call"
                       % (len(rows), nrows, name, c["kv_seq_len"], dt),
@@ -460,6 +474,21 @@ def main():
     torch.cuda.synchronize()
     warm_ms = (time.perf_counter() - tw0) * 1e3 / K
 
+    # ---- context: what HIP events read around a kernel that does nothing ----
+    # (a one-element fill on the same stream, recorded like the forward): the
+    # part of avg_launch_us that is launch and event overhead rather than the
+    # forward's own run, which matters for kernels of a few tens of µs
+    tiny = torch.empty(1, dtype=torch.float32, device="cuda")
+    floor = []
+    for i in range(40):
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        tiny.fill_(float(i))
+        b_ev.record(stream)
+        floor.append((a_ev, b_ev))
+    torch.cuda.synchronize()
+    event_floor_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in floor[5:])
+
     # ---- context: streaming bandwidth of this GPU ----
     # a device-to-device copy of 1 GiB (reads and writes every byte once),
     # reported as (read + write bytes) / time, best of five
@@ -533,6 +562,7 @@ def main():
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(args.workload, kind),
                      "kernel": "forward", "avg_launch_us": round(fwd_avg_ms * 1e3, 2),
+                     "event_floor_us": round(event_floor_us, 2),
                      "hbm_frac": round(hbm_frac, 4),
                      "mfma_frac": round(fwd_tfs / MFMA_F16_PEAK_TFS, 4)},
     }

@@ -175,11 +175,11 @@ FWD_CASES = [
     # reference unit tests
     (dict(mask_stride=50), L.TA_EINVAL, "mask_stride"),
     (dict(head_dim=64), L.TA_EUNSUPPORTED, "head_dim"),
-    (dict(q_l=0), L.TA_EINVAL, "q_seq_len"),
+    (dict(q_l=0), L.TA_EINVAL, "q_l"),
     # the rest of validate_params
     (dict(n_heads=0), L.TA_EINVAL, "n_heads"),
     (dict(n_kv_heads=0), L.TA_EINVAL, "n_kv_heads"),
-    (dict(n_heads=12, n_kv_heads=8), L.TA_EINVAL, "divisible"),
+    (dict(n_heads=12, n_kv_heads=8), L.TA_EINVAL, "multiple"),
     (dict(kv_seq_len=0), L.TA_EINVAL, "kv_seq_len"),
     (dict(kv_capacity=99), L.TA_EINVAL, "kv_capacity"),
     (dict(kv_dtype=7), L.TA_EUNSUPPORTED, "dtype"),
@@ -189,7 +189,7 @@ FWD_CASES = [
     (dict(q_bytes=16 * 256 * 4 - 1), L.TA_ESIZE, "q buffer"),
     (dict(kv_bytes=8 * 1024 * 256 * 2 - 1), L.TA_ESIZE, "k/v buffer"),
     (dict(kv_dtype=0, kv_bytes=8 * 1024 * 256 * 4 - 1), L.TA_ESIZE, "k/v buffer"),
-    (dict(mask_bytes=100 * 4 - 1), L.TA_ESIZE, "tree_mask"),
+    (dict(mask_bytes=100 * 4 - 1), L.TA_ESIZE, "tree mask"),
     (dict(nwg=1, out_bytes=16 * 256 * 4 - 1), L.TA_ESIZE, "output"),
     (dict(partials_bytes=16 * 4 * 258 * 4 - 1), L.TA_ESIZE, "partials"),
     # checked multiplication
@@ -269,7 +269,7 @@ def qf(lib, **kw):
     (dict(dim=64, G=128), L.TA_EINVAL, "divisible"),
     (dict(nq=30), L.TA_EINVAL, "divisible"),
     (dict(cap=100), L.TA_EINVAL, "kv_capacity"),
-    (dict(q_l=0), L.TA_EINVAL, "q_seq_len"),
+    (dict(q_l=0), L.TA_EINVAL, "q_l"),
     (dict(mask_stride=100), L.TA_EINVAL, "mask_stride"),
     (dict(kv_bytes=[BIG, BIG, BIG, 32 * 16384 * 16 * 4 - 1, BIG, BIG]), L.TA_ESIZE, "v_packed"),
     (dict(kv_bytes=[BIG, 32 * 16384 * 2 * 2 - 1, BIG, BIG, BIG, BIG]), L.TA_ESIZE, "k_scales"),

@@ -45,6 +45,10 @@ def test_baseline_parity_fp32():
     r = bench.cpu_baseline("tiny_chain", c, bench.fp_alg(c), False, gpu_out=got, tol=1e-4)
     assert r["parity"]["ok"] and r["parity"]["rows"] == 16
     assert r["cores"] >= 1 and r["kind"] == "oracle" and r["value"] > 0
+    # cores = the threads the oracle used; the host's own count beside it
+    import os
+    assert r["host_cores"] == len(os.sched_getaffinity(0))
+    assert r["threads"] == r["cores"] == min(16, r["host_cores"])
     bad = got.copy()
     bad[5, 17] += 2e-4
     r = bench.cpu_baseline("tiny_chain", c, bench.fp_alg(c), False, gpu_out=bad, tol=1e-4)
@@ -71,7 +75,7 @@ def test_baseline_sample_size(monkeypatch, target, expect_all):
     # rows, a huge one takes every row of the call
     c = inputs.fp_case("tiny_chain", q_l=4)
     monkeypatch.setattr(bench, "CPU_SAMPLE_S", target)
-    monkeypatch.setattr(bench.os, "cpu_count", lambda: 2)
+    monkeypatch.setattr(bench.os, "sched_getaffinity", lambda pid: {0, 1})
     r = bench.cpu_baseline("tiny_chain", c, bench.fp_alg(c), False)
     n = int(r["sample"].split(" of ")[0])
     total = c["n_heads"] * c["q_l"]

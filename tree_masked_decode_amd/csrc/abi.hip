@@ -60,6 +60,15 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
 
+// One argument rule: when `bad`, the call fails with `code` and the message
+// fmt (fn, a, b) -- two unsigned numbers at most, formatted only on failure.
+struct Rule {
+  bool bad;
+  int code;
+  const char *fmt;
+  unsigned long long a, b;
+};
+
 int hip_status(hipError_t e, const char *what) {
   if (e != hipSuccess)
     return fail(TA_EHIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
@@ -207,77 +216,74 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
                       uint32_t kv_seq_len, uint32_t kv_capacity, uint32_t q_l,
                       uint32_t mask_stride, uint32_t window_start, float scale,
                       uint32_t nwg, void *stream, bool static_partials = false) {
-  if (window_start >= kv_seq_len && kv_seq_len > 0)
-    return fail(TA_EINVAL, "%s: window_start (%u) must be < kv_seq_len (%u)", fn,
-                window_start, kv_seq_len);
-  // --- parameter contract ("ops/tree_attention.rs", validate_params) ---
-  if (head_dim != 128 && head_dim != 256 && head_dim != 512)
-    return fail(TA_EUNSUPPORTED, "%s: head_dim must be 128, 256, or 512, got %u",
-                fn, head_dim);
-  if (n_heads == 0 || n_kv_heads == 0)
-    return fail(TA_EINVAL, "%s: n_heads and n_kv_heads must be > 0", fn);
-  if (n_heads % n_kv_heads != 0)
-    return fail(TA_EINVAL, "%s: n_heads (%u) must be divisible by n_kv_heads (%u)",
-                fn, n_heads, n_kv_heads);
-  if (kv_seq_len == 0) return fail(TA_EINVAL, "%s: kv_seq_len must be > 0", fn);
-  if (kv_capacity < kv_seq_len)
-    return fail(TA_EINVAL, "%s: kv_capacity (%u) must be >= kv_seq_len (%u)", fn,
-                kv_capacity, kv_seq_len);
-  if (q_l == 0) return fail(TA_EINVAL, "%s: q_seq_len (q_l) must be > 0", fn);
-  if (mask != nullptr && mask_stride < kv_seq_len)
-    return fail(TA_EINVAL, "%s: mask_stride (%u) must be >= kv_seq_len (%u)", fn,
-                mask_stride, kv_seq_len);
-  if (kv_dtype != TA_F32 && kv_dtype != TA_F16)
-    return fail(TA_EUNSUPPORTED, "%s: k/v dtype must be TA_F32 or TA_F16, got %d",
-                fn, kv_dtype);
-  if (nwg == 0 || nwg > kMaxNwg)
-    return fail(TA_EINVAL, "%s: nwg must be in [1, %u], got %u", fn, kMaxNwg, nwg);
-  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
-    return fail(TA_EINVAL, "%s: scale must be finite", fn);
+  // Checked in table order; the first rule that fails names the problem
+  // and nothing is launched.  The contract (head dims, GQA divisibility,
+  // capacity, mask stride, byte sizes with checked products) is the one
+  // "ops/tree_attention.rs" states in validate_params and validate_buffers.
+  const bool f16 = kv_dtype == TA_F16;
+  const Rule args[] = {
+      {!q || !k || !v, TA_EINVAL, "%s: a NULL pointer among q, k, v", 0, 0},
+      {nwg == 1 && !out, TA_EINVAL, "%s: one split writes the result: out is NULL", 0, 0},
+      {nwg > 1 && !partials && !static_partials, TA_EINVAL,
+       "%s: %llu splits write partial results: partials is NULL", nwg, 0},
+      {kv_dtype != TA_F32 && kv_dtype != TA_F16, TA_EUNSUPPORTED,
+       "%s: unknown k/v dtype code %lld (TA_F32 or TA_F16)", (unsigned long long)(int64_t)kv_dtype,
+       0},
+      {head_dim != 128 && head_dim != 256 && head_dim != 512, TA_EUNSUPPORTED,
+       "%s: head_dim %llu not built (128, 256 and 512 are)", head_dim, 0},
+      {n_heads == 0, TA_EINVAL, "%s: n_heads is 0", 0, 0},
+      {n_kv_heads == 0, TA_EINVAL, "%s: n_kv_heads is 0", 0, 0},
+      {n_kv_heads != 0 && n_heads % n_kv_heads != 0, TA_EINVAL,
+       "%s: n_heads %llu is not a multiple of n_kv_heads %llu", n_heads, n_kv_heads},
+      {q_l == 0, TA_EINVAL, "%s: q_l (tree nodes) is 0", 0, 0},
+      {kv_seq_len == 0, TA_EINVAL, "%s: kv_seq_len is 0", 0, 0},
+      {kv_capacity < kv_seq_len, TA_EINVAL, "%s: kv_capacity %llu holds fewer than kv_seq_len %llu keys",
+       kv_capacity, kv_seq_len},
+      {mask != nullptr && mask_stride < kv_seq_len, TA_EINVAL,
+       "%s: mask_stride %llu is shorter than kv_seq_len %llu", mask_stride, kv_seq_len},
+      {kv_seq_len != 0 && window_start >= kv_seq_len, TA_EINVAL,
+       "%s: window_start %llu leaves no key (kv_seq_len %llu)", window_start, kv_seq_len},
+      {nwg == 0 || nwg > kMaxNwg, TA_EINVAL, "%s: nwg %llu outside [1, %llu]", nwg, kMaxNwg},
+      {!(scale == scale) || scale == INFINITY || scale == -INFINITY, TA_EINVAL,
+       "%s: scale is not a finite number", 0, 0},
+      {!aligned16(q) || !aligned16(k) || !aligned16(v) || (out && !aligned16(out)) ||
+           (partials && !aligned16(partials)) || (mask && ((uintptr_t)mask & 3u)),
+       TA_EINVAL, "%s: device pointers must be 16-byte aligned (the mask 4-byte aligned)", 0, 0},
+  };
+  for (const Rule &r : args)
+    if (r.bad) return fail(r.code, r.fmt, fn, r.a, r.b);
 
-  // --- pointers ---
-  if (!q || !k || !v) return fail(TA_EINVAL, "%s: q, k and v must not be NULL", fn);
-  if (nwg == 1 && !out) return fail(TA_EINVAL, "%s: out must not be NULL when nwg == 1", fn);
-  if (nwg > 1 && !partials && !static_partials)
-    return fail(TA_EINVAL, "%s: partials must not be NULL when nwg > 1", fn);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) ||
-      (out && !aligned16(out)) || (partials && !aligned16(partials)) ||
-      (mask && ((uintptr_t)mask & 3u)))
-    return fail(TA_EINVAL, "%s: device pointers must be 16-byte aligned (mask 4-byte)", fn);
-
-  // --- byte-length contract ("ops/tree_attention.rs", validate_buffers) ---
-  const uint64_t esz = kv_dtype == TA_F16 ? 2 : 4;
-  uint64_t req_q, req_kv, req_mask = 0, req_out, req_part = 0;
-  if (!mul4(n_heads, q_l, head_dim, 4, req_q))
-    return fail(TA_EOVERFLOW, "%s: n_heads*q_l*head_dim*4 overflows", fn);
-  if (!mul4(n_kv_heads, kv_capacity, head_dim, esz, req_kv))
-    return fail(TA_EOVERFLOW, "%s: n_kv_heads*kv_capacity*head_dim*esize overflows", fn);
-  if (mask && !mul3(q_l, mask_stride, 4, req_mask))
-    return fail(TA_EOVERFLOW, "%s: q_l*mask_stride*4 overflows", fn);
-  req_out = req_q;
-  bool of = false;
-  if (nwg > 1) req_part = partials_bytes_u64((uint64_t)n_heads * q_l, head_dim, nwg, of);
-  if (of) return fail(TA_EOVERFLOW, "%s: partials size overflows", fn);
-  if (q_bytes < req_q)
-    return fail(TA_ESIZE, "%s: q buffer too small: have %zu bytes, need >= %llu", fn,
-                q_bytes, (unsigned long long)req_q);
-  if (kv_bytes < req_kv)
-    return fail(TA_ESIZE, "%s: k/v buffer too small: have %zu bytes, need >= %llu", fn,
-                kv_bytes, (unsigned long long)req_kv);
-  if (mask && mask_bytes < req_mask)
-    return fail(TA_ESIZE, "%s: tree_mask buffer too small: have %zu bytes, need >= %llu",
-                fn, mask_bytes, (unsigned long long)req_mask);
-  if (nwg == 1 && out_bytes < req_out)
-    return fail(TA_ESIZE, "%s: output buffer too small: have %zu bytes, need >= %llu", fn,
-                out_bytes, (unsigned long long)req_out);
-  if (static_partials && req_part > kStaticScratchBytes)
-    return fail(TA_ESIZE,
-                "%s: the partials of %u splits need %llu bytes, more than the %llu bytes of "
-                "the static scratch: use fewer splits",
-                fn, nwg, (unsigned long long)req_part, (unsigned long long)kStaticScratchBytes);
-  if (!static_partials && nwg > 1 && partials_bytes < req_part)
-    return fail(TA_ESIZE, "%s: partials buffer too small: have %zu bytes, need >= %llu",
-                fn, partials_bytes, (unsigned long long)req_part);
+  // bytes each buffer must hold (64-bit products, overflow checked)
+  const uint64_t esz = f16 ? 2 : 4;
+  uint64_t req_q, req_kv, req_mask = 0, req_part = 0;
+  bool of = !mul4(n_heads, q_l, head_dim, 4, req_q) ||
+            !mul4(n_kv_heads, kv_capacity, head_dim, esz, req_kv) ||
+            (mask && !mul3(q_l, mask_stride, 4, req_mask));
+  if (nwg > 1 && !of) {
+    bool pof;
+    req_part = partials_bytes_u64((uint64_t)n_heads * q_l, head_dim, nwg, pof);
+    of = pof;
+  }
+  if (of) return fail(TA_EOVERFLOW, "%s: a buffer size overflows 64 bits", fn);
+  const uint64_t req_out = req_q;   // out holds as many floats as q
+  const Rule sizes[] = {
+      {q_bytes < req_q, TA_ESIZE, "%s: q buffer holds %llu bytes of the %llu needed", q_bytes,
+       req_q},
+      {kv_bytes < req_kv, TA_ESIZE, "%s: k/v buffers hold %llu bytes of the %llu needed", kv_bytes,
+       req_kv},
+      {mask && mask_bytes < req_mask, TA_ESIZE,
+       "%s: tree mask holds %llu bytes of the %llu needed", mask_bytes, req_mask},
+      {nwg == 1 && out_bytes < req_out, TA_ESIZE,
+       "%s: output buffer holds %llu bytes of the %llu needed", out_bytes, req_out},
+      {static_partials && req_part > kStaticScratchBytes, TA_ESIZE,
+       "%s: partials of these splits need %llu bytes, the static scratch holds %llu: use fewer "
+       "splits",
+       req_part, kStaticScratchBytes},
+      {!static_partials && nwg > 1 && partials_bytes < req_part, TA_ESIZE,
+       "%s: partials buffer holds %llu bytes of the %llu needed", partials_bytes, req_part},
+  };
+  for (const Rule &r : sizes)
+    if (r.bad) return fail(r.code, r.fmt, fn, r.a, r.b);
   // row count per kv head and the grid must fit the kernels' 32-bit indices
   uint64_t rows = (uint64_t)q_l * (n_heads / n_kv_heads);
   if ((uint64_t)n_heads * q_l > 0x7fffffffull || rows > 0x7fffffffull)
@@ -302,7 +308,6 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
   a.key_lo = mask ? 0u : window_start;
   a.qscale = scale * ta::kLog2e;
   a.scale = scale;
-  const bool f16 = kv_dtype == TA_F16;
   const bool mask_vec = mask == nullptr || ((uintptr_t)mask % 16u == 0 && mask_stride % 4u == 0);
   const uint32_t rpw = f16 ? ta::f16_rows_per_wg(head_dim, a.rows, a.group, mask == nullptr, mask_vec)
                            : ta::kF32RowsPerWG;
