@@ -70,6 +70,9 @@ def fp_alg(c):
     if ws is not None:   # decode: no mask buffer, keys from window_start on
         L -= ws
         mask = 0
+    mws = c.get("mask_window_start")
+    if mws:              # window as a mask: the mask is read whole, keys from mws on
+        L -= mws
     kv = 2 * Hk * L * D * esz
     qb = H * q_l * D * 4
     out = q_l * H * D * 4
@@ -228,6 +231,8 @@ def cpu_baseline(name, c, alg, quant, gpu_out=None, tol=None, out_elem=None):
         ws = c.get("window_start")
         mask = (None if ws is not None else
                 oracle.tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"]))
+        if c.get("mask_window_start"):
+            mask[:, :c["mask_window_start"]] = -65504.0
 
         def run(rows):
             return oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=c["n_kv_heads"],
@@ -356,6 +361,8 @@ def main():
         ws = c.get("window_start")
         base["mask"] = (None if ws is not None else
                         ta.build_tree_mask(c["parents"], c["kv_seq_len"], c["mask_stride"]))
+        if c.get("mask_window_start"):
+            base["mask"][:, :c["mask_window_start"]] = ta.MASKED
         H, Hk, D = c["n_heads"], c["n_kv_heads"], c["head_dim"]
         L, q_l = c["kv_seq_len"], c["q_l"]
         nwg = args.nwg or c.get("nwg") or ta.pick_nwg(H, Hk, D, L - (ws or 0), q_l,
@@ -364,7 +371,8 @@ def main():
         out_dtype = torch.float32
     copies = [base] + [{n: (None if t is None else t.clone()) for n, t in base.items()}
                        for _ in range(ncopies - 1)]
-    part = torch.empty(max(1, ta.partials_bytes(nrows, D, 1, nwg) // 4),
+    # (plus the tail tree_attn_forward may use for the live-key scan of a mask)
+    part = torch.empty(max(1, (ta.partials_bytes(nrows, D, 1, nwg) + ta.RANGE_BYTES) // 4),
                        dtype=torch.float32, device="cuda")
     out = torch.empty((nrows, D), dtype=out_dtype, device="cuda")
     stream = torch.cuda.current_stream()

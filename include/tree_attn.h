@@ -95,6 +95,23 @@ TA_API size_t tree_attn_partials_bytes(uint32_t n_heads, uint32_t head_dim,
                                 uint32_t q_l, uint32_t nwg);
 
 /*
+ * Optional tail of the partials buffer.  When tree_attn_forward gets an
+ * explicit mask, nwg > 1 and a partials buffer of at least
+ * tree_attn_partials_bytes(...) + TA_RANGE_BYTES bytes, it may first scan
+ * the mask for its first and last live key (one extra small kernel, results
+ * in those TA_RANGE_BYTES) and split only the tiles between them: a mask
+ * whose dead cells form a prefix or suffix of every row (a sliding window
+ * written as a mask) then costs neither K/V fetches nor idle splits ("tree_attention.metal",
+ * tree_attention_impl: a chunk whose cells are all masked is skipped).  It
+ * does so when the K/V bytes read are at least 64 MiB and at least 32 times
+ * the mask bytes; otherwise, or without the tail, every tile is split and
+ * fetched and a fully masked tile only skips its arithmetic.  The result
+ * meets the same contract either way; the tail's contents after the call
+ * are unspecified.
+ */
+#define TA_RANGE_BYTES 2048
+
+/*
  * A split count for tree_attn_forward that fills `num_cus` compute units
  * (0 means 256, MI355X), given the problem shape.  Pure function of its
  * arguments (no device query).  Always >= 1.  Callers pass the result as

@@ -486,6 +486,60 @@ def test_decode_window_in_first_tile_byte_identical_to_explicit(ta, kvd, D, ws, 
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+# ---- the live-key scan of an explicit mask (K/V >= 64 MiB, mask <= 1/32) ----
+RANGE = [
+    # seed, H, Hk, D, L, q_l, kv dtype, window start, nwg   (kernel)
+    (80, 8, 2, 512, 32768, 4, "f16", 24576, 8),     # fp16, one row block per wave
+    (81, 8, 2, 512, 32768, 4, "f16", 24577, 5),     # window inside a tile
+    (82, 24, 1, 256, 65536, 8, "f16", 49152, 16),   # wide (192 rows)
+    (83, 4, 2, 128, 65536, 2, "f32", 40960, 6),     # fp32
+]
+
+
+def _window_mask(L, q_l, ws):
+    i = np.arange(q_l)[:, None]
+    j = np.arange(L)[None, :]
+    return np.where((j >= ws) & (j <= L - q_l + i), 0.0, -65504.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("seed,H,Hk,D,L,q_l,kvd,ws,nwg", RANGE)
+def test_explicit_window_live_range(ta, seed, H, Hk, D, L, q_l, kvd, ws, nwg):
+    note("live range seed=%d H=%d Hk=%d D=%d L=%d q_l=%d %s ws=%d nwg=%d"
+         % (seed, H, Hk, D, L, q_l, kvd, ws, nwg))
+    c = small_case(seed, H, Hk, D, L, q_l, kvd, tree="chain", cap=L)
+    mask = _window_mask(L, q_l, ws)
+    got = run_verify(ta, c, mask, nwg=nwg)
+    ref = oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=Hk, kv_seq_len=L,
+                           scale=c["scale"])
+    assert_close(got, ref, TOL[kvd], "explicit window %d" % seed)
+    # a window that starts on a tile edge splits exactly the tiles the
+    # implicit rule's window start does: the same bytes as tree_attn_decode
+    bn = 32 if kvd == "f16" else (16 if D == 512 else 32)
+    if ws % bn == 0:
+        b = run_decode(ta, c, ws, nwg)
+        assert np.array_equal(got.view(np.uint32), b.view(np.uint32))
+
+
+def test_explicit_mask_live_range_edges(ta):
+    # fp16 d=512, 64 MiB of K/V: a dead band in the middle (kept, skipped per
+    # tile), every cell dead (zeros), one live key at the very end
+    H, Hk, D, L, q_l = 8, 1, 512, 32768, 3
+    c = small_case(84, H, Hk, D, L, q_l, "f16", tree="chain", cap=L)
+    for name, mask in (
+            ("band", np.where((np.arange(L) // 1000) % 7 == 3, -65504.0, 0.0)
+             .astype(np.float32)[None, :].repeat(q_l, 0)),
+            ("dead", np.full((q_l, L), -65504.0, np.float32)),
+            ("last key", np.where(np.arange(L) == L - 1, 0.0, -65504.0)
+             .astype(np.float32)[None, :].repeat(q_l, 0))):
+        note("live range edges: %s" % name)
+        got = run_verify(ta, c, mask, nwg=7)
+        ref = oracle.attention(c["q"], c["k"], c["v"], mask, n_kv_heads=Hk, kv_seq_len=L,
+                               scale=c["scale"])
+        assert_close(got, ref, TOL["f16"], name)
+        if name == "dead":
+            assert np.all(got == 0.0)
+
+
 def test_workload_decode_window_128k(ta):
     note("workload decode_window_128k (sampled rows)")
     c = inputs.fp_case("decode_window_128k")

@@ -149,6 +149,9 @@ def tree_attn_reduce(partials, out, *, nrows, head_dim, nwg, stream=None):
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
+# Tail after the partials that tree_attn_forward may use for the live-key
+# scan of an explicit mask (TA_RANGE_BYTES).
+RANGE_BYTES = 2048
 
 
 def tree_attn_forward_noalloc(q, k, v, mask, *, kv_seq_len, scale, nwg, out,
@@ -242,7 +245,8 @@ def verify(q, k, v, mask, *, kv_seq_len, scale, nwg=None, out=None,
     if out is None:
         out = torch.empty((q_l, H, D), dtype=torch.float32, device=q.device)
     if nwg > 1 and partials is None:
-        partials = torch.empty(partials_bytes(H, D, q_l, nwg) // 4,
+        # (with the live-key scan's tail: see RANGE_BYTES)
+        partials = torch.empty((partials_bytes(H, D, q_l, nwg) + RANGE_BYTES) // 4,
                                dtype=torch.float32, device=q.device)
     tree_attn_forward(q, k, v, mask, kv_seq_len=kv_seq_len, scale=scale,
                       nwg=nwg, out=out if nwg == 1 else None,

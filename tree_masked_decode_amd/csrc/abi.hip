@@ -78,6 +78,9 @@ int hip_status(hipError_t e, const char *what) {
 // Largest split count accepted (keeps every grid dimension and index in
 // range; far beyond any useful value).
 constexpr uint32_t kMaxNwg = 65536;
+// Key ranges of the live-key scan (8 bytes of result each).
+constexpr uint32_t kRangeChunks = TA_RANGE_BYTES / 8;
+static_assert(TA_RANGE_BYTES % 8 == 0, "range chunks");
 
 uint64_t partials_bytes_u64(uint64_t nrows, uint64_t dim, uint64_t nwg,
                             bool &overflow) {
@@ -329,6 +332,31 @@ static int fp_forward(const char *fn, const float *q, size_t q_bytes, const void
     a.part_sm = partials + (size_t)nwg * n_heads * q_l * head_dim;
   } else {
     a.part_o = a.part_sm = nullptr;
+  }
+  // Live-key scan of an explicit mask, into the TA_RANGE_BYTES after the
+  // partials when the buffer holds them.  Worth one more launch only where
+  // the K/V stream is long (>= 64 MiB) and the mask is small beside it
+  // (<= 1/32 of it): a dead prefix or suffix then costs neither fetches nor
+  // idle splits; shorter calls would mostly pay the extra launch.
+  a.range = nullptr;
+  a.range_chunks = 0;
+  const uint64_t spare =
+      static_partials ? kStaticScratchBytes - req_part : (uint64_t)partials_bytes - req_part;
+  const uint64_t kv_read = 2ull * n_kv_heads * kv_seq_len * head_dim * esz;
+  const uint64_t mask_read = (uint64_t)q_l * kv_seq_len * 4u;
+  if (mask && nwg > 1 && spare >= TA_RANGE_BYTES && kv_read >= (64ull << 20) &&
+      kv_read >= 32u * mask_read) {
+    ta::MaskRangeArgs r;
+    r.mask = mask;
+    r.out = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(partials) + req_part);
+    r.q_l = q_l;
+    r.kv_seq_len = kv_seq_len;
+    r.mask_stride = mask_stride;
+    r.chunks = kv_seq_len < kRangeChunks ? kv_seq_len : kRangeChunks;
+    hipError_t er = ta::launch_mask_range(r, s);
+    if (er != hipSuccess) return hip_status(er, fn);
+    a.range = r.out;
+    a.range_chunks = r.chunks;
   }
   hipError_t e = f16 ? ta::launch_forward_f16(a, head_dim, s)
                      : ta::launch_forward_f32(a, head_dim, s);

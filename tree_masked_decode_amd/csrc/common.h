@@ -43,6 +43,20 @@ struct FwdArgs {
   uint32_t key_lo;     // implicit rule only: first key any row sees (window start)
   float qscale;        // scale * log2(e): logits in base-2 units (fp32 kernel)
   float scale;         // softmax scale: logits in natural units (fp16 kernel)
+  // explicit mask only, or nullptr: (first, last) live key of each of
+  // range_chunks key ranges (mask_range_kernel); the splits then divide the
+  // tiles from the first live key's to the last live key's
+  const uint32_t *range;
+  uint32_t range_chunks;
+};
+
+// Live-key scan of an explicit mask: chunk c of `chunks` equal key ranges
+// gets (first, last) key whose cell is live (not <= -65504) in any row, or
+// (0xffffffff, 0) if none.
+struct MaskRangeArgs {
+  const float *mask;
+  uint32_t *out;        // [chunks][2]
+  uint32_t q_l, kv_seq_len, mask_stride, chunks;
 };
 
 // ---------------------------------------------------------------------------
@@ -100,6 +114,7 @@ hipError_t launch_quant_forward(const QuantArgs &a, uint32_t dim,
                                 uint32_t bits, uint32_t group, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 hipError_t launch_tree_mask(const MaskArgs &a, hipStream_t s);
+hipError_t launch_mask_range(const MaskRangeArgs &a, hipStream_t s);
 
 // Rows handled by one workgroup of each forward kernel (host-side shape
 // planning needs them).
@@ -170,6 +185,40 @@ __device__ inline void decode_block(uint32_t bid, uint32_t row_tiles,
   uint32_t slot = bid / kXcds;
   unit = (slot / row_tiles) * kXcds + xcd;
   rt = slot % row_tiles;
+}
+
+// The tiles [lo, hi) of `bn` keys that the splits divide: from tile_lo on
+// (the implicit rule's window start), narrowed to the live keys of an
+// explicit mask when its range scan is given (empty when no cell is live).
+// Every lane of the wavefront gets the same (wave-uniform) result.
+__device__ inline void split_tiles(const FwdArgs &a, uint32_t bn, uint32_t tile_lo,
+                                   uint32_t &lo, uint32_t &hi) {
+  lo = tile_lo;
+  hi = a.n_tiles;
+  if (a.range == nullptr) return;
+  const uint32_t lane = threadIdx.x % kWave;
+  uint32_t first = 0xffffffffu, last = 0u;
+  for (uint32_t c = lane; c < a.range_chunks; c += kWave) {
+    const u32x2 fl = reinterpret_cast<const u32x2 *>(a.range)[c];
+    if (fl[0] != 0xffffffffu) {
+      first = min(first, fl[0]);
+      last = max(last, fl[1]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    first = min(first, (uint32_t)__shfl_xor((int)first, o));
+    last = max(last, (uint32_t)__shfl_xor((int)last, o));
+  }
+  first = __builtin_amdgcn_readfirstlane(first);
+  last = __builtin_amdgcn_readfirstlane(last);
+  if (first == 0xffffffffu) {
+    lo = hi = tile_lo;
+    return;
+  }
+  lo = max(lo, first / bn);
+  hi = min(hi, last / bn + 1u);
+  if (hi < lo) hi = lo;
 }
 
 // Balanced contiguous split of n_tiles tiles into nwg ranges.

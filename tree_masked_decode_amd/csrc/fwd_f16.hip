@@ -426,9 +426,11 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   // implicit rule's window start; 0 otherwise)
   const uint32_t tile_lo = a.key_lo / BN;
   uint32_t t0, t1;
-  split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
-  t0 += tile_lo;
-  t1 += tile_lo;
+  uint32_t span_lo, span_hi;
+  split_tiles(a, BN, tile_lo, span_lo, span_hi);
+  split_range(span_hi - span_lo, a.nwg, split, t0, t1);
+  t0 += span_lo;
+  t1 += span_lo;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (t0 + s < t1) {

@@ -88,9 +88,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   // the splits cover the tiles from the one that holds key_lo
   const uint32_t tile_lo = a.key_lo / S::BN;
   uint32_t t0, t1;
-  split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
-  t0 += tile_lo;
-  t1 += tile_lo;
+  uint32_t span_lo, span_hi;
+  split_tiles(a, S::BN, tile_lo, span_lo, span_hi);
+  split_range(span_hi - span_lo, a.nwg, split, t0, t1);
+  t0 += span_lo;
+  t1 += span_lo;
   const size_t kvbase = (size_t)hk * a.kv_capacity * D;
   const float *K = static_cast<const float *>(a.k) + kvbase;
   const float *V = static_cast<const float *>(a.v) + kvbase;

@@ -236,9 +236,11 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
   // ---- split range ----
   const uint32_t tile_lo = a.key_lo / BN;
   uint32_t t0, t1;
-  split_range(a.n_tiles - tile_lo, a.nwg, split, t0, t1);
-  t0 += tile_lo;
-  t1 += tile_lo;
+  uint32_t span_lo, span_hi;
+  split_tiles(a, BN, tile_lo, span_lo, span_hi);
+  split_range(span_hi - span_lo, a.nwg, split, t0, t1);
+  t0 += span_lo;
+  t1 += span_lo;
   // K (with the mask cells) and V of tile u into stage st of their rings
   auto issue_k = [&](uint32_t u, uint32_t st) __attribute__((always_inline)) {
     const uint32_t key0 = u * BN;

@@ -1,5 +1,6 @@
-// kern_misc.hip -- the two small kernels of the path: explicit tree-mask
-// construction and the log-sum-exp merge of split partials.
+// kern_misc.hip -- the small kernels of the path: explicit tree-mask
+// construction, the live-key scan of an explicit mask, and the log-sum-exp
+// merge of split partials.
 #include "common.h"
 
 namespace ta {
@@ -194,6 +195,57 @@ hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s) {
   if (d4n > 32u) return launch_reduce_t<64, 1>(a, s);
   if (d4n > 16u) return launch_reduce_t<32, 1>(a, s);
   return launch_reduce_t<16, 1>(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Live-key scan of an explicit mask ("tree_attention.metal",
+// tree_attention_impl: a key chunk whose mask cells are all at or below
+// -65504 contributes nothing and is skipped).  Block c takes keys
+// [c L / chunks, (c + 1) L / chunks) of every row and writes the first and
+// last key with a live cell (a NaN cell counts as live, as the forward would
+// add it), or (0xffffffff, 0).  The forward then splits only the tiles
+// between the overall first and last live key, so a dead prefix or suffix
+// (a sliding window written as a mask) is neither fetched nor given splits.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mask_range_kernel(MaskRangeArgs a) {
+  __shared__ uint32_t s_first[4], s_last[4];
+  const uint32_t c = blockIdx.x;
+  const uint32_t k0 = (uint32_t)(((uint64_t)a.kv_seq_len * c) / a.chunks);
+  const uint32_t k1 = (uint32_t)(((uint64_t)a.kv_seq_len * (c + 1)) / a.chunks);
+  uint32_t first = 0xffffffffu, last = 0u;
+  for (uint32_t j = k0 + threadIdx.x; j < k1; j += 256u) {
+    bool live = false;
+    for (uint32_t i = 0; i < a.q_l && !live; ++i)
+      live = !(a.mask[(size_t)i * a.mask_stride + j] <= kMasked);
+    if (live) {
+      first = min(first, j);
+      last = max(last, j);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    first = min(first, (uint32_t)__shfl_xor((int)first, o));
+    last = max(last, (uint32_t)__shfl_xor((int)last, o));
+  }
+  const uint32_t wave = threadIdx.x / kWave;
+  if (threadIdx.x % kWave == 0) {
+    s_first[wave] = first;
+    s_last[wave] = last;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) {
+      first = min(first, s_first[w]);
+      last = max(last, s_last[w]);
+    }
+    if (first == 0xffffffffu) last = 0u;
+    reinterpret_cast<u32x2 *>(a.out)[c] = u32x2{first, last};
+  }
+}
+
+hipError_t launch_mask_range(const MaskRangeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(mask_range_kernel, dim3(a.chunks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace ta

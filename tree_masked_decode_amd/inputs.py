@@ -51,6 +51,12 @@ WORKLOADS = {
                                kv_seq_len=131072, kv_capacity=131072, q_l=8,
                                tree="chain", mask_stride=131072, kv_dtype="f16",
                                kv_std=1.0, nwg=None, window_start=98304),
+    # the same window written as an explicit mask (chain rule, keys below
+    # 98304 at -65504) and sent through the masked forward
+    "window_mask_128k": dict(n_heads=32, n_kv_heads=8, head_dim=512,
+                             kv_seq_len=131072, kv_capacity=131072, q_l=8,
+                             tree="chain", mask_stride=131072, kv_dtype="f16",
+                             kv_std=1.0, nwg=None, mask_window_start=98304),
 }
 
 QUANT_WORKLOADS = {
