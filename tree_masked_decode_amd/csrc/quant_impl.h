@@ -226,7 +226,12 @@ __device__ inline uint32_t step_word(int g, int sub, uint32_t gp) {
   return (uint32_t)(g * S::GW) + gp * S::RUN + (uint32_t)(sub * S::WPS);
 }
 
-template <int DIM, int BITS, int G, int MM, int ET>
+// SR (small R): the workgroup's live rows number at most 4 (one decode
+// query per head of a GQA group of 4, say).  The score epilogue and softmax
+// then run with each lane on one key of two rows (lane & 31, rows
+// 2 (lane >> 5) + 0..1) instead of on 8 keys of one MFMA row, 12 of whose 16
+// rows would be dead; scores and the p * scale operands pass through LDS.
+template <int DIM, int BITS, int G, int MM, int ET, int SR>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   using S = QShape<DIM, BITS, G, ET>;
   using ST = QStage<DIM, BITS, G, MM, ET>;
@@ -249,6 +254,22 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   const bool valid = gr < a.rows;
   const uint32_t node = valid ? gr / a.repeat : 0u;
   const uint32_t qidx = kv * a.repeat + (valid ? gr % a.repeat : 0u);
+  // SR roles: key kl of the tile, rows sr_row[0..1] = 2 rp + 0..1 (rt is 0)
+  const uint32_t kl = lane & 31u, rp = lane >> 5;
+  uint32_t sr_row[2];
+  bool sr_valid[2];
+  uint32_t sr_qidx[2];
+  int64_t sr_last[2];
+  size_t sr_mrow[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    sr_row[s2] = 2u * rp + (uint32_t)s2;
+    sr_valid[s2] = SR && sr_row[s2] < a.rows;
+    const uint32_t nd = sr_valid[s2] ? sr_row[s2] / a.repeat : 0u;
+    sr_qidx[s2] = kv * a.repeat + (sr_valid[s2] ? sr_row[s2] % a.repeat : 0u);
+    sr_last[s2] = (int64_t)a.kv_seq_len - (int64_t)a.q_l + (int64_t)nd;
+    sr_mrow[s2] = (size_t)sr_qidx[s2] * a.mask_head_stride + (size_t)nd * a.mask_stride;
+  }
 
   // ---- Q in the K operand's slot order; the attention scale is applied
   // to the fp32 dot products afterwards.  fp16 Q is used exactly; bf16 Q
@@ -314,6 +335,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     uint32_t vsb[2][2][S::SBW];   // V scales/biases: keys F(gp, 4h..4h+3)
     u32x4 vw[S::VCH];             // V words for the LDS transpose
     float m[2][4];                // mask cells (row n, keys 16kb+4gp+j)
+    // SR: scale and bias of the lane's key kl per group, and its mask cells
+    // of rows 2 rp + 0..1
+    float ksr[SR ? NG : 1], kbr[SR ? NG : 1], vsr[SR ? NG : 1], vbr[SR ? NG : 1];
+    float mr[2];
   };
   // ---- copies of tile t into stage (t - t0) % NS ----
   // Keys past kv_seq_len re-read row L - 1 (or the word that holds it), so
@@ -443,6 +468,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 #pragma unroll
         for (int r = 0; r < S::RUN; ++r)
           T.kw[kb][g][r] = Kl[kr * S::WPK + g * S::GW + gp * S::RUN + r];
+      if constexpr (SR) continue;
       // scales/biases of keys 16kb + 4gp + 0..3 (K side) and
       // 16h + 4gp + 0..3 (V side, the keys of B-operand half h)
       const uint32_t k4 = 16u * kb + 4u * gp;
@@ -473,6 +499,34 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
         T.m[kb][j] = mv;
       }
     }
+    if constexpr (SR) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        T.ksr[g] = elem_f32<ET>(SBl[0], kl * NG + g);
+        T.kbr[g] = elem_f32<ET>(SBl[1], kl * NG + g);
+        T.vsr[g] = elem_f32<ET>(SBl[2], kl * NG + g);
+        T.vbr[g] = elem_f32<ET>(SBl[3], kl * NG + g);
+      }
+      const uint32_t kk = key0 + kl;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bool in = sr_valid[s2] && kk < L && kk >= klo;
+        const uint32_t r = sr_row[s2];
+        float mv;
+        if (IMPLICIT) {
+          mv = (in && (int64_t)kk <= sr_last[s2]) ? 0.0f : kMasked;
+        } else if (MM == kMaskReg) {
+          mv = in ? elem_f32<ET>(a.mask, sr_mrow[s2] + kk) : kMasked;
+        } else if (MG::BOOL) {
+          mv = (in && reinterpret_cast<const uint32_t *>(Ml)[r * BN + kl] != 0u) ? 0.0f
+                                                                               : kMasked;
+        } else {
+          const float x = elem_f32<ET>(Ml, r * BN + kl);  // always in the stage
+          mv = in ? x : kMasked;
+        }
+        T.mr[s2] = mv;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < S::VCH; ++u) {
       const uint32_t c = lane + kThreads * u;
@@ -499,6 +553,18 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   // ---- online-softmax state of the lane's row ----
   float Mrow = -INFINITY, Srow = 0.0f;
   float pb[NG];                     // sum_t p_t * vbias_tg (lane's keys)
+  // SR state of rows sr_row[0..1]: reference max (the same in every lane of
+  // the half-wave), and this lane's shares of S and of the bias sums
+  float srM[2] = {-INFINITY, -INFINITY}, srS[2] = {0.0f, 0.0f};
+  float srB[2][SR ? NG : 1];
+  float sr_qs[2][SR ? NG : 1];      // Q's group sums of the lane's rows
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int g = 0; g < (SR ? NG : 1); ++g) srB[s2][g] = 0.0f;
+  float *sx = reinterpret_cast<float *>(lds + ST::LDS);                       // [NG][4][BN]
+  half_t *pw = reinterpret_cast<half_t *>(lds + ST::LDS + NG * 4 * BN * 4);  // [NG][4][BN]
+  half_t *pwl = pw + NG * 4 * BN;                                            // lo halves
 #pragma unroll
   for (int g = 0; g < NG; ++g) pb[g] = 0.0f;
   floatx4 oacc[DB];
@@ -508,6 +574,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     // the sink: a virtual key with raw logit sinks[h] and value zero
     Mrow = a.sinks[qidx % a.nq] * kLog2e;
     Srow = (gp == 0) ? 1.0f : 0.0f;
+  }
+  if (SR && a.sinks != nullptr && split == 0) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      if (sr_valid[s2]) {
+        srM[s2] = a.sinks[sr_qidx[s2] % a.nq] * kLog2e;
+        srS[s2] = (kl == 0u) ? 1.0f : 0.0f;
+      }
   }
 
   const uint32_t cmask = code_pair_mask<BITS>();
@@ -543,69 +617,148 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
                 kf, qfl[(g * S::SPG + sub) % (QLO ? STEPS : 1)], sacc[g][kb], 0, 0, 0);
         }
       }
-    float s[2][4];
-    float tmax = -INFINITY;
+    half8_t pf[NG], pl[NG];
+    if constexpr (SR) {
+      // ---- scores of the (at most 4) live rows, lane = (key kl, rows
+      // sr_row[0..1]) ----
+      if (n < 4u) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t *ksc = T.ksb[kb][0];
-      const uint32_t *kbi = T.ksb[kb][1];
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+          for (int kb = 0; kb < 2; ++kb)
+            *reinterpret_cast<floatx4 *>(&sx[(g * 4 + n) * BN + 16 * kb + 4 * gp]) = sacc[g][kb];
+      }
+      __builtin_amdgcn_wave_barrier();
+      float sc[2];
+      bool need = false;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
         float x = 0.0f;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          x = fmaf(elem_f32<ET>(ksc, j * NG + g), sacc[g][kb][j], x);
-          x = fmaf(elem_f32<ET>(kbi, j * NG + g), qsum[g], x);
+          x = fmaf(T.ksr[g], sx[(g * 4 + sr_row[s2]) * BN + kl], x);
+          x = fmaf(T.kbr[g], sr_qs[s2][g], x);
         }
-        const float mv = T.m[kb][j];
-        // an excluded cell adds -inf: the arithmetic above stays unconditional
+        const float mv = T.mr[s2];
         x = fmaf(x, a.qscale, (mv > kMasked) ? mv * kLog2e : -INFINITY);
-        s[kb][j] = x;
-        tmax = fmaxf(tmax, x);
+        sc[s2] = x;
+        need |= x > srM[s2] + kLazyQ;
       }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // Lazy rescale: the reference max M moves only when the tile's max
-    // exceeds it by more than kLazyQ (base 2); until then p <= 2^kLazyQ, held
-    // exactly by the fp32 sums and by the fp16 hi + lo P * scale pair, and
-    // O, S and M stay consistent: the same softmax.
-    const float m_new = (tmax > Mrow + kLazyQ) ? tmax : Mrow;
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(Mrow - m_use);
-    float p[8];
-    float psum = 0.0f;
+      // the reference max of a row moves only when one of its scores exceeds
+      // it by more than kLazyQ (base 2), as in the general path
+      float alpha[2] = {1.0f, 1.0f};
+      if (__builtin_expect(__any(need), 0)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(s[0][j] - m_use);
-      p[4 + j] = __builtin_amdgcn_exp2f(s[1][j] - m_use);
-    }
+        for (int s2 = 0; s2 < 2; ++s2) {
+          float tmax = sc[s2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) psum += p[j];
-    Srow = Srow * alpha + psum;
-    Mrow = m_new;
-    // B operands p * vscale_g as an fp16 pair hi + lo (the pair carries
-    // about 22 bits of the fp32 product, so the fp16 operand width does not
-    // limit the result), and the bias sums
-    half8_t pf[NG], pl[NG];
+          for (int o = 16; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+          const float m_new = (tmax > srM[s2] + kLazyQ) ? tmax : srM[s2];
+          const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+          alpha[s2] = __builtin_amdgcn_exp2f(srM[s2] - m_use);
+          srM[s2] = m_new;
+        }
+        // O of MFMA row n (n < 4) takes the alpha of that row: slot n & 1 of
+        // the lanes of half-wave n >> 1
+        const int src = (int)(min(n, 3u) >> 1) * 32;
+        const float a0 = __shfl(alpha[0], src), a1 = __shfl(alpha[1], src);
+        const float an = (n >= 4u) ? 1.0f : ((n & 1u) ? a1 : a0);
+        if (!__all(an == 1.0f)) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t *vsc = T.vsb[j >> 2][0];
-        const uint32_t *vbi = T.vsb[j >> 2][1];
-        const float w = p[j] * elem_f32<ET>(vsc, (j & 3) * NG + g);
-        const half_t hi = (half_t)w;
-        pf[g][j] = hi;
-        pl[g][j] = (half_t)(w - (float)hi);
-        acc = fmaf(p[j], elem_f32<ET>(vbi, (j & 3) * NG + g), acc);
+          for (int db = 0; db < DB; ++db) oacc[db] *= an;
+        }
       }
-      pb[g] = pb[g] * alpha + acc;
-    }
-    if (!__all(alpha == 1.0f)) {
+      // p, the lane's shares of S and of the V bias sums, and p * vscale_g
+      // into LDS as the PV operands [g][row][slot], an fp16 hi + lo pair as
+      // in the general path (8-bit codes reach s c ~ 25, where a single fp16
+      // operand would cost ~1e-2).  Slot order is the V operand's: key 16h + 4g4 + j
+      // sits at 8 g4 + 4h + j, lane group gp reading slots 8gp .. 8gp+7.
+      const uint32_t kpos = 8u * ((kl & 15u) >> 2) + 4u * (kl >> 4) + (kl & 3u);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const float m_use = (srM[s2] == -INFINITY) ? 0.0f : srM[s2];
+        const float pp = __builtin_amdgcn_exp2f(sc[s2] - m_use);
+        srS[s2] = srS[s2] * alpha[s2] + pp;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          srB[s2][g] = fmaf(pp, T.vbr[g], srB[s2][g] * alpha[s2]);
+          const float w = pp * T.vsr[g];
+          const half_t hi = (half_t)w;
+          pw[(g * 4 + sr_row[s2]) * BN + kpos] = hi;
+          pwl[(g * 4 + sr_row[s2]) * BN + kpos] = (half_t)(w - (float)hi);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // B operand of row n (rows past 3 read row n & 3: dead columns)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        pf[g] = *reinterpret_cast<const half8_t *>(&pw[(g * 4 + (n & 3u)) * BN + 8 * gp]);
+        pl[g] = *reinterpret_cast<const half8_t *>(&pwl[(g * 4 + (n & 3u)) * BN + 8 * gp]);
+      }
+    } else {
+      float s[2][4];
+      float tmax = -INFINITY;
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t *ksc = T.ksb[kb][0];
+        const uint32_t *kbi = T.ksb[kb][1];
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x = 0.0f;
+  #pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            x = fmaf(elem_f32<ET>(ksc, j * NG + g), sacc[g][kb][j], x);
+            x = fmaf(elem_f32<ET>(kbi, j * NG + g), qsum[g], x);
+          }
+          const float mv = T.m[kb][j];
+          // an excluded cell adds -inf: the arithmetic above stays unconditional
+          x = fmaf(x, a.qscale, (mv > kMasked) ? mv * kLog2e : -INFINITY);
+          s[kb][j] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // Lazy rescale: the reference max M moves only when the tile's max
+      // exceeds it by more than kLazyQ (base 2); until then p <= 2^kLazyQ, held
+      // exactly by the fp32 sums and by the fp16 hi + lo P * scale pair, and
+      // O, S and M stay consistent: the same softmax.
+      const float m_new = (tmax > Mrow + kLazyQ) ? tmax : Mrow;
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(Mrow - m_use);
+      float p[8];
+      float psum = 0.0f;
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(s[0][j] - m_use);
+        p[4 + j] = __builtin_amdgcn_exp2f(s[1][j] - m_use);
+      }
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) psum += p[j];
+      Srow = Srow * alpha + psum;
+      Mrow = m_new;
+      // B operands p * vscale_g as an fp16 pair hi + lo (the pair carries
+      // about 22 bits of the fp32 product, so the fp16 operand width does not
+      // limit the result), and the bias sums
+  #pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float acc = 0.0f;
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t *vsc = T.vsb[j >> 2][0];
+          const uint32_t *vbi = T.vsb[j >> 2][1];
+          const float w = p[j] * elem_f32<ET>(vsc, (j & 3) * NG + g);
+          const half_t hi = (half_t)w;
+          pf[g][j] = hi;
+          pl[g][j] = (half_t)(w - (float)hi);
+          acc = fmaf(p[j], elem_f32<ET>(vbi, (j & 3) * NG + g), acc);
+        }
+        pb[g] = pb[g] * alpha + acc;
+      }
+      if (!__all(alpha == 1.0f)) {
+  #pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
     }
     // PV: A = V codes of dim 16db+n for the lane's 8 keys (from LDS)
 #pragma unroll
@@ -638,6 +791,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   for (int i = 0; i < NS; ++i)
     if (t0 + i < t1) issue(t0 + i);
   load_q();
+  if constexpr (SR) {
+    // Q's group sums of the lane's SR rows (lane r holds row r's, r < 4)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) sr_qs[s2][g] = __shfl(qsum[g], (int)sr_row[s2]);
+  }
   Tile cur;
   for (uint32_t t = t0; t < t1; ++t) {
     wait_tile(min(t1 - 1u - t, (uint32_t)(NS - 1)));
@@ -646,10 +806,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (t + NS < t1) issue(t + NS);
     int live = 0;
+    if constexpr (SR) {
+      live = (cur.mr[0] > kMasked) | (cur.mr[1] > kMasked);
+    } else {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) live |= (cur.m[kb][j] > kMasked);
+        for (int j = 0; j < 4; ++j) live |= (cur.m[kb][j] > kMasked);
+    }
     if (__any(live)) {
       __builtin_amdgcn_wave_barrier();
       store_v(cur);
@@ -659,6 +823,30 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   }
 
   // ---- results ----
+  if constexpr (SR) {
+    // totals of the SR rows over the half-wave, then to lane (n, gp = 0) of
+    // MFMA row n, so that the general reduction below finds them
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) {
+        srS[s2] += __shfl_xor(srS[s2], o);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) srB[s2][g] += __shfl_xor(srB[s2][g], o);
+      }
+    }
+    const int src = (int)(min(n, 3u) >> 1) * 32;
+    const bool odd = (n & 1u) != 0u;
+    const float s0 = __shfl(srS[0], src), s1 = __shfl(srS[1], src);
+    const float m0 = __shfl(srM[0], src), m1 = __shfl(srM[1], src);
+    Srow = (gp == 0u) ? (odd ? s1 : s0) : 0.0f;
+    Mrow = odd ? m1 : m0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const float b0 = __shfl(srB[0][g], src), b1 = __shfl(srB[1][g], src);
+      pb[g] = (gp == 0u) ? (odd ? b1 : b0) : 0.0f;
+    }
+  }
   float stot = Srow + __shfl_xor(Srow, 16);
   stot += __shfl_xor(stot, 32);
 #pragma unroll
@@ -702,18 +890,36 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   }
 }
 
-template <int DIM, int BITS, int G, int MM, int ET>
-hipError_t launch_qm(const QuantArgs &a, hipStream_t s) {
+// LDS of a variant: the stages and V transpose area, plus (SR) the live
+// rows' scores [NG][4][BN] f32 and p * scale operands [NG][4][BN] as fp16
+// hi and lo halves
+template <int DIM, int BITS, int G, int MM, int ET, int SR> constexpr int quant_lds() {
   using ST = QStage<DIM, BITS, G, MM, ET>;
+  constexpr int NG = DIM / G;
+  return ST::LDS + (SR ? NG * 4 * BN * 4 + NG * 4 * BN * 2 * 2 : 0);
+}
+
+template <int DIM, int BITS, int G, int MM, int ET, int SR>
+hipError_t launch_qs(const QuantArgs &a, hipStream_t s) {
   static const bool attr_set = [] {
-    (void)hipFuncSetAttribute((const void *)quant_kernel<DIM, BITS, G, MM, ET>,
+    (void)hipFuncSetAttribute((const void *)quant_kernel<DIM, BITS, G, MM, ET, SR>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     return true;
   }();
   (void)attr_set;
   dim3 grid(grid_size(a.units, a.row_tiles));
-  hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, MM, ET>), grid, dim3(kThreads), ST::LDS, s, a);
+  constexpr int lds = quant_lds<DIM, BITS, G, MM, ET, SR>();
+  hipLaunchKernelGGL((quant_kernel<DIM, BITS, G, MM, ET, SR>), grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
+}
+
+// At most 4 rows per kv stream (decode with a GQA group of up to 4) and
+// head dims up to 128 take the SR epilogue.
+template <int DIM, int BITS, int G, int MM, int ET>
+hipError_t launch_qm(const QuantArgs &a, hipStream_t s) {
+  if constexpr (DIM <= 128)
+    if (a.rows <= 4u) return launch_qs<DIM, BITS, G, MM, ET, 1>(a, s);
+  return launch_qs<DIM, BITS, G, MM, ET, 0>(a, s);
 }
 
 template <int DIM, int BITS, int G, int ET>
@@ -760,7 +966,7 @@ template <int DIM, int BITS, int G, int MM, int ET>
 uint32_t wgs_per_cu() {
   using ST = QStage<DIM, BITS, G, MM, ET>;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_kernel<DIM, BITS, G, MM, ET>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_kernel<DIM, BITS, G, MM, ET, 0>,
                                                    kThreads, ST::LDS) == hipSuccess &&
       n > 0)
     return (uint32_t)n;
