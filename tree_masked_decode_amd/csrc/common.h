@@ -221,6 +221,35 @@ __device__ inline void split_tiles(const FwdArgs &a, uint32_t bn, uint32_t tile_
   if (hi < lo) hi = lo;
 }
 
+// Cross-lane maxima in registers (no LDS round trip): DPP within rows of 16
+// lanes, v_permlane16_swap / v_permlane32_swap across rows.
+// max over lanes l ^ 16 (rows 0 + 1, 2 + 3 of the wavefront)
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// max over lanes l ^ 32 (the two halves of the wavefront)
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// max over the 32 lanes of the lane's half-wave
+__device__ inline float half_wave_max(float x) {
+  int v = __float_as_int(x);
+  // quad_perm [1,0,3,2] and [2,3,0,1]: lanes l ^ 1, l ^ 2
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false)));
+  v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false)));
+  v = __float_as_int(x);
+  // row_ror 4 and 8: the four quads of a 16-lane row
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false)));
+  v = __float_as_int(x);
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false)));
+  return max_xor16(x);
+}
+
 // Balanced contiguous split of n_tiles tiles into nwg ranges.
 __device__ inline void split_range(uint32_t n_tiles, uint32_t nwg, uint32_t s,
                                    uint32_t &t0, uint32_t &t1) {

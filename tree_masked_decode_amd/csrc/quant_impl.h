@@ -650,19 +650,19 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       if (__builtin_expect(__any(need), 0)) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          float tmax = sc[s2];
-#pragma unroll
-          for (int o = 16; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+          const float tmax = half_wave_max(sc[s2]);
           const float m_new = (tmax > srM[s2] + kLazyQ) ? tmax : srM[s2];
           const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
           alpha[s2] = __builtin_amdgcn_exp2f(srM[s2] - m_use);
           srM[s2] = m_new;
         }
         // O of MFMA row n (n < 4) takes the alpha of that row: slot n & 1 of
-        // the lanes of half-wave n >> 1
-        const int src = (int)(min(n, 3u) >> 1) * 32;
-        const float a0 = __shfl(alpha[0], src), a1 = __shfl(alpha[1], src);
-        const float an = (n >= 4u) ? 1.0f : ((n & 1u) ? a1 : a0);
+        // the lanes of half-wave n >> 1 (lanes 0 and 32 hold them)
+        const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 0));
+        const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[1]), 0));
+        const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 32));
+        const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[1]), 32));
+        const float an = n == 0u ? r0 : n == 1u ? r1 : n == 2u ? r2 : n == 3u ? r3 : 1.0f;
         if (!__all(an == 1.0f)) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[db] *= an;
@@ -717,8 +717,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
           tmax = fmaxf(tmax, x);
         }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = max_xor32(max_xor16(tmax));
       // Lazy rescale: the reference max M moves only when the tile's max
       // exceeds it by more than kLazyQ (base 2); until then p <= 2^kLazyQ, held
       // exactly by the fp32 sums and by the fp16 hi + lo P * scale pair, and
