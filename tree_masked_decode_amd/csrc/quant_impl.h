@@ -238,6 +238,12 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   using MG = MaskGeom<MM, ET>;
   constexpr bool IMPLICIT = MM == kMaskNone;
   constexpr int NG = S::NG, STEPS = S::STEPS, DB = S::DB, NS = ST::NS;
+  // SBL: the scales and biases of a tile (8 SBW registers) stay in LDS
+  // where they would not fit beside the rest (many groups per token); the
+  // stage is then refilled after the tile's arithmetic instead of before.
+  constexpr bool SBL = !SR && (S::SBW > 8 || DIM >= 512);
+  // FUSE (head dim 512): scores folded per group, P operands built per group
+  constexpr bool FUSE = !SR && DIM >= 512;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) char *)lds);
   uint32_t *vlds = reinterpret_cast<uint32_t *>(lds + NS * ST::BYTES);
@@ -330,10 +336,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 
   // ---- per-tile registers ----
   struct Tile {
-    uint32_t kw[2][NG][S::RUN];   // K words: key 16kb+n, group g
-    uint32_t ksb[2][2][S::SBW];   // K scales/biases: keys 16kb+4gp..+3, all groups
-    uint32_t vsb[2][2][S::SBW];   // V scales/biases: keys F(gp, 4h..4h+3)
-    u32x4 vw[S::VCH];             // V words for the LDS transpose
+    uint32_t kw[2][SBL ? 1 : NG][S::RUN];   // K words: key 16kb+n, group g (SBL: in LDS)
+    uint32_t ksb[2][2][SBL ? 1 : S::SBW];   // K scales/biases: keys 16kb+4gp..+3, all groups
+    uint32_t vsb[2][2][SBL ? 1 : S::SBW];   // V scales/biases: keys F(gp, 4h..4h+3)
+    const char *stp;              // SBL: the tile's LDS stage
+    u32x4 vw[SBL ? 1 : S::VCH];   // V words for the LDS transpose (SBL: in LDS)
     float m[2][4];                // mask cells (row n, keys 16kb+4gp+j)
     // SR: scale and bias of the lane's key kl per group, and its mask cells
     // of rows 2 rp + 0..1
@@ -453,6 +460,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   auto load_tile = [&](uint32_t t, Tile &T) {
     const uint32_t key0 = t * BN;
     const char *st = lds + stage_off(t);
+    T.stp = st;
     const uint32_t *Kl = reinterpret_cast<const uint32_t *>(st);
     const uint32_t *Vl = reinterpret_cast<const uint32_t *>(st + S::KT);
     const uint32_t *SBl[4];
@@ -464,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       const uint32_t kr = 16u * kb + n;   // key within the tile
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
+      for (int g = 0; g < (SBL ? 0 : NG); ++g)
 #pragma unroll
         for (int r = 0; r < S::RUN; ++r)
           T.kw[kb][g][r] = Kl[kr * S::WPK + g * S::GW + gp * S::RUN + r];
@@ -473,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       // 16h + 4gp + 0..3 (V side, the keys of B-operand half h)
       const uint32_t k4 = 16u * kb + 4u * gp;
 #pragma unroll
-      for (int w = 0; w < S::SBW; ++w) {
+      for (int w = 0; w < (SBL ? 0 : S::SBW); ++w) {
         const uint32_t wi = (k4 * NG) / S::EPW + w;
         T.ksb[kb][0][w] = SBl[0][wi];
         T.ksb[kb][1][w] = SBl[1][wi];
@@ -528,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < S::VCH; ++u) {
+    for (int u = 0; u < (SBL ? 0 : S::VCH); ++u) {
       const uint32_t c = lane + kThreads * u;
       const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
       T.vw[u] = (S::VTOT % kThreads == 0 || c < (uint32_t)S::VTOT)
@@ -545,8 +553,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       if (S::VTOT % kThreads != 0 && c >= (uint32_t)S::VTOT) continue;
       const uint32_t key = c / (S::WPK / 4), q4 = c % (S::WPK / 4);
       const uint32_t pos = 8u * ((key & 15u) >> 2) + 4u * (key >> 4) + (key & 3u);
+      // (SBL: straight from the stage, which stays until the tile is done)
+      const u32x4 vv = SBL ? *reinterpret_cast<const u32x4 *>(
+                                 reinterpret_cast<const uint32_t *>(T.stp + S::KT) +
+                                 key * S::WPK + 4 * q4)
+                           : T.vw[SBL ? 0 : u];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vlds[(4 * q4 + e) * S::RS + pos] = T.vw[u][e];
+      for (int e = 0; e < 4; ++e) vlds[(4 * q4 + e) * S::RS + pos] = vv[e];
     }
   };
 
@@ -600,24 +613,51 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
                            : half2_t{(half_t)-1024.0f, (half_t)-1024.0f};
 
   auto compute = [&](const Tile &T) {
-    // scores, one accumulator per scale group
-    floatx4 sacc[NG][2];
+    // scores, one accumulator per scale group.  FUSE (wide heads): each
+    // group's accumulators are folded into the running logits xf as soon as
+    // its matrix instructions are done -- the same operations in the same
+    // order as the epilogue below, with one group's registers live at a time
+    floatx4 sacc[FUSE ? 1 : NG][2];
+    float xf[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < NG; ++g) {
+      const int gs = FUSE ? 0 : g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        sacc[g][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        sacc[gs][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sub = 0; sub < S::SPG; ++sub) {
-          half8_t kf = word_codes<BITS>(&T.kw[kb][g][sub * S::WPS], cmask);
-          sacc[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[g * S::SPG + sub],
-                                                               sacc[g][kb], 0, 0, 0);
+          const uint32_t *kwp =
+              SBL ? reinterpret_cast<const uint32_t *>(T.stp) +
+                        (16u * kb + n) * S::WPK + g * S::GW + gp * S::RUN + sub * S::WPS
+                  : &T.kw[kb][SBL ? 0 : g][sub * S::WPS];
+          half8_t kf = word_codes<BITS>(kwp, cmask);
+          sacc[gs][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[g * S::SPG + sub],
+                                                                sacc[gs][kb], 0, 0, 0);
           if (QLO)
-            sacc[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                kf, qfl[(g * S::SPG + sub) % (QLO ? STEPS : 1)], sacc[g][kb], 0, 0, 0);
+            sacc[gs][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                kf, qfl[(g * S::SPG + sub) % (QLO ? STEPS : 1)], sacc[gs][kb], 0, 0, 0);
         }
       }
-    half8_t pf[NG], pl[NG];
+      if constexpr (FUSE) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t k4 = 16u * kb + 4u * gp;
+          const void *ksc = SBL ? (const void *)(T.stp + 2 * S::KT + k4 * NG * ESZ)
+                                : (const void *)T.ksb[kb][0];
+          const void *kbi = SBL ? (const void *)(T.stp + 2 * S::KT + S::SBP + k4 * NG * ESZ)
+                                : (const void *)T.ksb[kb][1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            xf[kb][j] = fmaf(elem_f32<ET>(ksc, j * NG + g), sacc[0][kb][j], xf[kb][j]);
+            xf[kb][j] = fmaf(elem_f32<ET>(kbi, j * NG + g), qsum[g], xf[kb][j]);
+          }
+        }
+      }
+    }
+    half8_t pf[FUSE ? 1 : NG], pl[FUSE ? 1 : NG];
+    float pgen[8];             // general path: p of the lane's 8 keys
+    float alpha_gen = 1.0f;    // ... and the tile's rescale of the row
     if constexpr (SR) {
       // ---- scores of the (at most 4) live rows, lane = (key kl, rows
       // sr_row[0..1]) ----
@@ -700,13 +740,17 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       float tmax = -INFINITY;
   #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t *ksc = T.ksb[kb][0];
-        const uint32_t *kbi = T.ksb[kb][1];
+        // (SBL: straight from the stage, the key's first element)
+        const uint32_t k4 = 16u * kb + 4u * gp;
+        const void *ksc = SBL ? (const void *)(T.stp + 2 * S::KT + k4 * NG * ESZ)
+                              : (const void *)T.ksb[kb][0];
+        const void *kbi = SBL ? (const void *)(T.stp + 2 * S::KT + S::SBP + k4 * NG * ESZ)
+                              : (const void *)T.ksb[kb][1];
   #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float x = 0.0f;
+          float x = xf[kb][j];
   #pragma unroll
-          for (int g = 0; g < NG; ++g) {
+          for (int g = 0; g < (FUSE ? 0 : NG); ++g) {
             x = fmaf(elem_f32<ET>(ksc, j * NG + g), sacc[g][kb][j], x);
             x = fmaf(elem_f32<ET>(kbi, j * NG + g), qsum[g], x);
           }
@@ -736,16 +780,23 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       for (int j = 0; j < 8; ++j) psum += p[j];
       Srow = Srow * alpha + psum;
       Mrow = m_new;
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) pgen[j] = p[j];
+      alpha_gen = alpha;
       // B operands p * vscale_g as an fp16 pair hi + lo (the pair carries
       // about 22 bits of the fp32 product, so the fp16 operand width does not
       // limit the result), and the bias sums
+  // (FUSE: built per group inside the PV loop instead)
   #pragma unroll
-      for (int g = 0; g < NG; ++g) {
+      for (int g = 0; g < (FUSE ? 0 : NG); ++g) {
         float acc = 0.0f;
   #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint32_t *vsc = T.vsb[j >> 2][0];
-          const uint32_t *vbi = T.vsb[j >> 2][1];
+          const uint32_t k4 = 16u * (j >> 2) + 4u * gp;
+          const void *vsc = SBL ? (const void *)(T.stp + 2 * S::KT + 2 * S::SBP + k4 * NG * ESZ)
+                                : (const void *)T.vsb[j >> 2][0];
+          const void *vbi = SBL ? (const void *)(T.stp + 2 * S::KT + 3 * S::SBP + k4 * NG * ESZ)
+                                : (const void *)T.vsb[j >> 2][1];
           const float w = p[j] * elem_f32<ET>(vsc, (j & 3) * NG + g);
           const half_t hi = (half_t)w;
           pf[g][j] = hi;
@@ -776,9 +827,31 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
         r[e] = as_u(y * vmul + vadd);
       }
       const int g = (16 * db) / G;
+      if constexpr (FUSE) {
+        if ((16 * db) % G == 0) {
+          // group g's B operands p * vscale_g (hi + lo) and bias sum, as the
+          // general epilogue makes them
+          float acc = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t k4 = 16u * (j >> 2) + 4u * gp;
+            const void *vsc = SBL ? (const void *)(T.stp + 2 * S::KT + 2 * S::SBP + k4 * NG * ESZ)
+                                  : (const void *)T.vsb[j >> 2][0];
+            const void *vbi = SBL ? (const void *)(T.stp + 2 * S::KT + 3 * S::SBP + k4 * NG * ESZ)
+                                  : (const void *)T.vsb[j >> 2][1];
+            const float w = pgen[j] * elem_f32<ET>(vsc, (j & 3) * NG + g);
+            const half_t hi = (half_t)w;
+            pf[0][j] = hi;
+            pl[0][j] = (half_t)(w - (float)hi);
+            acc = fmaf(pgen[j], elem_f32<ET>(vbi, (j & 3) * NG + g), acc);
+          }
+          pb[g] = pb[g] * alpha_gen + acc;
+        }
+      }
+      const int gi = FUSE ? 0 : g;
       const half8_t vf = __builtin_bit_cast(half8_t, r);
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[g], oacc[db], 0, 0, 0);
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[g], oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[gi], oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[gi], oacc[db], 0, 0, 0);
     }
   };
 
@@ -802,8 +875,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     wait_tile(min(t1 - 1u - t, (uint32_t)(NS - 1)));
     load_tile(t, cur);
     // the reads of tile t's stage have returned before copies refill it
+    // (SBL: compute still reads the stage's scales, so its refill waits)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (t + NS < t1) issue(t + NS);
+    if (!SBL && t + NS < t1) issue(t + NS);
     int live = 0;
     if constexpr (SR) {
       live = (cur.mr[0] > kMasked) | (cur.mr[1] > kMasked);
@@ -818,6 +892,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       store_v(cur);
       __builtin_amdgcn_wave_barrier();
       compute(cur);
+    }
+    if (SBL) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (t + NS < t1) issue(t + NS);
     }
   }
 
