@@ -421,10 +421,18 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       for (int i = 0; i < S::SB_I; ++i) {
         const uint32_t o = S::SB_W * (64u * i + lane);
         const uint32_t e = (o % S::SBB) / ESZ;              // first element of the copy
-        uint32_t key = key0 + e / NG;
-        // a word holds two tokens' values when NG == 1 at two bytes each
-        if (key >= L) key = (ESZ == 2 && NG == 1) ? ((L - 1u) & ~1u) : L - 1u;
-        const char *g = sarr[o / S::SBB] + ((size_t)key * NG + e % NG) * ESZ;
+        const uint32_t key = key0 + e / NG;
+        size_t el = (size_t)key * NG + e % NG;                // element of the stream
+        // past kv_seq_len: any whole copy inside the stream's first L tokens
+        // (never used).  A 4-byte copy of 2-byte values starts on an even
+        // element, so the last such pair is elements (L NG - 2) & ~1 and up:
+        // with an odd count of values per token, the last token's last value
+        // would otherwise pair with token L's first, past a buffer that holds
+        // exactly L tokens.
+        if (key >= L)
+          el = (ESZ == 2 && !S::SB_WIDE) ? (((size_t)L * NG >= 2 ? (size_t)L * NG - 2 : 0) & ~(size_t)1)
+                                         : (size_t)(L - 1u) * NG + e % NG;
+        const char *g = sarr[o / S::SBB] + el * ESZ;
         if (S::SB_WIDE)
           dma_b128(g, sb + 2u * S::KT + 1024u * i);
         else
