@@ -254,6 +254,53 @@ class Gen:
         self.dma_part(st, 0, 4, st)
         self.dma_part(st, 1, 3, (st + 3) % NS)
 
+    # ---- the same copies spread over the score instructions: issued as one
+    # burst at the top of a step they held the wavefront's in-order issue
+    # (no matrix instruction can pass a copy waiting for the address unit),
+    # with all four wavefronts bursting at once.  dma_setup computes both
+    # parts' scalar bases, or branches to `partial` when either tile reaches
+    # past kv_seq_len (those steps keep the burst with per-lane clamping);
+    # dma_list gives the (M0, copy) pairs that region_a interleaves. ----
+    def dma_setup(self, st, partial):
+        e = self.e
+        e("s_add_u32 s85, s80, 4")          # K (and mask) tile of this step
+        e("s_min_u32 s85, s85, s81")
+        e("s_lshl_b32 s92, s85, 5")
+        e("s_add_u32 s83, s92, 32")
+        e("s_cmp_le_u32 s83, %[L]")
+        e("s_cbranch_scc0 %s" % partial)
+        e("s_add_u32 s84, s80, 3")          # V tile of this step
+        e("s_min_u32 s84, s84, s81")
+        e("s_lshl_b32 s83, s84, 5")
+        e("s_add_u32 s83, s83, 32")
+        e("s_cmp_le_u32 s83, %[L]")
+        e("s_cbranch_scc0 %s" % partial)
+        e("s_lshl_b32 s83, s85, 14")
+        e("s_add_u32 s86, %[kb0], s83")
+        e("s_addc_u32 s87, %[kb1], 0")
+        e("s_lshl_b32 s83, s84, 14")
+        e("s_add_u32 s88, %[vb0], s83")
+        e("s_addc_u32 s89, %[vb1], 0")
+        if self.ml:
+            e("s_lshl_b32 s83, s92, 2")
+            e("s_add_u32 s90, %[mb0], s83")
+            e("s_addc_u32 s91, %[mb1], 0")
+
+    def dma_list(self, st):
+        pairs = []
+        kl = st * KVB
+        for i in range(KV_PW):
+            pairs.append(["s_add_u32 m0, %%[m0k], %d" % (kl + i * 1024),
+                          "global_load_lds_dwordx4 %s, s[86:87]" % KOFF(i)])
+        for j in range(self.ml):
+            pairs.append(["s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(st) + j * 1024),
+                          "global_load_lds_dwordx4 %s, s[90:91]" % MROW[j]])
+        vl = NS * KVB + ((st + 3) % NS) * KVB
+        for i in range(KV_PW):
+            pairs.append(["s_add_u32 m0, %%[m0k], %d" % (vl + i * 1024),
+                          "global_load_lds_dwordx4 %s, s[88:89]" % VOFF(i)])
+        return pairs
+
     def class_read(self, stn):
         """Issue the mask-word reads of tile tn's class check (into the idle
         operand ring) so that their latency hides behind the copy issue."""
@@ -346,13 +393,16 @@ class Gen:
         return L
 
     # ---- scores of tile tn (stage stn) into buffer nxt, with the softmax of cur interleaved ----
-    def region_a(self, stn, nxt, cur, fast_c, with_softmax):
+    def region_a(self, stn, nxt, cur, fast_c, with_softmax, dma=()):
         e = self.e
         valu = self.softmax_list(cur) if with_softmax else []
         if with_softmax:
             e("s_mov_b32 s84, 0x%04x%04x" % (LAZY_F16, LAZY_F16))
         per = [[] for _ in range(16)]
-        # spread the VALU work over the 16 operand steps
+        # spread the copies (one per operand step from the first) and the
+        # VALU work over the 16 operand steps
+        for idx, pair in enumerate(dma):
+            per[min(15, idx * 16 // max(1, len(dma)))].extend(pair)
         for idx, ins in enumerate(valu):
             per[min(15, idx * 16 // max(1, len(valu)))].append(ins)
         nread = 16
@@ -408,14 +458,24 @@ class Gen:
         e("s_waitcnt vmcnt(%d)" % (2 * self.pt))
         e("s_barrier")
         self.class_read(stn)
-        self.dma(st)
         e("s_add_u32 s93, s80, 1")
         e("s_min_u32 s93, s93, s81")
         e("s_lshl_b32 s94, s93, 5")
+        self.dma_setup(st, ".Lwdmap%d" % st)
+        dl = self.dma_list(st)
         self.class_check(st, stn, ".Lwcslow%d" % st, read_done=True)
-        self.region_a(stn, nxt, cur, True, True)
+        self.region_a(stn, nxt, cur, True, True, dl)
         e("s_branch .Lwadone%d" % st)
         self.label(".Lwcslow%d" % st)
+        self.slow_class(stn, nxt)
+        self.region_a(stn, nxt, cur, False, True, dl)
+        e("s_branch .Lwadone%d" % st)
+        # a copy tile reaches past kv_seq_len (the last tiles of a split):
+        # the burst with per-lane clamping, then the per-cell scores (the
+        # class words may still be landing in the operand ring)
+        self.label(".Lwdmap%d" % st)
+        e("s_waitcnt lgkmcnt(0)")
+        self.dma(st)
         self.slow_class(stn, nxt)
         self.region_a(stn, nxt, cur, False, True)
         self.label(".Lwadone%d" % st)
