@@ -250,6 +250,32 @@ __device__ inline float half_wave_max(float x) {
   return max_xor16(x);
 }
 
+// Q'^T operand of one 32-dim step for a 16-row block: lane (n, gp) needs
+// dims 8gp .. 8gp+7 of its row n as fp16 (times sc).  The global loads take
+// dims 4gp .. 4gp+3 and 16+4gp .. 16+4gp+3 instead, so that the four lanes
+// of a row read 64 contiguous bytes per instruction; two swaps then regroup
+// the halves across the four 16-lane rows (gp): after the 32-lane swap the
+// rows of (x, y) hold (A0 A1 B0 B1, A2 A3 B2 B3), after the 16-lane swap
+// (A0 A2 B0 B2, A1 A3 B1 B3) -- lane gp's dims 8gp .. 8gp+3 and +4 .. +7.
+__device__ inline floatx4 q_fragment(const float *qrow_step, uint32_t gp, float sc) {
+  floatx4 a = *reinterpret_cast<const floatx4 *>(qrow_step + 4 * gp);
+  floatx4 b = *reinterpret_cast<const floatx4 *>(qrow_step + 16 + 4 * gp);
+  a *= sc;
+  b *= sc;
+  const half4_t ha = {(half_t)a[0], (half_t)a[1], (half_t)a[2], (half_t)a[3]};
+  const half4_t hb = {(half_t)b[0], (half_t)b[1], (half_t)b[2], (half_t)b[3]};
+  const u32x2 ua = __builtin_bit_cast(u32x2, ha), ub = __builtin_bit_cast(u32x2, hb);
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const auto s32 = __builtin_amdgcn_permlane32_swap(ua[k], ub[k], false, false);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+    r[k] = s16[0];
+    r[2 + k] = s16[1];
+  }
+  return __builtin_bit_cast(floatx4, r);
+}
+
 // Balanced contiguous split of n_tiles tiles into nwg ranges.
 __device__ inline void split_range(uint32_t n_tiles, uint32_t nwg, uint32_t s,
                                    uint32_t &t0, uint32_t &t1) {

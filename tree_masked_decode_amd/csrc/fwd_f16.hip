@@ -158,13 +158,8 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
       for (int ds = 0; ds < DS; ++ds) {
         // (a row past the end reads node0's row of its kv head's first head,
         // in bounds, and is zeroed: no branch splits the loads)
-        floatx4 x0 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp);
-        floatx4 x1 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp + 4);
         const float sc = valid[rb] ? a.scale : 0.0f;
-        x0 *= sc;
-        x1 *= sc;
-        qf[rb][ds] = half8_t{(half_t)x0[0], (half_t)x0[1], (half_t)x0[2], (half_t)x0[3],
-                             (half_t)x1[0], (half_t)x1[1], (half_t)x1[2], (half_t)x1[3]};
+        qf[rb][ds] = __builtin_bit_cast(half8_t, q_fragment(qrow + 32 * ds, gp, sc));
       }
     }
   };

@@ -301,13 +301,7 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
       const float sc = valid[rb] ? qs : 0.0f;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        floatx4 x0 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp);
-        floatx4 x1 = *reinterpret_cast<const floatx4 *>(qrow + 32 * ds + 8 * gp + 4);
-        x0 *= sc;
-        x1 *= sc;
-        const half8_t h = {(half_t)x0[0], (half_t)x0[1], (half_t)x0[2], (half_t)x0[3],
-                           (half_t)x1[0], (half_t)x1[1], (half_t)x1[2], (half_t)x1[3]};
-        const floatx4 w = __builtin_bit_cast(floatx4, h);
+        const floatx4 w = q_fragment(qrow + 32 * ds, gp, sc);
 #pragma unroll
         for (int k = 0; k < 4; ++k) Qv[rb][4 * ds + k] = w[k];
       }
