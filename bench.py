@@ -108,13 +108,20 @@ def source_sha(files):
     return h.hexdigest()[:16]
 
 
+# (the split planner in abi.hip sets the partial-result bytes, so it keys
+# the record too)
 FWD_SOURCES = {"f16": ["tree_masked_decode_amd/csrc/fwd_f16.hip",
-                       "tree_masked_decode_amd/csrc/common.h"],
+                       "tree_masked_decode_amd/csrc/fwd_wide.hip",
+                       "tree_masked_decode_amd/csrc/fwd_wide_loop.inc",
+                       "tree_masked_decode_amd/csrc/common.h",
+                       "tree_masked_decode_amd/csrc/abi.hip"],
                "f32": ["tree_masked_decode_amd/csrc/fwd_f32.hip",
-                       "tree_masked_decode_amd/csrc/common.h"],
+                       "tree_masked_decode_amd/csrc/common.h",
+                       "tree_masked_decode_amd/csrc/abi.hip"],
                "quant": ["tree_masked_decode_amd/csrc/quant.hip",
                          "tree_masked_decode_amd/csrc/quant_impl.h",
-                         "tree_masked_decode_amd/csrc/common.h"]}
+                         "tree_masked_decode_amd/csrc/common.h",
+                         "tree_masked_decode_amd/csrc/abi.hip"]}
 
 
 def measured_traffic(workload, kind):
