@@ -87,8 +87,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx32 __attribute__((ext_vector_type(32)));
 
 // The registers the tile loop (fwd_wide_loop.inc) writes besides the ones
-// bound to its operands: score buffers and P^T fragments, the operand ring
-// and softmax temporaries, and its scalar registers.
+// bound to its operands: the scores (accumulated in a[212:235], copied to
+// v[96:119]) and their -M' input (a[236:247]), P^T fragments, the operand
+// ring and softmax temporaries, and its scalar registers.
 #define TA_WIDE_CLOBBERS                                                                          \
   "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107",   \
       "v108", "v109", "v110", "v111", "v112", "v113", "v114", "v115", "v116", "v117", "v118",   \
@@ -99,7 +100,11 @@ typedef float floatx32 __attribute__((ext_vector_type(32)));
       "v183", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193",   \
       "v194", "v195", "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204",   \
       "v205", "v206", "v207", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "s88",     \
-      "s89", "s90", "s91", "s92", "s93", "s94", "s95", "s96", "s97", "s98", "s99", "vcc", "scc", \
+      "s89", "s90", "s91", "s92", "s93", "s94", "s95", "s96", "s97", "s98", "s99", "vcc", "scc", "m0", \
+      "a212", "a213", "a214", "a215", "a216", "a217", "a218", "a219", "a220", "a221", "a222", \
+      "a223", "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", \
+      "a234", "a235", "a236", "a237", "a238", "a239", "a240", "a241", "a242", "a243", "a244", \
+      "a245", "a246", "a247", \
       "memory"
 
 template <int ML>

@@ -19,11 +19,15 @@ Register map (fixed; fwd_wide.hip binds its variables to these ranges):
   a[192:203]  row sums (ones . P^T), rb at a[192 + 4 rb : +3]
   a[204:206]  the reference max the pending scores were issued with, saved
               when a slow step moves M (see "stale" below)
+  a[212:235]  score accumulators of the next tile, (rb, kb) at a[212 + 8 rb + 4 kb : +3]
+  a[236:247]  score accumulator input -M' (four copies), rb at a[236 + 4 rb : +3]
   v[0:95]     Q'^T fragments, (rb, ds) at v[32 rb + 4 ds : +3]
-  v[96:143]   scores, buffer b (tile parity), (rb, kb) at v[96 + 24 b + 8 rb + 4 kb : +3]
+  v[96:119]   the current tile's scores, copied out of a[212:235] at the top
+              of each step, (rb, kb) at v[96 + 8 rb + 4 kb : +3]
+  v[120:143]  per-cell accumulator inputs, staged for a[212:235] (slow paths)
   v[144:155]  P^T fragments (fp16), rb at v[144 + 4 rb : +3]
   v[156:159]  a half8 of ones (row-sum operand)
-  v[160:171]  score accumulator input -M' (four copies), rb at v[160 + 4 rb : +3]
+  v[160:162]  -M' of each row block (the value a[236:247] holds, for the VALU)
   v[172:174]  reference max M of each row block (base 2; -inf until a key is seen)
   v[175]      4 gp
   v[176:199]  operand ring, 6 slots of 4 registers; temporaries in the slow paths
@@ -45,6 +49,12 @@ SGPRs s80..s99 are the loop's own (declared clobbered):
   s93 next tile tn  s94 first key of tn  s95 L - 1  s[96:97] return address
   s[98:99] 64-bit temporary, and the return address of the rescale
 
+Every matrix instruction accumulates in the accumulation registers: a
+wavefront that mixes matrix instructions accumulating in ordinary registers
+with ones accumulating in accumulation registers issues them at about half
+rate (measured: 30 instead of 16 cycles each), so the scores are accumulated
+in a[212:235] and copied to ordinary registers for the softmax.
+
 Hazards (gfx950, as the compiler itself spaces them): a matrix result read by
 a VALU needs 8 wait states, a VALU result read by a matrix instruction 2, an
 exp result read by a VALU 1, a VALU result read by v_permlane*_swap 2.  The
@@ -58,9 +68,18 @@ D, RB, W, NS, BN = 256, 3, 4, 4, 32
 KVB = BN * D * 2          # bytes of one K (or V) tile
 DS, DB = D // 32, D // 16
 KV_PW = KVB // 1024 // W  # 1 KB copies per wavefront per K (or V) tile
-RING = 6
-AHEAD = 5                 # operand reads in flight ahead of the matrix instructions (ring slot of
-                          # step i+5 is that of step i-1, already consumed)
+# Operand ring slots (4 registers each); the first six double as the slow
+# paths' temporaries and the mask words of the class check, the rest as the
+# staging of per-cell accumulator inputs (slow paths, no reads in flight).
+# AHEAD_A / AHEAD_B: operand reads in flight ahead of the matrix instructions
+# in the score / PV region; the ring slot a read fills is that of the step
+# before the current one, already consumed.
+SLOTS = [176, 180, 184, 188, 192, 196, 120, 124, 128, 132, 136, 140]
+AHEAD_A = int(os.environ.get("TA_AHEAD_A", "5"))
+AHEAD_B = int(os.environ.get("TA_AHEAD_B", "5"))
+RING = max(6, max(AHEAD_A, AHEAD_B) + 1)
+assert RING <= len(SLOTS)
+assert 2 * AHEAD_B <= 15 and AHEAD_A <= 15   # the LDS counter holds 15
 LAZY = 15.0               # the reference max moves when a tile's row max exceeds it by > 15 (base 2)
 LAZY_F16 = 0x7800         # 2^15 as fp16 bits: a fast-path p above it needs a new reference
 
@@ -92,9 +111,18 @@ def Q(rb, ds):
     return r4(32 * rb + 4 * ds)
 
 
-def S(buf, rb, kb, j=None):
-    b = 96 + 24 * buf + 8 * rb + 4 * kb
+def SA(rb, kb, j=None):
+    b = 212 + 8 * rb + 4 * kb
+    return ("a[%d:%d]" % (b, b + 3)) if j is None else "a%d" % (b + j)
+
+
+def SV(rb, kb, j=None):
+    b = 96 + 8 * rb + 4 * kb
     return r4(b) if j is None else "v%d" % (b + j)
+
+
+def SSTG(rb, kb, j):
+    return "v%d" % (120 + 8 * rb + 4 * kb + j)
 
 
 def P(rb, k=None):
@@ -106,8 +134,12 @@ ONES = "v[156:159]"
 
 
 def C(rb, j=None):
-    b = 160 + 4 * rb
-    return r4(b) if j is None else "v%d" % (b + j)
+    b = 236 + 4 * rb
+    return ("a[%d:%d]" % (b, b + 3)) if j is None else "a%d" % (b + j)
+
+
+def CV(rb):
+    return "v%d" % (160 + rb)
 
 
 def M2(rb):
@@ -115,16 +147,16 @@ def M2(rb):
 
 
 def B(i):
-    return r4(176 + 4 * (i % RING))
+    return r4(SLOTS[i % RING])
 
 
 def Blo(i):
-    b = 176 + 4 * (i % RING)
+    b = SLOTS[i % RING]
     return "v[%d:%d]" % (b, b + 1)
 
 
 def Bhi(i):
-    b = 176 + 4 * (i % RING)
+    b = SLOTS[i % RING]
     return "v[%d:%d]" % (b + 2, b + 3)
 
 
@@ -352,14 +384,14 @@ class Gen:
             e("v_mov_b32_e32 %s, 0x%08x" % (T(3), F32_NEGINF))
             for rb in range(RB):
                 for kb in range(2):
-                    xb = 176 + 4 * ((2 * rb + kb) % RING)
+                    xb = SLOTS[2 * rb + kb]
                     for j in range(4):
                         x = "v%d" % (xb + j)
                         e("v_cmp_gt_i32_e64 s[98:99], %s, %d" % (T(1), 16 * kb + j))
                         e("v_cmp_lt_f32_e32 vcc, s83, %s" % x)
                         e("s_and_b64 vcc, vcc, s[98:99]")
-                        e("v_fma_f32 %s, %s, s84, %s" % (T(2), x, C(rb, 0)))
-                        e("v_cndmask_b32_e32 %s, %s, %s, vcc" % (S(nxt, rb, kb, j), T(3), T(2)))
+                        e("v_fma_f32 %s, %s, s84, %s" % (T(2), x, CV(rb)))
+                        e("v_cndmask_b32_e32 %s, %s, %s, vcc" % (SSTG(rb, kb, j), T(3), T(2)))
         else:
             e("v_mov_b32_e32 %s, 0x%08x" % (T(3), F32_NEGINF))
             for rb in range(RB):
@@ -371,8 +403,12 @@ class Gen:
                         e("s_and_b64 vcc, vcc, s[98:99]")
                         e("v_cmp_le_u32_e64 s[98:99], %%[keylo], %s" % T(2))
                         e("s_and_b64 vcc, vcc, s[98:99]")
-                        e("v_cndmask_b32_e32 %s, %s, %s, vcc" % (S(nxt, rb, kb, j), T(3), C(rb, 0)))
-        e("s_nop 1")
+                        e("v_cndmask_b32_e32 %s, %s, %s, vcc" % (SSTG(rb, kb, j), T(3), CV(rb)))
+        for rb in range(RB):
+            for kb in range(2):
+                for j in range(4):
+                    e("v_accvgpr_write_b32 %s, %s" % (SA(rb, kb, j), SSTG(rb, kb, j)))
+        e("s_nop 2")
 
     # ---- the fast softmax of buffer cur: exp2, fp16 packing, range check ----
     def softmax_list(self, cur):
@@ -380,7 +416,7 @@ class Gen:
         for rb in range(RB):
             for kb in range(2):
                 for j in range(4):
-                    L.append("v_exp_f32_e32 %s, %s" % (T(4 * kb + j), S(cur, rb, kb, j)))
+                    L.append("v_exp_f32_e32 %s, %s" % (T(4 * kb + j), SV(rb, kb, j)))
             for k in range(4):
                 L.append("v_cvt_pk_f16_f32 %s, %s, %s" % (P(rb, k), T(2 * k), T(2 * k + 1)))
         words = [P(rb, k) for rb in range(RB) for k in range(4)]
@@ -410,22 +446,19 @@ class Gen:
         def kread(i):
             ds, kb = i >> 1, i & 1
             e("ds_read_b128 %s, %s offset:%d" % (B(i), OFFK(ds), stn * KVB + kb * 16 * D * 2))
-        for i in range(AHEAD):
+        for i in range(AHEAD_A):
             kread(i)
         for i in range(16):
             ds, kb = i >> 1, i & 1
             # one wait covers two steps (steps i and i+1)
             if i % 2 == 0:
-                issued = min(nread, i + AHEAD)
+                issued = min(nread, i + AHEAD_A)
                 e("s_waitcnt lgkmcnt(%d)" % max(0, issued - min(nread, i + 2)))
             for rb in range(RB):
-                if ds == 0:
-                    src_c = C(rb) if fast_c else S(nxt, rb, kb)
-                else:
-                    src_c = S(nxt, rb, kb)
-                e("v_mfma_f32_16x16x32_f16 %s, %s, %s, %s" % (S(nxt, rb, kb), B(i), Q(rb, ds), src_c))
-            if i + AHEAD < nread:
-                kread(i + AHEAD)
+                src_c = C(rb) if fast_c and ds == 0 else SA(rb, kb)
+                e("v_mfma_f32_16x16x32_f16 %s, %s, %s, %s" % (SA(rb, kb), B(i), Q(rb, ds), src_c))
+            if i + AHEAD_A < nread:
+                kread(i + AHEAD_A)
             for ins in per[i]:
                 e(ins)
 
@@ -439,22 +472,28 @@ class Gen:
         def vread(db):
             e("ds_read_b64_tr_b16 %s, %s offset:%d" % (Blo(db), OFFV(db), st * KVB))
             e("ds_read_b64_tr_b16 %s, %s offset:%d" % (Bhi(db), OFFV(db), st * KVB + 16 * D * 2))
-        for db in range(AHEAD):
+        for db in range(AHEAD_B):
             vread(db)
         for db in range(DB):
             # one wait covers two d-blocks
             if db % 2 == 0:
-                issued = 2 * min(DB, db + AHEAD)
+                issued = 2 * min(DB, db + AHEAD_B)
                 e("s_waitcnt lgkmcnt(%d)" % max(0, issued - 2 * min(DB, db + 2)))
             for rb in range(RB):
                 e("v_mfma_f32_16x16x32_f16 %s, %s, %s, %s" % (O(rb, db), B(db), P(rb), O(rb, db)))
-            if db + AHEAD < DB:
-                vread(db + AHEAD)
+            if db + AHEAD_B < DB:
+                vread(db + AHEAD_B)
 
     def step(self, st):
         e = self.e
         cur, nxt, stn = st & 1, (st & 1) ^ 1, (st + 1) % NS
         self.label(".Lwstep%d" % st)
+        # tile t's scores out of the accumulation registers (region A below
+        # overwrites them with tile t+1's); before the wait, which they overlap
+        for rb in range(RB):
+            for kb in range(2):
+                for j in range(4):
+                    e("v_accvgpr_read_b32 %s, %s" % (SV(rb, kb, j), SA(rb, kb, j)))
         e("s_waitcnt vmcnt(%d)" % (2 * self.pt))
         e("s_barrier")
         self.class_read(stn)
@@ -508,14 +547,14 @@ class Gen:
             # the reference the scores were issued with
             e("s_bitcmp1_b32 s82, 1")
             e("s_cbranch_scc1 .Lwref%d_%d" % (cur, rb))
-            e("v_sub_f32_e32 %s, 0, %s" % (ref, C(rb, 0)))
+            e("v_sub_f32_e32 %s, 0, %s" % (ref, CV(rb)))
             e("s_branch .Lwrefd%d_%d" % (cur, rb))
             self.label(".Lwref%d_%d" % (cur, rb))
             e("v_accvgpr_read_b32 %s, %s" % (ref, AREF(rb)))
             self.label(".Lwrefd%d_%d" % (cur, rb))
             for kb in range(2):
                 for j in range(4):
-                    e("v_add_f32_e32 %s, %s, %s" % (T(4 * kb + j), S(cur, rb, kb, j), ref))
+                    e("v_add_f32_e32 %s, %s, %s" % (T(4 * kb + j), SV(rb, kb, j), ref))
             e("v_max3_f32 %s, %s, %s, %s" % (tmx, T(0), T(1), T(2)))
             e("v_max3_f32 %s, %s, %s, %s" % (tmx, tmx, T(3), T(4)))
             e("v_max3_f32 %s, %s, %s, %s" % (tmx, tmx, T(5), T(6)))
@@ -541,16 +580,16 @@ class Gen:
             e("v_cmp_neq_f32_e32 vcc, 1.0, %s" % alpha)
             e("s_or_b64 s[88:89], s[88:89], vcc")
             # the scores of the next tile were issued with the current -C
-            e("v_sub_f32_e32 %s, 0, %s" % (tmp, C(rb, 0)))
+            e("v_sub_f32_e32 %s, 0, %s" % (tmp, CV(rb)))
             e("v_accvgpr_write_b32 %s, %s" % (AREF(rb), tmp))
             e("v_mov_b32_e32 %s, %s" % (M2(rb), mnew))
             # reference used from now on: mnew, or 0 while it is -inf
             e("v_cmp_neq_f32_e32 vcc, 0x%08x, %s" % (F32_NEGINF, mnew))
             e("s_and_b64 s[90:91], s[90:91], vcc")
             e("v_cndmask_b32_e32 %s, 0, %s, vcc" % (msub, mnew))
-            e("v_sub_f32_e32 %s, 0, %s" % (C(rb, 0), msub))
-            for j in range(1, 4):
-                e("v_mov_b32_e32 %s, %s" % (C(rb, j), C(rb, 0)))
+            e("v_sub_f32_e32 %s, 0, %s" % (CV(rb), msub))
+            for j in range(4):
+                e("v_accvgpr_write_b32 %s, %s" % (C(rb, j), CV(rb)))
             for k in range(8):
                 e("v_sub_f32_e32 %s, %s, %s" % (T(k), T(k), msub))
             for k in range(8):
@@ -598,8 +637,13 @@ class Gen:
         e("s_sub_u32 s81, %[t1], 1")
         e("s_sub_u32 s95, %[L], 1")
         e("s_mov_b32 s82, 0")
+        # -M' = 0 while every M is -inf (the ordinary-register copy v[160:162]
+        # comes in as zero)
+        for rb in range(RB):
+            for j in range(4):
+                e("v_accvgpr_write_b32 %s, 0" % C(rb, j))
         e("s_barrier")
-        # scores of the first tile (stage 0, buffer 0)
+        # scores of the first tile (stage 0)
         e("s_mov_b32 s93, s80")
         e("s_lshl_b32 s94, s93, 5")
         self.class_check("p", 0, ".Lwpcslow")
@@ -609,6 +653,10 @@ class Gen:
         self.slow_class(0, 0)
         self.region_a(0, 0, 1, False, False)
         self.label(".Lwpdone")
+        # (step 0 reads those scores at once: the matrix results' wait states)
+        e("s_nop 7")
+        e("s_nop 7")
+        e("s_nop 7")
         for st in range(NS):
             self.step(st)
         e("s_branch .Lwstep0")
