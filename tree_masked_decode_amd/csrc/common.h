@@ -153,6 +153,10 @@ __device__ inline uint32_t sgpr_u32(uint32_t x) { return __builtin_amdgcn_readfi
 __device__ inline void dma_b128(const void *g, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(sgpr_u32(lds)) : "memory");
 }
+// The same, non-temporal: for data that is read once into LDS.
+__device__ inline void dma_b128_nt(const void *g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(sgpr_u32(lds)) : "memory");
+}
 __device__ inline void dma_b32(const void *g, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(sgpr_u32(lds)) : "memory");
 }

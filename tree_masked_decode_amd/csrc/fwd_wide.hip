@@ -254,7 +254,7 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
     for (int i = 0; i < S::KV_PW; ++i) {
       const uint32_t row = __float_as_uint(KVROW[i]);
       const uint32_t key = min(key0 + row, L - 1u);
-      dma_b128(reinterpret_cast<const char *>(K + (size_t)key * D) + (k_off[i] - 2u * row * D),
+      dma_b128_nt(reinterpret_cast<const char *>(K + (size_t)key * D) + (k_off[i] - 2u * row * D),
                lk + i * 1024u);
     }
     if constexpr (!IMPLICIT) {
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
       if (key >= L) key = (L - 1u) & ~3u;
 #pragma unroll
       for (int j = 0; j < ML; ++j)
-        dma_b128(reinterpret_cast<const char *>(a.mask) + (mrow[j] - 16u * (lane % 8u)) + 4u * key,
+        dma_b128_nt(reinterpret_cast<const char *>(a.mask) + (mrow[j] - 16u * (lane % 8u)) + 4u * key,
                  mask_lds + st * (W * S::MB) + j * 1024u);
     }
   };
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_wide_kernel(FwdArgs a) {
     for (int i = 0; i < S::KV_PW; ++i) {
       const uint32_t row = __float_as_uint(KVROW[i]);
       const uint32_t key = min(key0 + row, L - 1u);
-      dma_b128(reinterpret_cast<const char *>(V + (size_t)key * D) + (v_off[i] - 2u * row * D),
+      dma_b128_nt(reinterpret_cast<const char *>(V + (size_t)key * D) + (v_off[i] - 2u * row * D),
                lv + i * 1024u);
     }
   };

@@ -80,6 +80,10 @@ AHEAD_B = int(os.environ.get("TA_AHEAD_B", "5"))
 RING = max(6, max(AHEAD_A, AHEAD_B) + 1)
 assert RING <= len(SLOTS)
 assert 2 * AHEAD_B <= 15 and AHEAD_A <= 15   # the LDS counter holds 15
+# Cache policy of the K / V / mask copies: non-temporal.  Each 1 KB copy is
+# read once into LDS (the other row tile of its tile reads it at about the
+# same time); measured on the 32K tree, the tile loop ran 52.8 -> 47.5 us.
+CPOL = "nt"
 LAZY = 15.0               # the reference max moves when a tile's row max exceeds it by > 15 (base 2)
 LAZY_F16 = 0x7800         # 2^15 as fp16 bits: a fast-path p above it needs a new reference
 
@@ -243,14 +247,14 @@ class Gen:
         e("s_addc_u32 s87, %s, 0" % base[1])
         for i in range(KV_PW):
             e("s_add_u32 m0, %%[m0k], %d" % (lbase + i * 1024))
-            e("global_load_lds_dwordx4 %s, s[86:87]" % off(i))
+            e(("global_load_lds_dwordx4 %s, s[86:87] " + CPOL) % off(i))
         if part == 0 and self.ml:
             e("s_lshl_b32 s83, s92, 2")
             e("s_add_u32 s90, %[mb0], s83")
             e("s_addc_u32 s91, %[mb1], 0")
             for j in range(self.ml):
                 e("s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(stage) + j * 1024))
-                e("global_load_lds_dwordx4 %s, s[90:91]" % MROW[j])
+                e(("global_load_lds_dwordx4 %s, s[90:91] " + CPOL) % MROW[j])
         e("s_branch .Lwdmad%s" % tag)
         # a tile that ends past kv_seq_len: per-lane rows clamped to L - 1
         self.label(".Lwpdma%s" % tag)
@@ -264,7 +268,7 @@ class Gen:
             e("v_min_u32 %s, s95, %s" % (T(1), T(1)))
             e("v_lshl_add_u32 %s, %s, 9, %s" % (T(1), T(1), T(0)))
             e("s_add_u32 m0, %%[m0k], %d" % (lbase + i * 1024))
-            e("global_load_lds_dwordx4 %s, s[98:99]" % T(1))
+            e(("global_load_lds_dwordx4 %s, s[98:99] " + CPOL) % T(1))
         if part == 0 and self.ml:
             # key of the lane's chunk, clamped to the chunk that holds L - 1
             e("v_lshrrev_b32 %s, 2, %s" % (T(2), M16))
@@ -279,7 +283,7 @@ class Gen:
                 e("v_sub_u32 %s, %s, %s" % (T(4), MROW[j], M16))
                 e("v_add_u32 %s, %s, %s" % (T(4), T(4), T(2)))
                 e("s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(stage) + j * 1024))
-                e("global_load_lds_dwordx4 %s, s[98:99]" % T(4))
+                e(("global_load_lds_dwordx4 %s, s[98:99] " + CPOL) % T(4))
         self.label(".Lwdmad%s" % tag)
 
     def dma(self, st):
@@ -323,14 +327,14 @@ class Gen:
         kl = st * KVB
         for i in range(KV_PW):
             pairs.append(["s_add_u32 m0, %%[m0k], %d" % (kl + i * 1024),
-                          "global_load_lds_dwordx4 %s, s[86:87]" % KOFF(i)])
+                          ("global_load_lds_dwordx4 %s, s[86:87] " + CPOL) % KOFF(i)])
         for j in range(self.ml):
             pairs.append(["s_add_u32 m0, %%[m0m], %d" % (self.mask_stage(st) + j * 1024),
-                          "global_load_lds_dwordx4 %s, s[90:91]" % MROW[j]])
+                          ("global_load_lds_dwordx4 %s, s[90:91] " + CPOL) % MROW[j]])
         vl = NS * KVB + ((st + 3) % NS) * KVB
         for i in range(KV_PW):
             pairs.append(["s_add_u32 m0, %%[m0k], %d" % (vl + i * 1024),
-                          "global_load_lds_dwordx4 %s, s[88:89]" % VOFF(i)])
+                          ("global_load_lds_dwordx4 %s, s[88:89] " + CPOL) % VOFF(i)])
         return pairs
 
     def class_read(self, stn):
