@@ -150,25 +150,33 @@ uint32_t quant_wgs_per_cu(uint32_t dim, uint32_t bits, uint32_t group, int mask_
 // the "s" operands require.  The LDS address goes to M0 as an operand bound
 // to that register, so the compiler writes M0 itself and knows it changed.)
 __device__ inline uint32_t sgpr_u32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ inline void dma_b128(const void *g, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(sgpr_u32(lds)) : "memory");
+// NT: the non-temporal policy, for K/V streamed once into LDS (on the 128K
+// chain it raised the forward from 5.6 to 6.2 TB/s).
+template <bool NT = false> __device__ inline void dma_b128(const void *g, uint32_t lds) {
+  if constexpr (NT)
+    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(sgpr_u32(lds)) : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(sgpr_u32(lds)) : "memory");
 }
-// The same, non-temporal: for data that is read once into LDS.
-__device__ inline void dma_b128_nt(const void *g, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(sgpr_u32(lds)) : "memory");
-}
+__device__ inline void dma_b128_nt(const void *g, uint32_t lds) { dma_b128<true>(g, lds); }
 __device__ inline void dma_b32(const void *g, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(sgpr_u32(lds)) : "memory");
 }
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset (global_load_lds_dwordx4 v_off, s[base]): a loop that walks
 // tiles only moves the scalar base, the per-lane offsets stay put.
+template <bool NT = false>
 __device__ inline void dma_b128_s(const void *base, uint32_t voff, uint32_t lds) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   const uint64_t bs = ((uint64_t)sgpr_u32((uint32_t)(b >> 32)) << 32) | sgpr_u32((uint32_t)b);
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"((const void *)(uintptr_t)bs),
-               "{m0}"(sgpr_u32(lds))
-               : "memory");
+  if constexpr (NT)
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"((const void *)(uintptr_t)bs),
+                 "{m0}"(sgpr_u32(lds))
+                 : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"((const void *)(uintptr_t)bs),
+                 "{m0}"(sgpr_u32(lds))
+                 : "memory");
 }
 template <int N> __device__ inline void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -215,9 +215,9 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
       for (int i = 0; i < S::KV_PW; ++i) {
         const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
         if (PART == 0)
-          dma_b128_s(base, k_off[i], la);
+          dma_b128_s<true>(base, k_off[i], la);
         else
-          dma_b128_s(base, v_off[i], la + S::KV_BYTES);
+          dma_b128_s<true>(base, v_off[i], la + S::KV_BYTES);
       }
     } else {
 #pragma unroll
@@ -226,9 +226,9 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
         const uint32_t key = min(key0 + kv_row[i], L - 1u);
         const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
         if (PART == 0)
-          dma_b128(K + (size_t)key * D + kv_col[i], la);
+          dma_b128<true>(K + (size_t)key * D + kv_col[i], la);
         else
-          dma_b128(V + (size_t)key * D + v_col[i], la + S::KV_BYTES);
+          dma_b128<true>(V + (size_t)key * D + v_col[i], la + S::KV_BYTES);
       }
     }
     if (PART == 1) {
