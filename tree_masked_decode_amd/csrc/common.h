@@ -48,6 +48,9 @@ struct FwdArgs {
   // tiles from the first live key's to the last live key's
   const uint32_t *range;
   uint32_t range_chunks;
+  // fp16 kernel: K/V copies with the non-temporal policy (set for long K/V
+  // streams, where it measured faster; short, latency-bound calls lose by it)
+  uint32_t stream_nt;
 };
 
 // Live-key scan of an explicit mask: chunk c of `chunks` equal key ranges
@@ -165,17 +168,21 @@ __device__ inline void dma_b32(const void *g, uint32_t lds) {
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset (global_load_lds_dwordx4 v_off, s[base]): a loop that walks
 // tiles only moves the scalar base, the per-lane offsets stay put.
+// The base may reach its SGPRs through v_readfirstlane right before the
+// copy, and a vector-memory read of an SGPR that a VALU instruction wrote
+// needs 5 wait states, which the compiler does not count for inline
+// assembly (without them the copy can read a stale base): hence the s_nop.
 template <bool NT = false>
 __device__ inline void dma_b128_s(const void *base, uint32_t voff, uint32_t lds) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   const uint64_t bs = ((uint64_t)sgpr_u32((uint32_t)(b >> 32)) << 32) | sgpr_u32((uint32_t)b);
   if constexpr (NT)
-    asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"((const void *)(uintptr_t)bs),
-                 "{m0}"(sgpr_u32(lds))
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff),
+                 "s"((const void *)(uintptr_t)bs), "{m0}"(sgpr_u32(lds))
                  : "memory");
   else
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"((const void *)(uintptr_t)bs),
-                 "{m0}"(sgpr_u32(lds))
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+                 "s"((const void *)(uintptr_t)bs), "{m0}"(sgpr_u32(lds))
                  : "memory");
 }
 template <int N> __device__ inline void wait_vm() {

@@ -113,7 +113,9 @@ __device__ inline void lds_mfma_pipeline() {
   __builtin_amdgcn_sched_group_barrier(0x008, MF * AHEAD, 0);
 }
 
-template <int D, int RB, int MROWS, bool VEC, int W>
+// NT: the K/V copies take the non-temporal policy (long K/V streams; the
+// planner sets FwdArgs::stream_nt).
+template <int D, int RB, int MROWS, bool VEC, int W, bool NT>
 __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   constexpr bool IMPLICIT = MROWS == 0;
   using S = F16Shape<D, RB, MROWS, VEC, W>;
@@ -215,9 +217,9 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
       for (int i = 0; i < S::KV_PW; ++i) {
         const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
         if (PART == 0)
-          dma_b128_s<true>(base, k_off[i], la);
+          dma_b128_s<NT>(base, k_off[i], la);
         else
-          dma_b128_s<true>(base, v_off[i], la + S::KV_BYTES);
+          dma_b128_s<NT>(base, v_off[i], la + S::KV_BYTES);
       }
     } else {
 #pragma unroll
@@ -226,9 +228,9 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
         const uint32_t key = min(key0 + kv_row[i], L - 1u);
         const uint32_t la = sb + (wave * S::KV_PW + i) * 1024u;
         if (PART == 0)
-          dma_b128<true>(K + (size_t)key * D + kv_col[i], la);
+          dma_b128<NT>(K + (size_t)key * D + kv_col[i], la);
         else
-          dma_b128<true>(V + (size_t)key * D + v_col[i], la + S::KV_BYTES);
+          dma_b128<NT>(V + (size_t)key * D + v_col[i], la + S::KV_BYTES);
       }
     }
     if (PART == 1) {
@@ -530,19 +532,24 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int RB, int MROWS, bool VEC, int W>
-hipError_t launch_v(const FwdArgs &a, hipStream_t s) {
+template <int D, int RB, int MROWS, bool VEC, int W, bool NT>
+hipError_t launch_nt(const FwdArgs &a, hipStream_t s) {
   using Sh = F16Shape<D, RB, MROWS, VEC, W>;
   const size_t lds = (size_t)Sh::NS * Sh::STAGE;
   static const bool attr_set = [] {
-    (void)hipFuncSetAttribute((const void *)fwd_f16_kernel<D, RB, MROWS, VEC, W>,
+    (void)hipFuncSetAttribute((const void *)fwd_f16_kernel<D, RB, MROWS, VEC, W, NT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     return true;
   }();
   (void)attr_set;
   dim3 grid(grid_size(a.units, a.row_tiles));
-  hipLaunchKernelGGL((fwd_f16_kernel<D, RB, MROWS, VEC, W>), grid, dim3(Sh::kThreads), lds, s, a);
+  hipLaunchKernelGGL((fwd_f16_kernel<D, RB, MROWS, VEC, W, NT>), grid, dim3(Sh::kThreads), lds, s, a);
   return hipGetLastError();
+}
+template <int D, int RB, int MROWS, bool VEC, int W>
+hipError_t launch_v(const FwdArgs &a, hipStream_t s) {
+  return a.stream_nt ? launch_nt<D, RB, MROWS, VEC, W, true>(a, s)
+                     : launch_nt<D, RB, MROWS, VEC, W, false>(a, s);
 }
 
 template <int D, int RB, int W>
