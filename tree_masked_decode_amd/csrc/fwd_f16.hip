@@ -300,6 +300,12 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) sacc[rb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // A tile wholly before the window start has no live cell.  The fast
+      // tiles never are, but the branch keeps the tile loop below nested:
+      // without it, at one row block, the compiler folds the rescale exit
+      // into the tile loop and copies every O accumulator out of the
+      // matrix-core registers once per tile.
+      if (key0 + BN <= a.key_lo) return 0;
     } else {
       float mmax = -INFINITY;
 #pragma unroll
