@@ -67,16 +67,6 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   const uint32_t tid = threadIdx.x;
   const uint32_t row0 = rt * kRT;
 
-  // Q rows of this workgroup (rows past the end read as zero).
-  for (uint32_t e = tid; e < (uint32_t)(kRT * D); e += kThreads) {
-    uint32_t r = e / D, d = e % D, gr = row0 + r;
-    float x = 0.0f;
-    if (gr < a.rows) {
-      uint32_t i = gr / a.group, h = hk * a.group + gr % a.group;
-      x = a.q[((size_t)h * a.q_l + i) * D + d];
-    }
-    Qs[r * S::QST + d] = x;
-  }
   if (tid < (uint32_t)kRT) {
     Mrow[tid] = -INFINITY;
     Srow[tid] = 0.0f;
@@ -104,8 +94,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
   constexpr int kRowStep = kThreads / BN;
 
   // K/V tile loads go into registers one tile ahead, so that their latency
-  // overlaps the arithmetic of the tile before (keys past kv_seq_len read as
-  // zero).
+  // overlaps the arithmetic of the tile before.  They are unconditional, from
+  // an in-bounds address (a key past kv_seq_len reads row kv_seq_len - 1),
+  // and such rows are zeroed where they are staged, so no load waits at a
+  // branch.  (Loading the mask cells one tile ahead as well measured slower
+  // on the short calls this kernel serves; they are read at the top of
+  // their tile.)
   constexpr int kLoadsPerThread = BN * D / 4 / kThreads;
   static_assert(kLoadsPerThread * kThreads * 4 == BN * D, "tile / thread shape");
   floatx4 kreg[kLoadsPerThread], vreg[kLoadsPerThread];
@@ -113,16 +107,29 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < kLoadsPerThread; ++i) {
       const uint32_t e = tid + (uint32_t)i * kThreads;
-      const uint32_t key = e / (D / 4), c4 = e % (D / 4);
-      kreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-      vreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (t * BN + key < a.kv_seq_len) {
-        kreg[i] = *reinterpret_cast<const floatx4 *>(K + (size_t)(t * BN + key) * D + 4 * c4);
-        vreg[i] = *reinterpret_cast<const floatx4 *>(V + (size_t)(t * BN + key) * D + 4 * c4);
-      }
+      const uint32_t key = min(t * BN + e / (D / 4), a.kv_seq_len - 1u), c4 = e % (D / 4);
+      kreg[i] = *reinterpret_cast<const floatx4 *>(K + (size_t)key * D + 4 * c4);
+      vreg[i] = *reinterpret_cast<const floatx4 *>(V + (size_t)key * D + 4 * c4);
     }
   };
   if (t0 < t1) load_kv(t0);
+
+  // Q rows of this workgroup (rows past the end read as zero), loaded after
+  // the first tile's so that the two latencies overlap
+  {
+    constexpr int kQPerThread = kRT * D / 4 / kThreads;
+    static_assert(kQPerThread * kThreads * 4 == kRT * D, "Q / thread shape");
+#pragma unroll
+    for (int v = 0; v < kQPerThread; ++v) {
+      const uint32_t e = tid + (uint32_t)v * kThreads;
+      const uint32_t r = e / (D / 4), c4 = e % (D / 4), gr = row0 + r;
+      const uint32_t grc = gr < a.rows ? gr : row0;
+      const uint32_t i = grc / a.group, h = hk * a.group + grc % a.group;
+      const floatx4 x = *reinterpret_cast<const floatx4 *>(a.q + ((size_t)h * a.q_l + i) * D + 4 * c4);
+      *reinterpret_cast<floatx4 *>(Qs + r * S::QST + 4 * c4) =
+          gr < a.rows ? x : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 
   for (uint32_t t = t0; t < t1; ++t) {
     const uint32_t key0 = t * BN;
@@ -144,14 +151,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a) {
       continue;
     }
 
-    // --- stage the K/V tile from registers, then fetch the next live one ---
+    // --- stage the K/V tile from registers (keys past kv_seq_len as zero),
+    // then fetch the next one ---
 #pragma unroll
     for (int i = 0; i < kLoadsPerThread; ++i) {
       const uint32_t e = tid + (uint32_t)i * kThreads;
       const uint32_t key = e / (D / 4), c4 = e % (D / 4);
+      const bool in = key0 + key < a.kv_seq_len;
+      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+      const floatx4 kx = in ? kreg[i] : zero;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) Ks[key * S::KST + 4 * c4 + x] = kreg[i][x];
-      *reinterpret_cast<floatx4 *>(Vs + key * D + 4 * c4) = vreg[i];
+      for (int x = 0; x < 4; ++x) Ks[key * S::KST + 4 * c4 + x] = kx[x];
+      *reinterpret_cast<floatx4 *>(Vs + key * D + 4 * c4) = in ? vreg[i] : zero;
     }
     __syncthreads();
     if (t + 1 < t1) load_kv(t + 1);
