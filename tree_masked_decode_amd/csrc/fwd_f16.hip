@@ -87,6 +87,15 @@ template <int D, int RB, int MROWS, bool VEC, int W> struct F16Shape {
   static_assert(PER_TILE * (NS - 2) <= 63, "vmcnt range");
 };
 
+// Q'^T fragments wanted in registers at this point: the compiler waits for
+// their loads here rather than where they are first used.
+template <int RB, int DS> __device__ inline void hold_q(const half8_t (&q)[RB][DS]) {
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < DS; ++j) asm volatile("" ::"v"(q[i][j]));
+}
+
 __device__ inline uint32_t swz(uint32_t row, uint32_t chunk) { return chunk ^ (row & 15u); }
 // V tiles use pairs of chunks: the transposing reads take 32 bytes (two
 // chunks) from each of four rows per 16 lanes, so rows are spread over chunk
@@ -434,15 +443,23 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_f16_kernel(FwdArgs a) {
   split_range(span_hi - span_lo, a.nwg, split, t0, t1);
   t0 += span_lo;
   t1 += span_lo;
+  // Tile t0 first, then Q: the wait the compiler puts before Q's first use
+  // (loads complete in order) also completes tile t0, and the two latencies
+  // overlap.  The rest of the prologue's tiles go out once Q is in
+  // registers, so that wait does not hold up on them; the first tile's wait
+  // below then allows exactly those NS - 2 tiles in flight.
+  if (t0 < t1) {
+    issue(t0, t0, std::integral_constant<int, 0>{});
+    issue(t0, t0, std::integral_constant<int, 1>{});
+  }
+  load_q();
+  hold_q(qf);
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
+  for (int s = 1; s < NS - 1; ++s)
     if (t0 + s < t1) {
       issue(t0 + s, t0, std::integral_constant<int, 0>{});
       issue(t0 + s, t0, std::integral_constant<int, 1>{});
     }
-  // Q after the first copies: the two memory latencies overlap (the wait the
-  // compiler puts before Q's first use also covers those copies)
-  load_q();
   // Top of tile t: wait for its copies, barrier (every wavefront is done with
   // tile t - 1), then start refilling tile t - 1's stage with tile t + NS - 1
   // (K now, V and mask once the scores are out: refill_rest).
