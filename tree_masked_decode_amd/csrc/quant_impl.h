@@ -867,10 +867,17 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   // A tile's stage is copied whole into registers (load_tile), so the copies
   // of tile t + NS go into tile t's own stage as soon as those reads have
   // returned: NS tiles stay in flight behind the arithmetic.
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-    if (t0 + i < t1) issue(t0 + i);
+  // Tile t0 first, then Q: the wait for Q's loads (they complete in order)
+  // also completes tile t0, and the two latencies overlap.  The other NS - 1
+  // tiles go out once Q's sums are in registers, so that wait does not
+  // cover them; the first tile's wait below allows exactly those in flight.
+  if (t0 < t1) issue(t0);
   load_q();
+#pragma unroll
+  for (int g = 0; g < NG; ++g) asm volatile("" ::"v"(qsum[g]));
+#pragma unroll
+  for (int i = 1; i < NS; ++i)
+    if (t0 + i < t1) issue(t0 + i);
   if constexpr (SR) {
     // Q's group sums of the lane's SR rows (lane r holds row r's, r < 4)
 #pragma unroll
