@@ -438,10 +438,10 @@ int tree_attn_reduce(const float *partials, size_t partials_bytes, void *out,
   if (of || !mul3(nrows, head_dim, out_dtype == TA_F32 ? 4 : 2, req_out))
     return fail(TA_EOVERFLOW, "%s: size computation overflows", fn);
   if (partials_bytes < req_part)
-    return fail(TA_ESIZE, "%s: partials buffer too small: have %zu bytes, need >= %llu",
+    return fail(TA_ESIZE, "%s: partials buffer holds %zu bytes of the %llu needed",
                 fn, partials_bytes, (unsigned long long)req_part);
   if (out_bytes < req_out)
-    return fail(TA_ESIZE, "%s: output buffer too small: have %zu bytes, need >= %llu", fn,
+    return fail(TA_ESIZE, "%s: output buffer holds %zu bytes of the %llu needed", fn,
                 out_bytes, (unsigned long long)req_out);
   if (nrows > 0x7ffffff0u) return fail(TA_EUNSUPPORTED, "%s: nrows too large", fn);
   ta::ReduceArgs a;
@@ -521,11 +521,11 @@ static int quant_forward(
                 n_q_heads, n_kv_heads);
   if (kv_seq_len == 0) return fail(TA_EINVAL, "%s: kv_seq_len must be > 0", fn);
   if (kv_capacity < kv_seq_len)
-    return fail(TA_EINVAL, "%s: kv_capacity (%u) must be >= kv_seq_len (%u)", fn,
+    return fail(TA_EINVAL, "%s: kv_capacity %u holds fewer than kv_seq_len %u keys", fn,
                 kv_capacity, kv_seq_len);
   if (q_l == 0) return fail(TA_EINVAL, "%s: q_seq_len (q_l) must be > 0", fn);
   if (mask != nullptr && mask_stride < kv_seq_len)
-    return fail(TA_EINVAL, "%s: mask_stride (%u) must be >= kv_seq_len (%u)", fn,
+    return fail(TA_EINVAL, "%s: mask_stride %u is shorter than kv_seq_len %u", fn,
                 mask_stride, kv_seq_len);
   if (nwg == 0 || nwg > kMaxNwg)
     return fail(TA_EINVAL, "%s: nwg must be in [1, %u], got %u", fn, kMaxNwg, nwg);
@@ -571,26 +571,26 @@ static int quant_forward(
   if (nwg > 1) req_part = partials_bytes_u64(BnQ * q_l, dim, nwg, of);
   if (of) return fail(TA_EOVERFLOW, "%s: partials size overflows", fn);
   if (q_bytes < req_q)
-    return fail(TA_ESIZE, "%s: q buffer too small: have %zu bytes, need >= %llu", fn, q_bytes,
+    return fail(TA_ESIZE, "%s: q buffer holds %zu bytes of the %llu needed", fn, q_bytes,
                 (unsigned long long)req_q);
   const char *names[6] = {"k_packed", "k_scales", "k_biases", "v_packed", "v_scales", "v_biases"};
   for (int b = 0; b < 6; ++b) {
     uint64_t need = (b % 3 == 0) ? req_packed : req_sb;
     if (kv_bytes[b] < need)
-      return fail(TA_ESIZE, "%s: %s buffer too small: have %zu bytes, need >= %llu", fn,
+      return fail(TA_ESIZE, "%s: %s buffer holds %zu bytes of the %llu needed", fn,
                   names[b], kv_bytes[b], (unsigned long long)need);
   }
   if (sinks && sinks_bytes < req_sinks)
-    return fail(TA_ESIZE, "%s: sinks buffer too small: have %zu bytes, need >= %llu", fn,
+    return fail(TA_ESIZE, "%s: sinks buffer holds %zu bytes of the %llu needed", fn,
                 sinks_bytes, (unsigned long long)req_sinks);
   if (mask && mask_bytes < req_mask)
-    return fail(TA_ESIZE, "%s: mask buffer too small: have %zu bytes, need >= %llu", fn,
+    return fail(TA_ESIZE, "%s: mask buffer holds %zu bytes of the %llu needed", fn,
                 mask_bytes, (unsigned long long)req_mask);
   if (nwg == 1 && out_bytes < req_out)
-    return fail(TA_ESIZE, "%s: output buffer too small: have %zu bytes, need >= %llu", fn,
+    return fail(TA_ESIZE, "%s: output buffer holds %zu bytes of the %llu needed", fn,
                 out_bytes, (unsigned long long)req_out);
   if (nwg > 1 && partials_bytes < req_part)
-    return fail(TA_ESIZE, "%s: partials buffer too small: have %zu bytes, need >= %llu", fn,
+    return fail(TA_ESIZE, "%s: partials buffer holds %zu bytes of the %llu needed", fn,
                 partials_bytes, (unsigned long long)req_part);
   uint64_t rows = (uint64_t)q_l * (n_q_heads / n_kv_heads);
   if (BnQ * q_l > 0x7fffffffull || rows > 0x7fffffffull)
@@ -687,9 +687,9 @@ int build_tree_mask(const int32_t *parents, uint32_t q_l, uint32_t kv_seq_len,
   if (q_l > (uint32_t)ta::kMaxTreeNodes)
     return fail(TA_EUNSUPPORTED, "%s: q_l must be <= %d, got %u", fn, ta::kMaxTreeNodes, q_l);
   if (kv_seq_len < q_l)
-    return fail(TA_EINVAL, "%s: kv_seq_len (%u) must be >= q_l (%u)", fn, kv_seq_len, q_l);
+    return fail(TA_EINVAL, "%s: kv_seq_len %u is shorter than the q_l %u tree nodes", fn, kv_seq_len, q_l);
   if (mask_stride < kv_seq_len)
-    return fail(TA_EINVAL, "%s: mask_stride (%u) must be >= kv_seq_len (%u)", fn, mask_stride,
+    return fail(TA_EINVAL, "%s: mask_stride %u is shorter than kv_seq_len %u", fn, mask_stride,
                 kv_seq_len);
   if (!parents || !mask) return fail(TA_EINVAL, "%s: parents and mask must not be NULL", fn);
   if ((uintptr_t)mask & 3u) return fail(TA_EINVAL, "%s: mask must be 4-byte aligned", fn);
@@ -703,7 +703,7 @@ int build_tree_mask(const int32_t *parents, uint32_t q_l, uint32_t kv_seq_len,
   uint64_t req;
   if (!mul3(q_l, mask_stride, 4, req)) return fail(TA_EOVERFLOW, "%s: size overflows", fn);
   if (mask_bytes < req)
-    return fail(TA_ESIZE, "%s: mask buffer too small: have %zu bytes, need >= %llu", fn,
+    return fail(TA_ESIZE, "%s: mask buffer holds %zu bytes of the %llu needed", fn,
                 mask_bytes, (unsigned long long)req);
   ta::MaskArgs a;
   memset(a.parents, 0, sizeof a.parents);
