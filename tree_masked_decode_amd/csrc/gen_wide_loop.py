@@ -674,8 +674,8 @@ class Gen:
         return self.lines
 
 
-def main():
-    here = os.path.dirname(os.path.abspath(__file__))
+def render():
+    """The text of fwd_wide_loop.inc."""
     out = ["// Generated by gen_wide_loop.py -- do not edit.  The tile loop of the",
            "// wide fp16 forward, one string per mask mode (0: implicit causal rule,",
            "// 1 / 2: mask cells copied per tile, 16 bytes per lane per copy).",
@@ -686,8 +686,13 @@ def main():
         for ln in lines:
             out.append('  "%s\\n" \\' % ln.replace('"', '\\"'))
         out.append('  ""')
+    return "\n".join(out) + "\n"
+
+
+def main():
+    here = os.path.dirname(os.path.abspath(__file__))
     with open(os.path.join(here, "fwd_wide_loop.inc"), "w") as f:
-        f.write("\n".join(out) + "\n")
+        f.write(render())
 
 
 if __name__ == "__main__":
