@@ -92,3 +92,16 @@ def test_bench_refuses_several_gpus():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_traffic_record_only_for_the_source_it_was_taken_on(monkeypatch):
+    # a committed HBM-traffic record is reported while the forward kernel's
+    # sources hash to its key, and dropped (None) once they differ
+    import json
+    w = "dynamic_tree_32k"
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_%s.json" % w)))
+    monkeypatch.setattr(bench, "source_sha", lambda files: rec["source_sha"])
+    assert bench.measured_traffic(w, "f16") == rec["bytes_per_launch"]
+    monkeypatch.setattr(bench, "source_sha", lambda files: "0" * 16)
+    assert bench.measured_traffic(w, "f16") is None
+    assert bench.measured_traffic("no_such_workload", "f16") is None
